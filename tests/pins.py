@@ -1,0 +1,409 @@
+"""Pins for the oracle: checks against formulations that do not share its arithmetic.
+
+Each ``pin_*`` function raises AssertionError when the oracle disagrees with
+  * a structural brute force (the host pool is rebuilt by walking pages,
+    sub-buffers, layers and rows in layout order and concatenating byte
+    strings; positions come from running sums, never from an offset formula),
+  * the CPU mock formula of the hybrid-pool write-back page (key source
+    excerpts: for every layer, host[dst_index, layer] = device_layer[src_index])
+    written with numpy fancy indexing on a 4-d view,
+  * invariants: a write-back followed by a load-back into fresh slots restores
+    every row bit-exactly, untouched rows and pages keep their bytes, shard pad
+    bytes become zero (CacheStore H2H page, "page_first_kv_split support"),
+  * closed forms worked out by hand in ``golden/layout_closed_forms.txt``.
+
+``run_all()`` runs every pin; the mutation test runs it in a subprocess
+against deliberately broken builds of the oracle and expects a failure.
+"""
+from __future__ import annotations
+
+import os
+import sys
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from oracle import oracle as O  # noqa: E402
+
+T, B = O.TOKEN_ROWS, O.PAGE_BLOCKS
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "layout_closed_forms.txt")
+
+# Tiny geometries: both layouts, token rows and page blocks, nonzero shard pad.
+GEOMS = {
+    "pf_kv": O.Geometry(2, 4, [(T, 32), (T, 32)], 6, 64, O.PAGE_FIRST),
+    "pf_one": O.Geometry(3, 4, [(T, 48)], 5, 40, O.PAGE_FIRST),
+    "shard_kv_pad": O.Geometry(3, 4, [(T, 32), (T, 16)], 6, 64, O.KV_SPLIT_SHARD, align=256),
+    "pf_latent_indexer": O.Geometry(2, 4, [(T, 32), (B, 48)], 6, 64, O.PAGE_FIRST),
+    "shard_block_pad": O.Geometry(2, 4, [(T, 16), (B, 32)], 5, 32, O.KV_SPLIT_SHARD, align=128),
+}
+
+
+def has_blocks(g: O.Geometry) -> bool:
+    return any(gr == B for gr, _ in g.subs)
+
+
+# ---------------------------------------------------------------- structural model
+def layout_walk(g: O.Geometry):
+    """Yield (key, nbytes) for every piece of the host pool in storage order.
+    key = ("row", b, p, l, r) for a token row, ("blk", b, p, l) for a page block,
+    ("pad", p) for shard padding."""
+
+    def page_pieces(b, p):
+        gran, e = g.subs[b]
+        for l in range(g.layers):
+            if gran == B:
+                yield ("blk", b, p, l), e
+            else:
+                for r in range(g.page_size):
+                    yield ("row", b, p, l, r), e
+
+    if g.layout == O.PAGE_FIRST:
+        for b in range(len(g.subs)):
+            for p in range(g.host_pages):
+                yield from page_pieces(b, p)
+    else:
+        payload = 0
+        for b in range(len(g.subs)):
+            for _, e in page_pieces(b, 0):
+                payload += e
+        pad = (-payload) % g.align
+        for p in range(g.host_pages):
+            for b in range(len(g.subs)):
+                yield from page_pieces(b, p)
+            yield ("pad", p), pad
+
+
+def positions(g: O.Geometry) -> dict:
+    """key -> (start, nbytes), by running sum over the storage order."""
+    pos, at = {}, 0
+    for key, n in layout_walk(g):
+        pos[key] = (at, n)
+        at += n
+    return pos, at
+
+
+def random_device(g: O.Geometry, rng) -> list:
+    return [[rng.integers(0, 256, g.device_units(b) * e, dtype=np.uint8) for _ in range(g.layers)]
+            for b, (_, e) in enumerate(g.subs)]
+
+
+def copy_device(dev) -> list:
+    return [[a.copy() for a in layers] for layers in dev]
+
+
+def make_burst(g: O.Geometry, rng, partial: bool = True):
+    """Distinct host pages; whole pages, plus (token-row pools only) one partial page
+    missing some rows; device slots distinct (page-aligned whole pages for block pools)."""
+    P = g.page_size
+    npages = max(1, g.host_pages // 2)
+    pages = rng.choice(g.host_pages, size=npages, replace=False)
+    toks = []
+    for j, p in enumerate(pages):
+        rows = np.arange(P)
+        if partial and not has_blocks(g) and j == len(pages) - 1 and P > 1:
+            rows = np.sort(rng.choice(P, size=P - 1, replace=False))
+        toks.append(p * P + rows)
+    h = np.concatenate(toks).astype(np.int64)
+    if has_blocks(g):
+        dpages = rng.choice(g.device_slots // P, size=npages, replace=False)
+        d = (dpages[:, None] * P + np.arange(P)[None, :]).reshape(-1).astype(np.int64)
+    else:
+        d = rng.choice(g.device_slots, size=h.size, replace=False).astype(np.int64)
+    return d, h
+
+
+def fresh_slots(g: O.Geometry, rng, used: np.ndarray, n: int) -> np.ndarray:
+    P = g.page_size
+    if has_blocks(g):
+        free = np.setdiff1d(np.arange(g.device_slots // P), np.unique(used // P))
+        dp = rng.choice(free, size=n // P, replace=False)
+        return (dp[:, None] * P + np.arange(P)[None, :]).reshape(-1).astype(np.int64)
+    free = np.setdiff1d(np.arange(g.device_slots), used)
+    return rng.choice(free, size=n, replace=False).astype(np.int64)
+
+
+def expected_host_after_write_back(g, dev, host0: np.ndarray, d, h) -> np.ndarray:
+    """Brute force: walk the layout, and for every piece decide its bytes."""
+    P = g.page_size
+    named = {int(hh): int(dd) for dd, hh in zip(d, h)}
+    touched = {int(hh) // P for hh in h}
+    out, at = [], 0
+    for key, n in layout_walk(g):
+        cur = host0[at:at + n].tobytes()
+        if key[0] == "row":
+            _, b, p, l, r = key
+            if p * P + r in named:
+                s = named[p * P + r]
+                e = g.subs[b][1]
+                cur = dev[b][l][s * e:(s + 1) * e].tobytes()
+        elif key[0] == "blk":
+            _, b, p, l = key
+            if p * P in named:
+                blk = named[p * P] // P
+                e = g.subs[b][1]
+                cur = dev[b][l][blk * e:(blk + 1) * e].tobytes()
+        else:
+            _, p = key
+            if p in touched:
+                cur = bytes(n)
+        out.append(cur)
+        at += n
+    return np.frombuffer(b"".join(out), dtype=np.uint8).copy()
+
+
+def expected_device_after_load_back(g, layer, dev0, host: np.ndarray, h, d):
+    pos, _ = positions(g)
+    P = g.page_size
+    dev = copy_device(dev0)
+    for dd, hh in zip(d, h):
+        p, r = int(hh) // P, int(hh) % P
+        for b, (gran, e) in enumerate(g.subs):
+            if gran == B:
+                if r != 0:
+                    continue
+                st, n = pos[("blk", b, p, layer)]
+                blk = int(dd) // P
+                dev[b][layer][blk * e:(blk + 1) * e] = host[st:st + n]
+            else:
+                st, n = pos[("row", b, p, layer, r)]
+                dev[b][layer][int(dd) * e:(int(dd) + 1) * e] = host[st:st + n]
+    return dev
+
+
+def assert_dev_equal(x, y, what=""):
+    for b in range(len(x)):
+        for l in range(len(x[b])):
+            assert np.array_equal(x[b][l], y[b][l]), f"{what}: sub {b} layer {l} differs"
+
+
+# ---------------------------------------------------------------- pins
+def pin_sizes_match_structure():
+    for name, g in GEOMS.items():
+        _, total = positions(g)
+        assert O.host_pool_bytes(g) == total, name
+        if g.layout == O.KV_SPLIT_SHARD:
+            assert total % g.host_pages == 0
+            stride = total // g.host_pages
+            assert O.shard_bytes(g) == stride, name
+            assert stride % g.align == 0, name
+            assert stride - O.page_payload_bytes(g) < g.align, name
+
+
+def pin_offsets_match_structure():
+    for name, g in GEOMS.items():
+        pos, _ = positions(g)
+        for key, (st, _) in pos.items():
+            if key[0] == "row":
+                _, b, p, l, r = key
+                assert O.host_offset(g, b, p, l, r) == st, (name, key)
+            elif key[0] == "blk":
+                _, b, p, l = key
+                for r in (0, g.page_size - 1):
+                    assert O.host_offset(g, b, p, l, r) == st, (name, key, r)
+
+
+def pin_write_back_brute_force():
+    for seed, (name, g) in enumerate(GEOMS.items()):
+        rng = np.random.default_rng(100 + seed)
+        dev = random_device(g, rng)
+        host0 = rng.integers(0, 256, O.host_pool_bytes(g), dtype=np.uint8)
+        d, h = make_burst(g, rng)
+        want = expected_host_after_write_back(g, dev, host0, d, h)
+        host = host0.copy()
+        dev_before = copy_device(dev)
+        O.write_back(g, dev, host, d, h)
+        assert np.array_equal(host, want), name
+        assert_dev_equal(dev, dev_before, f"{name}: write-back changed the device pool")
+
+
+def pin_write_back_mock_formula():
+    """host4[page, layer, row] = device_layer[slot], per layer, on 4-d views."""
+    for seed, (name, g) in enumerate(GEOMS.items()):
+        if has_blocks(g):
+            continue
+        rng = np.random.default_rng(200 + seed)
+        dev = random_device(g, rng)
+        host = np.zeros(O.host_pool_bytes(g), dtype=np.uint8)
+        d, h = make_burst(g, rng)
+        O.write_back(g, dev, host, d, h)
+        want = np.zeros_like(host)
+        L, P, H = g.layers, g.page_size, g.host_pages
+        page, row = h // P, h % P
+        if g.layout == O.PAGE_FIRST:
+            start = 0
+            for b, (_, e) in enumerate(g.subs):
+                region = want[start:start + H * L * P * e].reshape(H, L, P, e)
+                for l in range(L):
+                    region[page, l, row] = dev[b][l].reshape(-1, e)[d]
+                start += H * L * P * e
+        else:
+            payload = sum(L * P * e for _, e in g.subs)
+            stride = payload + (-payload) % g.align
+            shards = want.reshape(H, stride)
+            start = 0
+            for b, (_, e) in enumerate(g.subs):
+                view = shards[:, start:start + L * P * e].reshape(H, L, P, e)
+                for l in range(L):
+                    view[page, l, row] = dev[b][l].reshape(-1, e)[d]
+                start += L * P * e
+        assert np.array_equal(host, want), name
+
+
+def pin_load_back_brute_force():
+    for seed, (name, g) in enumerate(GEOMS.items()):
+        rng = np.random.default_rng(300 + seed)
+        dev0 = random_device(g, rng)
+        host = rng.integers(0, 256, O.host_pool_bytes(g), dtype=np.uint8)
+        host_before = host.copy()
+        d, h = make_burst(g, rng)
+        for layer in range(g.layers):
+            want = expected_device_after_load_back(g, layer, dev0, host, h, d)
+            dev = copy_device(dev0)
+            O.load_back_layer(g, layer, dev, host, h, d)
+            assert_dev_equal(dev, want, f"{name} layer {layer}")
+        assert np.array_equal(host, host_before), f"{name}: load-back changed the host pool"
+
+
+def pin_round_trip_restores():
+    """Write back all layers, then load every layer into fresh slots: rows equal."""
+    for seed, (name, g) in enumerate(GEOMS.items()):
+        rng = np.random.default_rng(400 + seed)
+        dev = random_device(g, rng)
+        host = rng.integers(0, 256, O.host_pool_bytes(g), dtype=np.uint8)
+        d, h = make_burst(g, rng)
+        O.write_back(g, dev, host, d, h)
+        dev_before = copy_device(dev)
+        d2 = fresh_slots(g, rng, d, d.size)
+        for layer in range(g.layers):
+            O.load_back_layer(g, layer, dev, host, h, d2)
+        P = g.page_size
+        for b, (gran, e) in enumerate(g.subs):
+            for l in range(g.layers):
+                a = dev[b][l].reshape(-1, e)
+                a0 = dev_before[b][l].reshape(-1, e)
+                src = d // P if gran == B else d
+                dst = d2 // P if gran == B else d2
+                assert np.array_equal(a[dst], a0[src]), (name, b, l)
+                untouched = np.setdiff1d(np.arange(a.shape[0]), dst)
+                assert np.array_equal(a[untouched], a0[untouched]), (name, b, l)
+        assert O.round_trip_check(g, dev, d, d2) == 0, name
+
+
+def pin_untouched_and_byte_accounting():
+    for seed, (name, g) in enumerate(GEOMS.items()):
+        rng = np.random.default_rng(500 + seed)
+        dev = random_device(g, rng)
+        host0 = rng.integers(0, 256, O.host_pool_bytes(g), dtype=np.uint8)
+        d, h = make_burst(g, rng)
+        host = host0.copy()
+        O.write_back(g, dev, host, d, h)
+        pos, _ = positions(g)
+        P = g.page_size
+        named = set(int(x) for x in h)
+        touched = set(int(x) // P for x in h)
+        changed_allowed = np.zeros(host.size, dtype=bool)
+        for key, (st, n) in pos.items():
+            if key[0] == "row" and key[2] * P + key[4] in named:
+                changed_allowed[st:st + n] = True
+            if key[0] == "blk" and key[2] * P in named:
+                changed_allowed[st:st + n] = True
+            if key[0] == "pad" and key[1] in touched:
+                changed_allowed[st:st + n] = True
+                assert not host[st:st + n].any(), (name, "pad not zero")
+        assert np.array_equal(host[~changed_allowed], host0[~changed_allowed]), name
+        row_bytes = sum(e * g.layers for gran, e in g.subs if gran == T) * len(named)
+        blk_bytes = sum(e * g.layers for gran, e in g.subs if gran == B) * len(touched)
+        pad_bytes = sum(n for k, (st, n) in pos.items() if k[0] == "pad" and k[1] in touched)
+        assert int((host != host0).sum()) <= row_bytes + blk_bytes + pad_bytes, name
+
+
+def pin_round_trip_check_counts():
+    for seed, (name, g) in enumerate(GEOMS.items()):
+        rng = np.random.default_rng(600 + seed)
+        dev = random_device(g, rng)
+        d, _ = make_burst(g, rng, partial=False)
+        c = fresh_slots(g, rng, d, d.size)
+        # make a known set of units equal: copy rows of d onto c for some units
+        P = g.page_size
+        want = 0
+        for b, (gran, e) in enumerate(g.subs):
+            for l in range(g.layers):
+                a = dev[b][l].reshape(-1, e)
+                for i in range(d.size):
+                    if gran == B and d[i] % P != 0:
+                        continue
+                    x = d[i] // P if gran == B else d[i]
+                    y = c[i] // P if gran == B else c[i]
+                    if (i + l + b) % 3 == 0:
+                        a[y] = a[x]
+                    elif (i + l) % 5 == 0:
+                        a[y] = a[x]
+                        a[y, (i * 7 + l) % e] ^= 0x40
+                        want += 1
+                    else:
+                        want += int(not np.array_equal(a[x], a[y]))
+        assert O.round_trip_check(g, dev, d, c) == want, name
+
+
+def pin_index_preconditions():
+    g = GEOMS["pf_kv"]
+    assert O.check_indices(g, [0, 1, 2], [0, 1, 2])
+    assert not O.check_indices(g, [0, 0], [0, 1]), "repeated device slot accepted"
+    assert not O.check_indices(g, [0, 1], [5, 5]), "repeated host token accepted"
+    assert not O.check_indices(g, [g.device_slots], [0]), "device slot out of range accepted"
+    assert not O.check_indices(g, [0], [g.host_pages * g.page_size]), "host token out of range accepted"
+    assert not O.check_indices(g, [-1], [0]), "negative slot accepted"
+    assert O.check_indices(g, [], [])
+    gb = GEOMS["pf_latent_indexer"]
+    P = gb.page_size
+    whole = np.arange(P)
+    assert O.check_indices(gb, 8 + whole, 2 * P + whole)
+    assert not O.check_indices(gb, 8 + whole[:-1], 2 * P + whole[:-1]), "partial block page accepted"
+    assert not O.check_indices(gb, 9 + whole, 2 * P + whole), "misaligned device page accepted"
+    assert not O.check_indices(gb, 8 + whole[::-1], 2 * P + whole), "reordered rows accepted"
+
+
+def pin_golden_closed_forms():
+    with open(GOLDEN) as f:
+        lines = [ln.strip() for ln in f if ln.strip() and not ln.startswith("#")]
+    assert len(lines) >= 20
+    for ln in lines:
+        name, geo, q = [x.strip() for x in ln.split("|")]
+        layout, L, P, H, S, align, subs = geo.split()
+        sub = [((T if s[0] == "T" else B), int(s[1:])) for s in subs.split(",")]
+        g = O.Geometry(int(L), int(P), sub, int(H), int(S),
+                       O.KV_SPLIT_SHARD if layout == "shard" else O.PAGE_FIRST, int(align))
+        lhs, rhs = [x.strip() for x in q.split("=")]
+        what, *args = lhs.split()
+        args = [int(a) for a in args]
+        fn = {"sub_page_bytes": O.sub_page_bytes, "payload_bytes": O.page_payload_bytes,
+              "shard_bytes": O.shard_bytes, "host_pool_bytes": O.host_pool_bytes,
+              "host_offset": O.host_offset, "device_offset": O.device_offset}[what]
+        got = fn(g, *args)
+        assert got == int(rhs), f"{name}: {lhs} = {got}, closed form {rhs}"
+
+
+PINS = [pin_sizes_match_structure, pin_offsets_match_structure, pin_write_back_brute_force,
+        pin_write_back_mock_formula, pin_load_back_brute_force, pin_round_trip_restores,
+        pin_untouched_and_byte_accounting, pin_round_trip_check_counts, pin_index_preconditions,
+        pin_golden_closed_forms]
+
+
+def run_all() -> list:
+    failed = []
+    for pin in PINS:
+        try:
+            pin()
+        except AssertionError as e:
+            failed.append(f"{pin.__name__}: {e}")
+    return failed
+
+
+if __name__ == "__main__":
+    bad = run_all()
+    for b in bad:
+        print("FAIL", b)
+    sys.exit(1 if bad else 0)

@@ -1,0 +1,77 @@
+"""The oracle against its pins, and the pins against planted mistakes (CPU only)."""
+import os
+import subprocess
+import sys
+import tempfile
+
+import pytest
+
+import pins
+from oracle import oracle as O
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+@pytest.mark.parametrize("pin", pins.PINS, ids=lambda p: p.__name__)
+def test_pin(pin):
+    pin()
+
+
+# Plausible mistakes, planted in a copy of the oracle source.  Each must make at
+# least one pin fail (or crash the pin run): a dropped term, a wrong index, a
+# transposed operand, a missing rounding step, a wrong fill value.
+MUTANTS = [
+    ("layer and row transposed in the host offset",
+     "inner = ((int64_t)l * g->page_size + r) * g->bytes[b];",
+     "inner = ((int64_t)r * g->layers + l) * g->bytes[b];"),
+    ("shard size not rounded up",
+     "if (k * a < s) k = k + 1;", ";"),
+    ("sub-buffer region ignores the page count",
+     "region += g->host_pages * orc_sub_page_bytes(g, c);",
+     "region += orc_sub_page_bytes(g, c);"),
+    ("earlier sub-buffers dropped inside a shard",
+     "for (int c = 0; c < b; c++) before += orc_sub_page_bytes(g, c);", ";"),
+    ("page block indexed by token slot",
+     "if (g->gran[b] == ORC_PAGE_BLOCKS) return (s / g->page_size) * g->bytes[b];",
+     "if (g->gran[b] == ORC_PAGE_BLOCKS) return s * g->bytes[b];"),
+    ("row off by one in write-back",
+     "int32_t row = (int32_t)(h[i] % P);\n    for (int b = 0; b < g->nsub; b++) {\n      if (g->gran[b] == ORC_PAGE_BLOCKS && row != 0) continue;\n      for (int l = 0; l < L; l++) {",
+     "int32_t row = (int32_t)((h[i] + 1) % P);\n    for (int b = 0; b < g->nsub; b++) {\n      if (g->gran[b] == ORC_PAGE_BLOCKS && row != 0) continue;\n      for (int l = 0; l < L; l++) {"),
+    ("pad filled with a nonzero byte",
+     "memset(host + page * stride + payload, 0,", "memset(host + page * stride + payload, 1,"),
+    ("pad never written",
+     "memset(host + page * stride + payload, 0, (size_t)(stride - payload));", ";"),
+    ("load-back always writes layer 0",
+     "uint8_t* dst = dev[b * L + layer] + orc_device_offset(g, b, d[i]);",
+     "uint8_t* dst = dev[b * L + 0] + orc_device_offset(g, b, d[i]);"),
+    ("load-back reads layer 0 of the host page",
+     "const uint8_t* src = host + orc_host_offset(g, b, page, layer, row);",
+     "const uint8_t* src = host + orc_host_offset(g, b, page, 0, row);"),
+    ("misaligned device page accepted for page blocks",
+     "if (first < 0 || first % g->page_size != 0) { rc = ORC_ERR_INVALID; break; }",
+     "if (first < 0) { rc = ORC_ERR_INVALID; break; }"),
+    ("round-trip check counts equal rows",
+     "if (memcmp(x, y, (size_t)g->bytes[b]) != 0) bad++;",
+     "if (memcmp(x, y, (size_t)g->bytes[b]) == 0) bad++;"),
+    ("repeated host tokens accepted",
+     "if (seen_d[d[i]] || seen_h[h[i]]) {", "if (seen_d[d[i]]) {"),
+    ("device and host index swapped in write-back",
+     "const uint8_t* src = dev[b * L + l] + orc_device_offset(g, b, d[i]);",
+     "const uint8_t* src = dev[b * L + l] + orc_device_offset(g, b, h[i] % g->device_slots);"),
+]
+
+
+@pytest.mark.parametrize("desc,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_planted_mistake(desc, old, new):
+    src = open(os.path.join(os.path.dirname(O.__file__), "hc_oracle.c")).read()
+    assert src.count(old) >= 1, f"mutation anchor not found: {desc}"
+    with tempfile.TemporaryDirectory() as tmp:
+        msrc = os.path.join(tmp, "mutant.c")
+        mlib = os.path.join(tmp, "libmutant.so")
+        with open(msrc, "w") as f:
+            f.write(src.replace(old, new, 1))
+        O.build(msrc, mlib)
+        env = dict(os.environ, HC_ORACLE_LIB=mlib)
+        r = subprocess.run([sys.executable, os.path.join(HERE, "pins.py")], env=env,
+                           capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0, f"pins did not catch: {desc}\n{r.stdout}"
