@@ -1,0 +1,304 @@
+"""ctypes binding of libhc.so -- argument marshalling only.
+
+Every function here forwards to the C ABI declared in ``include/hc.h`` under
+the same name.  Torch supplies device memory and streams; the pinned host pool
+comes from ``hc_host_alloc``.  Importing this module fails loudly when the
+library has not been built: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libhc.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m host_device_page_amd.build` "
+                      "(hipcc, gfx950); the transfer path has no fallback")
+
+lib = ctypes.CDLL(LIB_PATH)
+
+HC_OK = 0
+HC_ERR_INVALID = -1
+HC_ERR_UNSUPPORTED = -2
+HC_ERR_HIP = -3
+HC_ERR_NOMEM = -4
+HC_ERR_DEVICE = -5
+HC_TOKEN_ROWS = 0
+HC_PAGE_BLOCKS = 1
+HC_LAYOUT_PAGE_FIRST = 0
+HC_LAYOUT_KV_SPLIT_SHARD = 1
+HC_MODE_AUTO = 0
+HC_MODE_STAGED = 1
+HC_MODE_ZEROCOPY = 2
+HC_FLAG_VALIDATE = 1
+HC_FLAG_PROFILE = 2
+HC_MAX_SUBBUFS = 4
+
+# hc_pool_kernel_time kinds
+KIND_GATHER, KIND_ZC_WRITE, KIND_ZC_READ, KIND_PADS, KIND_COMPARE, KIND_COPY_ENGINE = range(6)
+
+
+class hc_subbuf_desc(ctypes.Structure):
+    _fields_ = [("granularity", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("elem_bytes", ctypes.c_int64), ("device_layers", ctypes.POINTER(ctypes.c_void_p))]
+
+
+class hc_pool_desc(ctypes.Structure):
+    _fields_ = [("num_layers", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("num_subbufs", ctypes.c_int32), ("layout", ctypes.c_int32),
+                ("sub", hc_subbuf_desc * HC_MAX_SUBBUFS),
+                ("device_slots", ctypes.c_int64), ("host_pages", ctypes.c_int64),
+                ("shard_align", ctypes.c_int64),
+                ("host_base", ctypes.c_void_p), ("host_bytes", ctypes.c_int64),
+                ("staging", ctypes.c_void_p), ("staging_bytes", ctypes.c_int64),
+                ("copy_stream", ctypes.c_void_p),
+                ("write_back_mode", ctypes.c_int32), ("load_back_mode", ctypes.c_int32),
+                ("flags", ctypes.c_int32), ("max_ctas", ctypes.c_int32)]
+
+
+_D = ctypes.POINTER(hc_pool_desc)
+_V = ctypes.c_void_p
+_I64P = ctypes.POINTER(ctypes.c_int64)
+_SIGS = {
+    "hc_desc_check": (ctypes.c_int, [_D]),
+    "hc_host_pool_bytes": (ctypes.c_int, [_D, _I64P]),
+    "hc_staging_page_bytes": (ctypes.c_int, [_D, _I64P]),
+    "hc_host_offset": (ctypes.c_int, [_D, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _I64P]),
+    "hc_host_alloc": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int32, ctypes.POINTER(_V)]),
+    "hc_host_free": (ctypes.c_int, [_V]),
+    "hc_pool_create": (ctypes.c_int, [_D, ctypes.POINTER(_V)]),
+    "hc_pool_destroy": (ctypes.c_int, [_V]),
+    "hc_pool_mode": (ctypes.c_int, [_V, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]),
+    "hc_pool_sync": (ctypes.c_int, [_V]),
+    "hc_write_back_all_layers": (ctypes.c_int, [_V, _V, _V, ctypes.c_int64, _V]),
+    "hc_load_back_layer": (ctypes.c_int, [_V, ctypes.c_int32, _V, _V, ctypes.c_int64, _V]),
+    "hc_round_trip_check": (ctypes.c_int, [_V, _V, _V, ctypes.c_int64, _I64P]),
+    "hc_pool_kernel_time": (ctypes.c_int, [_V, ctypes.c_int32, ctypes.c_int32, _I64P,
+                                           ctypes.POINTER(ctypes.c_double)]),
+    "hc_last_error": (ctypes.c_char_p, []),
+    "hc_version": (ctypes.c_int, []),
+}
+for _name, (_res, _args) in _SIGS.items():
+    _fn = getattr(lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+
+class HcError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        msg = lib.hc_last_error().decode(errors="replace")
+        super().__init__(f"{where}: status {code}: {msg}")
+
+
+def check(code: int, where: str) -> None:
+    if code != HC_OK:
+        raise HcError(code, where)
+
+
+# ---------------------------------------------------------------- HIP events (plumbing)
+_hip = ctypes.CDLL("libamdhip64.so")
+for _name, _args in {"hipEventCreateWithFlags": [ctypes.POINTER(_V), ctypes.c_uint],
+                     "hipEventDestroy": [_V], "hipEventSynchronize": [_V], "hipEventQuery": [_V],
+                     "hipEventRecord": [_V, _V], "hipStreamWaitEvent": [_V, _V, ctypes.c_uint],
+                     "hipEventElapsedTime": [ctypes.POINTER(ctypes.c_float), _V, _V],
+                     "hipMemsetAsync": [_V, ctypes.c_int, ctypes.c_size_t, _V],
+                     "hipStreamSynchronize": [_V]}.items():
+    getattr(_hip, _name).argtypes = _args
+    getattr(_hip, _name).restype = ctypes.c_int
+
+
+def _hip_check(code: int, what: str) -> None:
+    if code != 0:
+        raise RuntimeError(f"{what} failed with hipError {code}")
+
+
+class HipEvent:
+    """A raw hipEvent_t (the layer-done events handed to hc_load_back_layer)."""
+
+    def __init__(self, timing: bool = False):
+        self.handle = _V()
+        _hip_check(_hip.hipEventCreateWithFlags(ctypes.byref(self.handle), 0 if timing else 2),
+                   "hipEventCreateWithFlags")
+
+    def wait_on(self, stream) -> None:
+        """Make `stream` (a torch stream) wait for this event."""
+        _hip_check(_hip.hipStreamWaitEvent(_V(stream.cuda_stream), self.handle, 0), "hipStreamWaitEvent")
+
+    def record(self, stream) -> None:
+        _hip_check(_hip.hipEventRecord(self.handle, _V(stream.cuda_stream)), "hipEventRecord")
+
+    def synchronize(self) -> None:
+        _hip_check(_hip.hipEventSynchronize(self.handle), "hipEventSynchronize")
+
+    def query(self) -> bool:
+        return _hip.hipEventQuery(self.handle) == 0
+
+    def elapsed_ms(self, end: "HipEvent") -> float:
+        ms = ctypes.c_float()
+        _hip_check(_hip.hipEventElapsedTime(ctypes.byref(ms), self.handle, end.handle), "hipEventElapsedTime")
+        return float(ms.value)
+
+    def __del__(self):
+        if getattr(self, "handle", None) and self.handle.value:
+            _hip.hipEventDestroy(self.handle)
+            self.handle = _V()
+
+
+# ---------------------------------------------------------------- pinned host memory
+class HostBuffer:
+    """Pinned host memory from hc_host_alloc; .np is a uint8 numpy view of it."""
+
+    def __init__(self, nbytes: int, noncoherent: bool = False):
+        self.nbytes = int(nbytes)
+        self.ptr = _V()
+        check(lib.hc_host_alloc(self.nbytes, 1 if noncoherent else 0, ctypes.byref(self.ptr)), "hc_host_alloc")
+        self.np = np.ctypeslib.as_array((ctypes.c_uint8 * self.nbytes).from_address(self.ptr.value))
+
+    def fill(self, byte: int, stream=None) -> None:
+        """Fill every byte through the device mapping (a HIP memset; plumbing for tests)."""
+        s = _V(stream.cuda_stream) if stream is not None else _V()
+        _hip_check(_hip.hipMemsetAsync(self.ptr, int(byte), self.nbytes, s), "hipMemsetAsync")
+        _hip_check(_hip.hipStreamSynchronize(s), "hipStreamSynchronize")
+
+    def free(self) -> None:
+        if self.ptr.value:
+            self.np = None
+            check(lib.hc_host_free(self.ptr), "hc_host_free")
+            self.ptr = _V()
+
+    def __del__(self):
+        try:
+            self.free()
+        except Exception:
+            pass
+
+
+# ---------------------------------------------------------------- descriptors and pools
+def make_desc(*, layers: int, page_size: int, subs, device_slots: int, host_pages: int,
+              layout: int = HC_LAYOUT_PAGE_FIRST, shard_align: int = 4096, host_ptr: int = 0,
+              host_bytes: int = 0, staging_ptr: int = 0, staging_bytes: int = 0, stream_ptr: int = 0,
+              write_back_mode: int = HC_MODE_AUTO, load_back_mode: int = HC_MODE_AUTO, flags: int = 0,
+              max_ctas: int = 0):
+    """Build an hc_pool_desc.  subs: [(granularity, elem_bytes, [layer device pointers])].
+    Returns (desc, keepalive) -- keep the second value alive as long as desc is used."""
+    d = hc_pool_desc()
+    d.num_layers, d.page_size, d.num_subbufs, d.layout = layers, page_size, len(subs), layout
+    keep = []
+    for b, (gran, elem, ptrs) in enumerate(subs):
+        arr = (ctypes.c_void_p * max(1, len(ptrs)))(*[int(p) for p in ptrs])
+        keep.append(arr)
+        d.sub[b].granularity = gran
+        d.sub[b].reserved = 0
+        d.sub[b].elem_bytes = elem
+        d.sub[b].device_layers = ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p))
+    d.device_slots, d.host_pages, d.shard_align = device_slots, host_pages, shard_align
+    d.host_base, d.host_bytes = host_ptr or None, host_bytes
+    d.staging, d.staging_bytes = staging_ptr or None, staging_bytes
+    d.copy_stream = stream_ptr or None
+    d.write_back_mode, d.load_back_mode, d.flags, d.max_ctas = write_back_mode, load_back_mode, flags, max_ctas
+    return d, keep
+
+
+def host_pool_bytes(desc) -> int:
+    out = ctypes.c_int64()
+    check(lib.hc_host_pool_bytes(ctypes.byref(desc), ctypes.byref(out)), "hc_host_pool_bytes")
+    return out.value
+
+
+def staging_page_bytes(desc) -> int:
+    out = ctypes.c_int64()
+    check(lib.hc_staging_page_bytes(ctypes.byref(desc), ctypes.byref(out)), "hc_staging_page_bytes")
+    return out.value
+
+
+def host_offset(desc, sub: int, page: int, layer: int, row: int) -> int:
+    out = ctypes.c_int64()
+    check(lib.hc_host_offset(ctypes.byref(desc), sub, page, layer, row, ctypes.byref(out)), "hc_host_offset")
+    return out.value
+
+
+def _ptr(x) -> int:
+    """Address of a torch tensor, a numpy array, a HostBuffer or an int."""
+    if x is None:
+        return 0
+    if isinstance(x, int):
+        return x
+    if isinstance(x, HostBuffer):
+        return x.ptr.value
+    if isinstance(x, np.ndarray):
+        return x.ctypes.data
+    return x.data_ptr()
+
+
+class Pool:
+    """Owns one hc_pool handle.  device_layers[b][l] are torch CUDA tensors (or raw
+    addresses); host is a HostBuffer; staging a torch CUDA tensor or None; stream a
+    torch.cuda.Stream (the copy stream)."""
+
+    def __init__(self, *, layers, page_size, subs, device_slots, host_pages, device_layers, host,
+                 stream, layout=HC_LAYOUT_PAGE_FIRST, shard_align=4096, staging=None,
+                 write_back_mode=HC_MODE_AUTO, load_back_mode=HC_MODE_AUTO, flags=0, max_ctas=0):
+        sub_specs = [(g, e, [_ptr(t) for t in device_layers[b]]) for b, (g, e) in enumerate(subs)]
+        self.stream = stream
+        self.desc, self._keep = make_desc(
+            layers=layers, page_size=page_size, subs=sub_specs, device_slots=device_slots,
+            host_pages=host_pages, layout=layout, shard_align=shard_align, host_ptr=_ptr(host),
+            host_bytes=host.nbytes, staging_ptr=_ptr(staging),
+            staging_bytes=(staging.numel() * staging.element_size()) if staging is not None else 0,
+            stream_ptr=stream.cuda_stream if stream is not None else 0,
+            write_back_mode=write_back_mode, load_back_mode=load_back_mode, flags=flags, max_ctas=max_ctas)
+        self._refs = (device_layers, host, staging)
+        self.handle = _V()
+        check(lib.hc_pool_create(ctypes.byref(self.desc), ctypes.byref(self.handle)), "hc_pool_create")
+
+    def mode(self, which: int) -> int:
+        out = ctypes.c_int32()
+        check(lib.hc_pool_mode(self.handle, which, ctypes.byref(out)), "hc_pool_mode")
+        return out.value
+
+    def write_back_all_layers(self, device_idx, host_idx, event: HipEvent | None = None) -> None:
+        """device_idx: int64 CUDA tensor; host_idx: int64 CPU tensor or numpy array."""
+        n = int(device_idx.numel())
+        assert int(host_idx.size if isinstance(host_idx, np.ndarray) else host_idx.numel()) == n
+        check(lib.hc_write_back_all_layers(self.handle, _V(_ptr(device_idx)), _V(_ptr(host_idx)), n,
+                                           event.handle if event else None), "hc_write_back_all_layers")
+
+    def load_back_layer(self, layer: int, host_idx, device_idx, event: HipEvent | None = None) -> None:
+        """host_idx, device_idx: int64 CUDA tensors."""
+        n = int(device_idx.numel())
+        assert int(host_idx.numel()) == n
+        check(lib.hc_load_back_layer(self.handle, layer, _V(_ptr(host_idx)), _V(_ptr(device_idx)), n,
+                                     event.handle if event else None), "hc_load_back_layer")
+
+    def round_trip_check(self, idx_a, idx_b) -> int:
+        out = ctypes.c_int64()
+        n = int(idx_a.numel())
+        check(lib.hc_round_trip_check(self.handle, _V(_ptr(idx_a)), _V(_ptr(idx_b)), n, ctypes.byref(out)),
+              "hc_round_trip_check")
+        return out.value
+
+    def sync(self) -> None:
+        check(lib.hc_pool_sync(self.handle), "hc_pool_sync")
+
+    def kernel_time(self, kind: int, reset: bool = False):
+        n = ctypes.c_int64()
+        ms = ctypes.c_double()
+        check(lib.hc_pool_kernel_time(self.handle, kind, 1 if reset else 0, ctypes.byref(n), ctypes.byref(ms)),
+              "hc_pool_kernel_time")
+        return n.value, ms.value
+
+    def close(self) -> None:
+        if self.handle.value:
+            check(lib.hc_pool_destroy(self.handle), "hc_pool_destroy")
+            self.handle = _V()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

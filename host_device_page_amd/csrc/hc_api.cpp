@@ -1,0 +1,765 @@
+// C ABI of libhc.so: pool lifetime, the write-back planner, transfer orchestration
+// on the copy stream, the layer-done event chain and measurement hooks.
+//
+// Write-back (hybrid-pool write-back page, sglang PR 28434 summary): the host
+// index list stays on the CPU, as in the controller change that keeps host
+// indices CPU-side; the CPU validates it once per burst and uploads a compact
+// plan.  Zero-copy mode then runs one kernel over all tokens, layers and
+// sub-buffers that writes straight into the pinned host pool.  Staged mode
+// gathers chunks of whole host pages into the device staging buffer as exact
+// host page images (one launch per chunk, all layers) and moves each page with
+// the copy engines; tokens of partially named pages go through the zero-copy
+// kernel so rows the list does not name are never overwritten.
+//
+// Load-back (loader-thread page, sglang PR 38472, Motivation): one kernel per
+// layer reads device-resident index lists, so the CPU builds no per-layer
+// descriptor; the layer-done event is recorded right after it, and recorded even
+// when the call fails so that a consumer waiting on it cannot hang (the same
+// page, Modifications: loader failure still completes every layer event).
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <string>
+#include <vector>
+
+#include "hc_internal.h"
+
+using hc::Geom;
+using hc::Layout;
+
+namespace {
+
+thread_local std::string g_err;
+
+int set_err(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+#define HIP_TRY(call)                                                                  \
+  do {                                                                                 \
+    hipError_t e_ = (call);                                                            \
+    if (e_ != hipSuccess) return set_err(HC_ERR_HIP, "%s failed: %s", #call, hipGetErrorString(e_)); \
+  } while (0)
+
+constexpr int kKinds = 6;  // gather, zc write, zc read, pads, compare, copy engine
+constexpr int32_t kDefaultMaxCtas = 256;
+
+struct PlanBuf {
+  uint8_t* h = nullptr;   // pinned
+  uint8_t* d = nullptr;   // device
+  int64_t cap = 0;
+  hipEvent_t ev = nullptr;
+  bool pending = false;
+};
+
+struct Region {
+  uint8_t* dst;
+  const uint8_t* src;
+  int64_t len;
+};
+
+struct Chunk {
+  int64_t t0, t1;
+  size_t r0, r1;  // regions [r0, r1)
+};
+
+struct TimedLaunch {
+  int kind;
+  hipEvent_t a, b;
+};
+
+}  // namespace
+
+struct hc_pool {
+  Layout lay;
+  Geom geom;
+  int device = 0;
+  hipStream_t stream = nullptr;
+  int32_t wb_mode = HC_MODE_ZEROCOPY;
+  int32_t lb_mode = HC_MODE_ZEROCOPY;
+  int32_t flags = 0;
+  int32_t max_ctas = kDefaultMaxCtas;
+  uint8_t* host = nullptr;      // host pool (host address == device address on ROCm)
+  uint8_t* staging = nullptr;
+  int64_t staging_bytes = 0;
+  int64_t chunk_pages = 0;
+  uint64_t* d_tables = nullptr; // [nsub][L] layer addresses
+  int32_t* d_err = nullptr;
+  unsigned long long* d_counter = nullptr;
+  unsigned long long* h_counter = nullptr;  // pinned
+  int32_t* h_err = nullptr;                 // pinned
+  // planner scratch
+  std::vector<int32_t> page_slot;   // [H] staging slot of a page in the open chunk, -1 otherwise
+  std::vector<uint64_t> seen;       // bitmap over host tokens (distinctness)
+  std::vector<uint64_t> page_seen;  // bitmap over host pages
+  std::vector<int64_t> slot_page;
+  std::vector<int32_t> slot_rows;
+  std::vector<Region> regions;
+  std::vector<Chunk> chunks;
+  PlanBuf plan[2];
+  int plan_cur = 0;
+  // measurement
+  std::vector<hipEvent_t> free_events;
+  std::vector<TimedLaunch> pending_timed;
+  int64_t kind_launches[kKinds] = {};
+  double kind_ms[kKinds] = {};
+};
+
+namespace {
+
+int check_device_ptr(const void* p, const char* what) {
+  hipPointerAttribute_t attr;
+  hipError_t e = hipPointerGetAttributes(&attr, p);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return set_err(HC_ERR_INVALID, "%s is not memory known to HIP", what);
+  }
+  if (attr.type != hipMemoryTypeDevice)
+    return set_err(HC_ERR_INVALID, "%s must be device memory", what);
+  return HC_OK;
+}
+
+int use_device(hc_pool* p) {
+  int cur = -1;
+  HIP_TRY(hipGetDevice(&cur));
+  if (cur != p->device) HIP_TRY(hipSetDevice(p->device));
+  return HC_OK;
+}
+
+hipEvent_t take_event(hc_pool* p) {
+  if (!p->free_events.empty()) {
+    hipEvent_t e = p->free_events.back();
+    p->free_events.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Brackets one launch with events when the pool profiles.
+struct Timer {
+  hc_pool* p;
+  int kind;
+  hipEvent_t a = nullptr;
+  Timer(hc_pool* pool, int k) : p(pool), kind(k) {
+    if (p->flags & HC_FLAG_PROFILE) {
+      a = take_event(p);
+      if (a) (void)hipEventRecord(a, p->stream);
+    }
+  }
+  void done() {
+    if (!a) return;
+    hipEvent_t b = take_event(p);
+    if (!b) return;
+    (void)hipEventRecord(b, p->stream);
+    p->pending_timed.push_back({kind, a, b});
+    a = nullptr;
+  }
+};
+
+int harvest_timing(hc_pool* p) {
+  if (p->pending_timed.empty()) return HC_OK;
+  HIP_TRY(hipStreamSynchronize(p->stream));
+  for (auto& t : p->pending_timed) {
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, t.a, t.b) == hipSuccess) {
+      p->kind_launches[t.kind] += 1;
+      p->kind_ms[t.kind] += ms;
+    }
+    p->free_events.push_back(t.a);
+    p->free_events.push_back(t.b);
+  }
+  p->pending_timed.clear();
+  return HC_OK;
+}
+
+uint64_t magic_for(uint32_t vecs) {
+  // ceil(2^40 / vecs)
+  const uint64_t one = (uint64_t)1 << 40;
+  return (one + vecs - 1) / vecs;
+}
+
+void fill_geom(hc_pool* p) {
+  const Layout& L = p->lay;
+  Geom& g = p->geom;
+  memset(&g, 0, sizeof(g));
+  g.nsub = L.nsub;
+  g.L = L.L;
+  g.P = L.P;
+  g.validate = (p->flags & HC_FLAG_VALIDATE) ? 1 : 0;
+  g.S = L.S;
+  g.host_tokens = L.H * L.P;
+  g.img_bytes = L.stride;
+  g.payload_bytes = L.payload;
+  g.pad_bytes = L.stride - L.payload;
+  for (int b = 0; b < L.nsub; b++) {
+    hc::SubGeom& s = g.sub[b];
+    s.layers = p->d_tables + (size_t)b * L.L;
+    s.elem = L.elem[b];
+    s.vecs = (uint32_t)(L.elem[b] / 16);
+    s.gran = L.gran[b];
+    s.vec_magic = magic_for(s.vecs);
+    s.host_region = L.host_region[b];
+    s.host_page_stride = L.host_page_stride[b];
+    s.layer_stride = L.layer_stride[b];
+    s.img_off = L.img_off[b];
+  }
+}
+
+// Makes plan buffer `cur` hold at least `bytes` (pinned + device), waiting for its
+// previous upload to finish before the CPU rewrites it.
+int plan_reserve(hc_pool* p, int64_t bytes) {
+  PlanBuf& pb = p->plan[p->plan_cur];
+  if (pb.pending) {
+    HIP_TRY(hipEventSynchronize(pb.ev));
+    pb.pending = false;
+  }
+  if (pb.cap >= bytes) return HC_OK;
+  // the device copy may still be read by queued kernels: drain before freeing
+  HIP_TRY(hipStreamSynchronize(p->stream));
+  if (pb.h) HIP_TRY(hipHostFree(pb.h));
+  if (pb.d) HIP_TRY(hipFree(pb.d));
+  pb.h = nullptr;
+  pb.d = nullptr;
+  pb.cap = 0;
+  int64_t cap = std::max<int64_t>(bytes, 1 << 16);
+  cap = (cap + 4095) / 4096 * 4096;
+  HIP_TRY(hipHostMalloc((void**)&pb.h, (size_t)cap, hipHostMallocDefault));
+  HIP_TRY(hipMalloc((void**)&pb.d, (size_t)cap));
+  if (!pb.ev) HIP_TRY(hipEventCreateWithFlags(&pb.ev, hipEventDisableTiming));
+  pb.cap = cap;
+  return HC_OK;
+}
+
+int plan_upload(hc_pool* p, int64_t bytes) {
+  PlanBuf& pb = p->plan[p->plan_cur];
+  if (bytes > 0) {
+    HIP_TRY(hipMemcpyAsync(pb.d, pb.h, (size_t)bytes, hipMemcpyHostToDevice, p->stream));
+    HIP_TRY(hipEventRecord(pb.ev, p->stream));
+    pb.pending = true;
+  }
+  return HC_OK;
+}
+
+inline int64_t align16(int64_t x) { return (x + 15) / 16 * 16; }
+
+inline bool test_and_set(std::vector<uint64_t>& bits, int64_t k) {
+  uint64_t& w = bits[(size_t)(k >> 6)];
+  const uint64_t m = (uint64_t)1 << (k & 63);
+  const bool was = (w & m) != 0;
+  w |= m;
+  return was;
+}
+
+inline void clear_bit(std::vector<uint64_t>& bits, int64_t k) { bits[(size_t)(k >> 6)] &= ~((uint64_t)1 << (k & 63)); }
+
+// Range and distinctness of the host index list (CPU-resident for write-back).
+int validate_host_idx(hc_pool* p, const int64_t* h, int64_t n) {
+  const int64_t tokens = p->lay.H * p->lay.P;
+  int64_t bad = -1;
+  int64_t i = 0;
+  for (; i < n; i++) {
+    const int64_t x = h[i];
+    if (x < 0 || x >= tokens) {
+      bad = i;
+      break;
+    }
+    if (test_and_set(p->seen, x)) {
+      bad = i;
+      break;
+    }
+  }
+  for (int64_t j = 0; j < i; j++) clear_bit(p->seen, h[j]);
+  if (bad >= 0) {
+    const int64_t x = h[bad];
+    if (x < 0 || x >= tokens)
+      return set_err(HC_ERR_INVALID, "host_idx[%lld] = %lld out of range [0, %lld)", (long long)bad, (long long)x,
+                     (long long)tokens);
+    return set_err(HC_ERR_INVALID, "host_idx[%lld] = %lld repeats an earlier entry", (long long)bad, (long long)x);
+  }
+  if (p->lay.has_blocks) {
+    // every named page whole: count rows per page
+    std::vector<int32_t> rows;
+    rows.assign((size_t)p->lay.H, 0);
+    for (int64_t j = 0; j < n; j++) rows[(size_t)(h[j] / p->lay.P)]++;
+    for (int64_t j = 0; j < n; j++) {
+      if (rows[(size_t)(h[j] / p->lay.P)] != p->lay.P)
+        return set_err(HC_ERR_INVALID, "page %lld is named partially; page-block sub-buffers need whole pages",
+                       (long long)(h[j] / p->lay.P));
+    }
+  }
+  return HC_OK;
+}
+
+void emit_region(hc_pool* p, uint8_t* dst, const uint8_t* src, int64_t len) {
+  if (!p->regions.empty()) {
+    Region& r = p->regions.back();
+    if (r.dst + r.len == dst && r.src + r.len == src) {
+      r.len += len;
+      return;
+    }
+  }
+  p->regions.push_back({dst, src, len});
+}
+
+// Staged plan: chunks of at most chunk_pages staging slots walked in list order.
+// Writes srow (int32 per token), ztok (tokens of partially named pages) and pads
+// (pages whose shard pad the zero-copy pass must clear) into the pinned plan buffer.
+void plan_staged(hc_pool* p, const int64_t* h, int64_t n, int32_t* srow, int32_t* ztok, int64_t* nz,
+                 int64_t* pads, int64_t* npads) {
+  const Layout& L = p->lay;
+  const int64_t C = p->chunk_pages;
+  p->regions.clear();
+  p->chunks.clear();
+  p->slot_page.assign((size_t)C, -1);
+  p->slot_rows.assign((size_t)C, 0);
+  int64_t nslots = 0, t0 = 0;
+  *nz = 0;
+  *npads = 0;
+  auto close_chunk = [&](int64_t t1) {
+    const size_t r0 = p->regions.size();
+    for (int64_t s = 0; s < nslots; s++) {
+      const int64_t page = p->slot_page[(size_t)s];
+      if (p->slot_rows[(size_t)s] == L.P) {
+        const uint8_t* img = p->staging + s * L.stride;
+        if (L.layout == HC_LAYOUT_KV_SPLIT_SHARD) {
+          emit_region(p, p->host + page * L.stride, img, L.stride);
+        } else {
+          for (int b = 0; b < L.nsub; b++)
+            emit_region(p, p->host + L.host_region[b] + page * L.subpage[b], img + L.img_off[b], L.subpage[b]);
+        }
+      } else if (L.layout == HC_LAYOUT_KV_SPLIT_SHARD && L.stride > L.payload) {
+        pads[(*npads)++] = page;
+      }
+      p->page_slot[(size_t)page] = -1;
+    }
+    for (int64_t i = t0; i < t1; i++) {
+      const int32_t s = srow[i] / L.P;
+      if (p->slot_rows[(size_t)s] != L.P) {
+        srow[i] = -1;
+        ztok[(*nz)++] = (int32_t)i;
+      }
+    }
+    p->chunks.push_back({t0, t1, r0, p->regions.size()});
+    t0 = t1;
+    nslots = 0;
+  };
+  for (int64_t i = 0; i < n; i++) {
+    const int64_t page = h[i] / L.P;
+    const int32_t r = (int32_t)(h[i] - page * L.P);
+    int32_t s = p->page_slot[(size_t)page];
+    if (s < 0) {
+      if (nslots == C) close_chunk(i);
+      s = (int32_t)nslots++;
+      p->page_slot[(size_t)page] = s;
+      p->slot_page[(size_t)s] = page;
+      p->slot_rows[(size_t)s] = 0;
+    }
+    p->slot_rows[(size_t)s]++;
+    srow[i] = s * L.P + r;
+  }
+  close_chunk(n);
+}
+
+// Distinct pages named by h (shard pads for the zero-copy write-back).
+int64_t distinct_pages(hc_pool* p, const int64_t* h, int64_t n, int64_t* pages) {
+  int64_t k = 0;
+  for (int64_t i = 0; i < n; i++) {
+    const int64_t page = h[i] / p->lay.P;
+    if (!test_and_set(p->page_seen, page)) pages[k++] = page;
+  }
+  for (int64_t j = 0; j < k; j++) clear_bit(p->page_seen, pages[j]);
+  return k;
+}
+
+int record_event(void* ev, hipStream_t s) {
+  if (!ev) return HC_OK;
+  hipError_t e = hipEventRecord((hipEvent_t)ev, s);
+  if (e != hipSuccess) return set_err(HC_ERR_HIP, "hipEventRecord failed: %s", hipGetErrorString(e));
+  return HC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int hc_version(void) { return 1; }
+
+const char* hc_last_error(void) { return g_err.c_str(); }
+
+int hc_desc_check(const hc_pool_desc* desc) {
+  Layout L;
+  char msg[256];
+  int rc = hc::layout_from_desc(desc, &L, msg, sizeof(msg));
+  if (rc != HC_OK) return set_err(rc, "%s", msg);
+  if (desc->write_back_mode < HC_MODE_AUTO || desc->write_back_mode > HC_MODE_ZEROCOPY ||
+      desc->load_back_mode < HC_MODE_AUTO || desc->load_back_mode > HC_MODE_ZEROCOPY)
+    return set_err(HC_ERR_INVALID, "unknown transfer mode");
+  if (desc->load_back_mode == HC_MODE_STAGED)
+    return set_err(HC_ERR_UNSUPPORTED,
+                   "staged load-back is not provided: per-(page, layer) copy-engine transfers run far below "
+                   "the host-link rate, the zero-copy kernel does not");
+  if (desc->flags & ~(HC_FLAG_VALIDATE | HC_FLAG_PROFILE)) return set_err(HC_ERR_INVALID, "unknown flags");
+  if (desc->max_ctas < 0) return set_err(HC_ERR_INVALID, "max_ctas must be >= 0");
+  if (!desc->host_base) return set_err(HC_ERR_INVALID, "host_base is null");
+  if (((uintptr_t)desc->host_base) % 16 != 0) return set_err(HC_ERR_UNSUPPORTED, "host_base must be 16-byte aligned");
+  if (desc->host_bytes < L.host_bytes)
+    return set_err(HC_ERR_INVALID, "host_bytes %lld below the layout's %lld", (long long)desc->host_bytes,
+                   (long long)L.host_bytes);
+  for (int b = 0; b < L.nsub; b++) {
+    if (!desc->sub[b].device_layers) return set_err(HC_ERR_INVALID, "sub-buffer %d: device_layers is null", b);
+    for (int l = 0; l < L.L; l++) {
+      const void* q = desc->sub[b].device_layers[l];
+      if (!q) return set_err(HC_ERR_INVALID, "sub-buffer %d layer %d: null device pointer", b, l);
+      if (((uintptr_t)q) % 16 != 0)
+        return set_err(HC_ERR_UNSUPPORTED, "sub-buffer %d layer %d: device pointer not 16-byte aligned", b, l);
+    }
+  }
+  if (desc->write_back_mode == HC_MODE_STAGED) {
+    if (!desc->staging) return set_err(HC_ERR_INVALID, "staged write-back needs a staging buffer");
+    if (((uintptr_t)desc->staging) % 16 != 0) return set_err(HC_ERR_UNSUPPORTED, "staging must be 16-byte aligned");
+    if (desc->staging_bytes < L.stride)
+      return set_err(HC_ERR_INVALID, "staging_bytes %lld below one page image (%lld bytes)",
+                     (long long)desc->staging_bytes, (long long)L.stride);
+  }
+  return HC_OK;
+}
+
+int hc_host_pool_bytes(const hc_pool_desc* desc, int64_t* out_bytes) {
+  if (!out_bytes) return set_err(HC_ERR_INVALID, "out_bytes is null");
+  Layout L;
+  char msg[256];
+  int rc = hc::layout_from_desc(desc, &L, msg, sizeof(msg));
+  if (rc != HC_OK) return set_err(rc, "%s", msg);
+  *out_bytes = L.host_bytes;
+  return HC_OK;
+}
+
+int hc_staging_page_bytes(const hc_pool_desc* desc, int64_t* out_bytes) {
+  if (!out_bytes) return set_err(HC_ERR_INVALID, "out_bytes is null");
+  Layout L;
+  char msg[256];
+  int rc = hc::layout_from_desc(desc, &L, msg, sizeof(msg));
+  if (rc != HC_OK) return set_err(rc, "%s", msg);
+  *out_bytes = L.stride;
+  return HC_OK;
+}
+
+int hc_host_offset(const hc_pool_desc* desc, int32_t sub, int64_t page, int32_t layer, int32_t row,
+                   int64_t* out_offset) {
+  if (!out_offset) return set_err(HC_ERR_INVALID, "out_offset is null");
+  Layout L;
+  char msg[256];
+  int rc = hc::layout_from_desc(desc, &L, msg, sizeof(msg));
+  if (rc != HC_OK) return set_err(rc, "%s", msg);
+  if (sub < 0 || sub >= L.nsub || page < 0 || page >= L.H || layer < 0 || layer >= L.L || row < 0 || row >= L.P)
+    return set_err(HC_ERR_INVALID, "coordinate out of range");
+  *out_offset = hc::layout_host_offset(L, sub, page, layer, row);
+  return HC_OK;
+}
+
+int hc_host_alloc(int64_t bytes, int32_t flags, void** out) {
+  if (!out || bytes <= 0) return set_err(HC_ERR_INVALID, "hc_host_alloc: bad size or null out");
+  if (flags != 0 && flags != 1) return set_err(HC_ERR_INVALID, "hc_host_alloc: flags must be 0 or 1");
+  void* p = nullptr;
+  const unsigned hf = hipHostMallocMapped | (flags ? hipHostMallocNonCoherent : hipHostMallocCoherent);
+  HIP_TRY(hipHostMalloc(&p, (size_t)bytes, hf));
+  // zero through the device mapping (the host link is faster than CPU first touch)
+  hipError_t e = hipMemset(p, 0, (size_t)bytes);
+  if (e != hipSuccess) {
+    (void)hipHostFree(p);
+    return set_err(HC_ERR_HIP, "hipMemset of pinned memory failed: %s", hipGetErrorString(e));
+  }
+  *out = p;
+  return HC_OK;
+}
+
+int hc_host_free(void* ptr) {
+  if (!ptr) return HC_OK;
+  HIP_TRY(hipHostFree(ptr));
+  return HC_OK;
+}
+
+int hc_pool_create(const hc_pool_desc* desc, hc_pool** out) {
+  if (!out) return set_err(HC_ERR_INVALID, "out is null");
+  *out = nullptr;
+  int rc = hc_desc_check(desc);
+  if (rc != HC_OK) return rc;
+  hc_pool* p = new (std::nothrow) hc_pool();
+  if (!p) return set_err(HC_ERR_NOMEM, "pool allocation failed");
+  char msg[256];
+  hc::layout_from_desc(desc, &p->lay, msg, sizeof(msg));
+  const Layout& L = p->lay;
+  auto bail = [&](int code) {
+    hc_pool_destroy(p);
+    return code;
+  };
+  if (hipGetDevice(&p->device) != hipSuccess) return bail(set_err(HC_ERR_HIP, "no HIP device"));
+  p->stream = (hipStream_t)desc->copy_stream;
+  p->flags = desc->flags;
+  p->max_ctas = desc->max_ctas > 0 ? desc->max_ctas : kDefaultMaxCtas;
+  // memory kinds
+  {
+    void* dptr = nullptr;
+    if (hipHostGetDevicePointer(&dptr, desc->host_base, 0) != hipSuccess || !dptr) {
+      (void)hipGetLastError();
+      return bail(set_err(HC_ERR_INVALID, "host_base is not pinned (page-locked) host memory"));
+    }
+    p->host = (uint8_t*)dptr;
+  }
+  for (int b = 0; b < L.nsub; b++)
+    for (int l = 0; l < L.L; l++) {
+      rc = check_device_ptr(desc->sub[b].device_layers[l], "device layer");
+      if (rc != HC_OK) return bail(rc);
+    }
+  // modes: zero-copy is the measured default for both directions
+  p->wb_mode = desc->write_back_mode == HC_MODE_STAGED ? HC_MODE_STAGED : HC_MODE_ZEROCOPY;
+  p->lb_mode = HC_MODE_ZEROCOPY;
+  if (p->wb_mode == HC_MODE_STAGED) {
+    rc = check_device_ptr(desc->staging, "staging");
+    if (rc != HC_OK) return bail(rc);
+    p->staging = (uint8_t*)desc->staging;
+    p->staging_bytes = desc->staging_bytes;
+    p->chunk_pages = std::min<int64_t>(desc->staging_bytes / L.stride, (int64_t)1 << 20);
+    if (p->chunk_pages * L.P >= ((int64_t)1 << 31)) p->chunk_pages = (((int64_t)1 << 31) - 1) / L.P;
+  }
+  // device tables and scratch
+  std::vector<uint64_t> tables((size_t)L.nsub * L.L);
+  for (int b = 0; b < L.nsub; b++)
+    for (int l = 0; l < L.L; l++) tables[(size_t)b * L.L + l] = (uint64_t)(uintptr_t)desc->sub[b].device_layers[l];
+  if (hipMalloc((void**)&p->d_tables, tables.size() * sizeof(uint64_t)) != hipSuccess)
+    return bail(set_err(HC_ERR_HIP, "hipMalloc of layer tables failed"));
+  if (hipMalloc((void**)&p->d_err, 64) != hipSuccess) return bail(set_err(HC_ERR_HIP, "hipMalloc failed"));
+  p->d_counter = (unsigned long long*)((uint8_t*)p->d_err + 32);
+  if (hipHostMalloc((void**)&p->h_counter, 64, hipHostMallocDefault) != hipSuccess)
+    return bail(set_err(HC_ERR_HIP, "hipHostMalloc failed"));
+  p->h_err = (int32_t*)((uint8_t*)p->h_counter + 32);
+  if (hipMemcpyAsync(p->d_tables, tables.data(), tables.size() * sizeof(uint64_t), hipMemcpyHostToDevice,
+                     p->stream) != hipSuccess ||
+      hipMemsetAsync(p->d_err, 0, 64, p->stream) != hipSuccess)
+    return bail(set_err(HC_ERR_HIP, "initial copies failed"));
+  if (p->staging && L.stride > L.payload) {
+    // staging page images carry the shard pad, which stays zero
+    if (hipMemsetAsync(p->staging, 0, (size_t)(p->chunk_pages * L.stride), p->stream) != hipSuccess)
+      return bail(set_err(HC_ERR_HIP, "staging clear failed"));
+  }
+  if (hipStreamSynchronize(p->stream) != hipSuccess) return bail(set_err(HC_ERR_HIP, "stream sync failed"));
+  p->page_slot.assign((size_t)L.H, -1);
+  p->seen.assign((size_t)((L.H * L.P + 63) / 64), 0);
+  p->page_seen.assign((size_t)((L.H + 63) / 64), 0);
+  fill_geom(p);
+  *out = p;
+  return HC_OK;
+}
+
+int hc_pool_destroy(hc_pool* p) {
+  if (!p) return HC_OK;
+  int rc = HC_OK;
+  if (p->stream || p->d_tables) {
+    if (hipStreamSynchronize(p->stream) != hipSuccess) rc = set_err(HC_ERR_HIP, "stream sync failed in destroy");
+  }
+  for (auto& pb : p->plan) {
+    if (pb.h) (void)hipHostFree(pb.h);
+    if (pb.d) (void)hipFree(pb.d);
+    if (pb.ev) (void)hipEventDestroy(pb.ev);
+  }
+  for (auto& t : p->pending_timed) {
+    (void)hipEventDestroy(t.a);
+    (void)hipEventDestroy(t.b);
+  }
+  for (auto e : p->free_events) (void)hipEventDestroy(e);
+  if (p->d_tables) (void)hipFree(p->d_tables);
+  if (p->d_err) (void)hipFree(p->d_err);
+  if (p->h_counter) (void)hipHostFree(p->h_counter);
+  delete p;
+  return rc;
+}
+
+int hc_pool_mode(const hc_pool* p, int32_t which, int32_t* out_mode) {
+  if (!p || !out_mode) return set_err(HC_ERR_INVALID, "null argument");
+  if (which == 0) *out_mode = p->wb_mode;
+  else if (which == 1) *out_mode = p->lb_mode;
+  else return set_err(HC_ERR_INVALID, "which must be 0 (write-back) or 1 (load-back)");
+  return HC_OK;
+}
+
+int hc_pool_sync(hc_pool* p) {
+  if (!p) return set_err(HC_ERR_INVALID, "pool is null");
+  int rc = use_device(p);
+  if (rc != HC_OK) return rc;
+  HIP_TRY(hipMemcpyAsync(p->h_err, p->d_err, sizeof(int32_t), hipMemcpyDeviceToHost, p->stream));
+  HIP_TRY(hipStreamSynchronize(p->stream));
+  const int32_t e = *p->h_err;
+  if (e) {
+    HIP_TRY(hipMemsetAsync(p->d_err, 0, sizeof(int32_t), p->stream));
+    HIP_TRY(hipStreamSynchronize(p->stream));
+    return set_err(HC_ERR_DEVICE, "device-side check flagged an index list (code %d: %s)", e,
+                   (e & 1) ? "index out of range" : "page-block rows not one whole device page");
+  }
+  return HC_OK;
+}
+
+int hc_write_back_all_layers(hc_pool* p, const int64_t* device_idx, const int64_t* host_idx, int64_t n,
+                             void* event) {
+  if (!p) return set_err(HC_ERR_INVALID, "pool is null");
+  int rc = use_device(p);
+  if (rc != HC_OK) return rc;
+  auto finish = [&](int code) {
+    int r2 = record_event(event, p->stream);
+    return code != HC_OK ? code : r2;
+  };
+  if (n < 0) return finish(set_err(HC_ERR_INVALID, "n must be >= 0"));
+  if (n == 0) return finish(HC_OK);
+  if (!device_idx || !host_idx) return finish(set_err(HC_ERR_INVALID, "null index list"));
+  if (n >= ((int64_t)1 << 31)) return finish(set_err(HC_ERR_INVALID, "n must be below 2^31"));
+  rc = validate_host_idx(p, host_idx, n);
+  if (rc != HC_OK) return finish(rc);
+  const Layout& L = p->lay;
+  const bool staged = p->wb_mode == HC_MODE_STAGED;
+  // plan buffer layout: hidx int64[n] | pads int64[n] | srow int32[n] | ztok int32[n]
+  const int64_t o_hidx = 0;
+  const int64_t o_pads = align16(o_hidx + 8 * n);
+  const int64_t o_srow = align16(o_pads + 8 * n);
+  const int64_t o_ztok = align16(o_srow + 4 * n);
+  const int64_t bytes = align16(o_ztok + 4 * n);
+  rc = plan_reserve(p, bytes);
+  if (rc != HC_OK) return finish(rc);
+  PlanBuf& pb = p->plan[p->plan_cur];
+  int64_t* hidx = (int64_t*)(pb.h + o_hidx);
+  int64_t* pads = (int64_t*)(pb.h + o_pads);
+  int32_t* srow = (int32_t*)(pb.h + o_srow);
+  int32_t* ztok = (int32_t*)(pb.h + o_ztok);
+  memcpy(hidx, host_idx, (size_t)(8 * n));
+  int64_t nz = 0, npads = 0;
+  if (staged) {
+    plan_staged(p, host_idx, n, srow, ztok, &nz, pads, &npads);
+  } else if (L.layout == HC_LAYOUT_KV_SPLIT_SHARD && L.stride > L.payload) {
+    npads = distinct_pages(p, host_idx, n, pads);
+  }
+  const int64_t upload = staged ? bytes : align16(o_pads + 8 * npads);
+  rc = plan_upload(p, upload);
+  if (rc != HC_OK) return finish(rc);
+  const int64_t* d_hidx = (const int64_t*)(pb.d + o_hidx);
+  const int64_t* d_pads = (const int64_t*)(pb.d + o_pads);
+  const int32_t* d_srow = (const int32_t*)(pb.d + o_srow);
+  const int32_t* d_ztok = (const int32_t*)(pb.d + o_ztok);
+  p->plan_cur ^= 1;
+  hipError_t e = hipSuccess;
+  if (staged) {
+    for (const Chunk& c : p->chunks) {
+      {
+        Timer t(p, 0);
+        e = hc::launch_gather_stage(p->geom, device_idx, d_srow, c.t0, c.t1 - c.t0, p->staging, p->d_err, p->stream);
+        t.done();
+      }
+      if (e != hipSuccess) return finish(set_err(HC_ERR_HIP, "gather launch failed: %s", hipGetErrorString(e)));
+      if (c.r1 > c.r0) {
+        Timer t(p, 5);
+        for (size_t r = c.r0; r < c.r1 && e == hipSuccess; r++) {
+          const Region& g = p->regions[r];
+          e = hipMemcpyAsync(g.dst, g.src, (size_t)g.len, hipMemcpyDeviceToHost, p->stream);
+        }
+        t.done();
+        if (e != hipSuccess) return finish(set_err(HC_ERR_HIP, "hipMemcpyAsync failed: %s", hipGetErrorString(e)));
+      }
+    }
+    if (nz > 0) {
+      Timer t(p, 1);
+      e = hc::launch_zc_write(p->geom, device_idx, d_hidx, d_ztok, nz, p->host, p->d_err, p->max_ctas, p->stream);
+      t.done();
+      if (e != hipSuccess) return finish(set_err(HC_ERR_HIP, "zero-copy launch failed: %s", hipGetErrorString(e)));
+    }
+  } else {
+    Timer t(p, 1);
+    e = hc::launch_zc_write(p->geom, device_idx, d_hidx, nullptr, n, p->host, p->d_err, p->max_ctas, p->stream);
+    t.done();
+    if (e != hipSuccess) return finish(set_err(HC_ERR_HIP, "zero-copy launch failed: %s", hipGetErrorString(e)));
+  }
+  if (npads > 0) {
+    Timer t(p, 3);
+    e = hc::launch_zero_pads(p->host, d_pads, npads, L.stride, L.payload, L.stride - L.payload, p->stream);
+    t.done();
+    if (e != hipSuccess) return finish(set_err(HC_ERR_HIP, "pad launch failed: %s", hipGetErrorString(e)));
+  }
+  return finish(HC_OK);
+}
+
+int hc_load_back_layer(hc_pool* p, int32_t layer, const int64_t* host_idx, const int64_t* device_idx, int64_t n,
+                       void* event) {
+  if (!p) {
+    // still complete the layer event so a waiting consumer is released
+    if (event) (void)hipEventRecord((hipEvent_t)event, nullptr);
+    return set_err(HC_ERR_INVALID, "pool is null");
+  }
+  int rc = use_device(p);
+  auto finish = [&](int code) {
+    int r2 = record_event(event, p->stream);
+    return code != HC_OK ? code : r2;
+  };
+  if (rc != HC_OK) return finish(rc);
+  if (layer < 0 || layer >= p->lay.L)
+    return finish(set_err(HC_ERR_INVALID, "layer %d out of range [0, %d)", layer, p->lay.L));
+  if (n < 0) return finish(set_err(HC_ERR_INVALID, "n must be >= 0"));
+  if (n == 0) return finish(HC_OK);
+  if (!host_idx || !device_idx) return finish(set_err(HC_ERR_INVALID, "null index list"));
+  if (p->lay.has_blocks && n % p->lay.P != 0)
+    return finish(set_err(HC_ERR_INVALID, "page-block sub-buffers need whole pages (n %% page_size != 0)"));
+  hipError_t e;
+  {
+    Timer t(p, 2);
+    e = hc::launch_zc_read(p->geom, layer, host_idx, device_idx, n, p->host, p->d_err, p->max_ctas, p->stream);
+    t.done();
+  }
+  if (e != hipSuccess) return finish(set_err(HC_ERR_HIP, "load-back launch failed: %s", hipGetErrorString(e)));
+  return finish(HC_OK);
+}
+
+int hc_round_trip_check(hc_pool* p, const int64_t* idx_a, const int64_t* idx_b, int64_t n,
+                        int64_t* mismatched_units) {
+  if (!p || !mismatched_units) return set_err(HC_ERR_INVALID, "null argument");
+  int rc = use_device(p);
+  if (rc != HC_OK) return rc;
+  if (n < 0) return set_err(HC_ERR_INVALID, "n must be >= 0");
+  if (n > 0 && (!idx_a || !idx_b)) return set_err(HC_ERR_INVALID, "null index list");
+  HIP_TRY(hipMemsetAsync(p->d_counter, 0, sizeof(unsigned long long), p->stream));
+  if (n > 0) {
+    Timer t(p, 4);
+    hipError_t e = hc::launch_compare(p->geom, idx_a, idx_b, n, p->d_counter, p->d_err, p->stream);
+    t.done();
+    if (e != hipSuccess) return set_err(HC_ERR_HIP, "compare launch failed: %s", hipGetErrorString(e));
+  }
+  HIP_TRY(hipMemcpyAsync(p->h_counter, p->d_counter, sizeof(unsigned long long), hipMemcpyDeviceToHost, p->stream));
+  rc = hc_pool_sync(p);
+  *mismatched_units = (int64_t)*p->h_counter;
+  return rc;
+}
+
+int hc_pool_kernel_time(hc_pool* p, int32_t kind, int32_t reset, int64_t* launches, double* total_ms) {
+  if (!p || !launches || !total_ms) return set_err(HC_ERR_INVALID, "null argument");
+  if (kind < 0 || kind >= kKinds) return set_err(HC_ERR_INVALID, "kind out of range");
+  int rc = use_device(p);
+  if (rc != HC_OK) return rc;
+  rc = harvest_timing(p);
+  if (rc != HC_OK) return rc;
+  *launches = p->kind_launches[kind];
+  *total_ms = p->kind_ms[kind];
+  if (reset) {
+    for (int k = 0; k < kKinds; k++) {
+      p->kind_launches[k] = 0;
+      p->kind_ms[k] = 0.0;
+    }
+  }
+  return HC_OK;
+}
+
+}  // extern "C"

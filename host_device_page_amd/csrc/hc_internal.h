@@ -1,0 +1,75 @@
+// Internal declarations shared by the host-side API (hc_api.cpp) and the kernels
+// (hc_kernels.hip).  Not part of the public ABI.
+#pragma once
+
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+#include "hc.h"
+
+namespace hc {
+
+// Geometry of one sub-buffer as the kernels see it.  Every byte offset is int64.
+struct SubGeom {
+  const uint64_t* layers;  // device array [L] of layer base addresses
+  int64_t elem;            // bytes per token row / page block
+  uint32_t vecs;           // elem / 16
+  int32_t gran;            // HC_TOKEN_ROWS or HC_PAGE_BLOCKS
+  uint64_t vec_magic;      // ceil(2^40 / vecs): q = (u * magic) >> 40 == u / vecs for u < 2^20
+  int64_t host_region;     // page-first: start of this sub-buffer's region; shard: offset inside a shard
+  int64_t host_page_stride;// bytes from page p to page p+1 of this sub-buffer in the host pool
+  int64_t layer_stride;    // bytes from layer l to l+1 inside one page (P*elem rows, elem blocks)
+  int64_t img_off;         // offset of this sub-buffer inside one staging page image
+};
+
+struct Geom {
+  SubGeom sub[HC_MAX_SUBBUFS];
+  int32_t nsub;
+  int32_t L;
+  int32_t P;
+  int32_t validate;        // HC_FLAG_VALIDATE: page-block row contiguity checks
+  int64_t S;               // device token slots per layer
+  int64_t host_tokens;     // H * P
+  int64_t img_bytes;       // one staging page image (shard stride or summed sub pages)
+  int64_t payload_bytes;   // summed sub-buffer pages
+  int64_t pad_bytes;       // shard padding (0 for page-first)
+};
+
+// Host-side derived layout (pure arithmetic; no HIP calls).
+struct Layout {
+  int32_t L = 0, P = 0, nsub = 0, layout = 0;
+  int32_t gran[HC_MAX_SUBBUFS] = {};
+  int64_t elem[HC_MAX_SUBBUFS] = {};
+  int64_t S = 0, H = 0, align = 0;
+  int64_t subpage[HC_MAX_SUBBUFS] = {};   // one page of sub b over all layers
+  int64_t payload = 0;                    // sum of subpage
+  int64_t stride = 0;                     // shard stride / page image bytes
+  int64_t host_region[HC_MAX_SUBBUFS] = {};
+  int64_t host_page_stride[HC_MAX_SUBBUFS] = {};
+  int64_t layer_stride[HC_MAX_SUBBUFS] = {};
+  int64_t img_off[HC_MAX_SUBBUFS] = {};
+  int64_t host_bytes = 0;
+  bool has_blocks = false;
+};
+
+// Fills *out from desc; on failure returns a negative hc_status and writes a message.
+int layout_from_desc(const hc_pool_desc* desc, Layout* out, char* msg, size_t msg_len);
+int64_t layout_host_offset(const Layout& lay, int b, int64_t page, int32_t layer, int32_t row);
+
+// Kernel launchers (hc_kernels.hip).  All enqueue on `stream` and return the launch status.
+hipError_t launch_gather_stage(const Geom& g, const int64_t* dev_idx, const int32_t* srow,
+                               int64_t t0, int64_t count, uint8_t* staging, int32_t* err,
+                               hipStream_t stream);
+hipError_t launch_zc_write(const Geom& g, const int64_t* dev_idx, const int64_t* host_idx,
+                           const int32_t* tok_list, int64_t count, uint8_t* host, int32_t* err,
+                           int32_t max_ctas, hipStream_t stream);
+hipError_t launch_zc_read(const Geom& g, int32_t layer, const int64_t* host_idx, const int64_t* dev_idx,
+                          int64_t n, const uint8_t* host, int32_t* err, int32_t max_ctas,
+                          hipStream_t stream);
+hipError_t launch_zero_pads(uint8_t* base, const int64_t* pages, int64_t npages, int64_t stride,
+                            int64_t off, int64_t bytes, hipStream_t stream);
+hipError_t launch_compare(const Geom& g, const int64_t* a, const int64_t* c, int64_t n,
+                          unsigned long long* counter, int32_t* err, hipStream_t stream);
+
+}  // namespace hc

@@ -1,0 +1,383 @@
+// HIP kernels of the KV page transfer, written for CDNA4 (gfx950, wave64).
+//
+// Every kernel moves opaque 16-byte vectors: rows of a layer-first device pool
+// to/from a page-first host pool (directly over the host link, "zero-copy") or
+// to a device staging buffer laid out as host page images (staged write-back:
+// the layer-first -> page-first relayout of the hybrid-pool write-back page,
+// sglang PR 28434 summary, implementation breakdown).
+//
+// Work is cut into units of (tile of 256 tokens, layer, sub-buffer).  A unit
+// starts with an index intake: each of the 256 threads reads one token's
+// device and host index, range-checks it, and computes the byte addresses of
+// its source and destination row.  Rows that move are compacted into LDS with
+// a wavefront ballot and a mbcnt prefix (page blocks keep only the row-0 token
+// of each page; the staged write-back skips tokens of partial pages).  The copy
+// loop then walks the unit's rows * (elem/16) vectors with all 256 lanes: lane
+// u copies vector u % vecs of row u / vecs, so consecutive lanes touch
+// consecutive 16-byte vectors of a row, and a run of slots that are adjacent
+// on both sides is one contiguous stream of addresses.  Loads are issued
+// kUnroll deep before the stores to keep enough bytes in flight.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "hc_internal.h"
+
+namespace hc {
+namespace {
+
+constexpr int kThreads = 256;  // 4 waves of 64
+constexpr int kTile = 256;     // tokens per unit: one per thread at intake
+constexpr int kUnroll = 8;     // 16-byte loads in flight per thread
+constexpr int kWaves = kThreads / 64;
+
+// 16-byte vector in global address space (global_load/store_dwordx4, not flat).
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) const v4u* gload_t;
+typedef __attribute__((address_space(1))) v4u* gstore_t;
+
+__device__ __forceinline__ v4u ld16(uint64_t a) { return *reinterpret_cast<gload_t>(a); }
+__device__ __forceinline__ void st16(uint64_t a, v4u v) { *reinterpret_cast<gstore_t>(a) = v; }
+
+// q = u / vecs for u < 2^20 and vecs <= 2^20 (magic = ceil(2^40 / vecs)).
+__device__ __forceinline__ uint32_t div_vecs(uint32_t u, uint64_t magic) {
+  return (uint32_t)(((uint64_t)u * magic) >> 40);
+}
+
+// Block-wide compaction of a per-thread predicate.  Each wave takes a 64-bit
+// ballot; a lane's rank among its wave's kept lanes is mbcnt of the ballot;
+// wave totals go through LDS for the block prefix.  Returns the thread's slot
+// (meaningful when keep) and the block total in *total.
+__device__ __forceinline__ int compact_slot(bool keep, int* s_wave, int* total) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const unsigned long long m = __ballot(keep);
+  const int rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+  if (lane == 0) s_wave[wave] = __popcll(m);
+  __syncthreads();
+  int base = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; w++) {
+    const int c = s_wave[w];
+    base += (w < wave) ? c : 0;
+    all += c;
+  }
+  *total = all;
+  return base + rank;
+}
+
+// Copies `rows` rows of `vecs` 16-byte vectors: row q from s_src[q] to s_dst[q].
+__device__ __forceinline__ void copy_rows(const uint64_t* s_src, const uint64_t* s_dst, int rows,
+                                          uint32_t vecs, uint64_t magic) {
+  const uint32_t total = (uint32_t)rows * vecs;
+  for (uint32_t u0 = threadIdx.x; u0 < total; u0 += kThreads * kUnroll) {
+    v4u v[kUnroll];
+    uint64_t dst[kUnroll];
+#pragma unroll
+    for (int k = 0; k < kUnroll; k++) {
+      const uint32_t u = u0 + k * kThreads;
+      if (u < total) {
+        const uint32_t q = div_vecs(u, magic);
+        const uint64_t off = (uint64_t)(u - q * vecs) * 16u;
+        v[k] = ld16(s_src[q] + off);
+        dst[k] = s_dst[q] + off;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kUnroll; k++) {
+      const uint32_t u = u0 + k * kThreads;
+      if (u < total) st16(dst[k], v[k]);
+    }
+  }
+}
+
+__device__ __forceinline__ uint64_t layer_base(const SubGeom& s, int l) { return s.layers[l]; }
+
+// Host byte offset of (sub s, page p, layer l, row r).
+__device__ __forceinline__ int64_t host_off(const SubGeom& s, int64_t p, int l, int r) {
+  int64_t o = s.host_region + p * s.host_page_stride + (int64_t)l * s.layer_stride;
+  if (s.gran == HC_TOKEN_ROWS) o += (int64_t)r * s.elem;
+  return o;
+}
+
+// Device byte offset of slot d inside one layer.
+__device__ __forceinline__ int64_t dev_off(const SubGeom& s, int64_t d, int P) {
+  return (s.gran == HC_TOKEN_ROWS ? d : d / P) * s.elem;
+}
+
+// ---------------------------------------------------------------- staged write-back: gather
+// grid = (tiles over [t0, t0+count), L, nsub).  srow[i] = slot * P + row inside the
+// chunk's staging images, or -1 for tokens that do not go through staging.
+__global__ __launch_bounds__(kThreads) void k_gather_stage(Geom g, const int64_t* __restrict__ dev_idx,
+                                                           const int32_t* __restrict__ srow, int64_t t0,
+                                                           int64_t count, uint8_t* __restrict__ staging,
+                                                           int32_t* __restrict__ err) {
+  __shared__ uint64_t s_src[kTile];
+  __shared__ uint64_t s_dst[kTile];
+  __shared__ int s_wave[kWaves];
+  const int b = blockIdx.z;
+  const int l = blockIdx.y;
+  const SubGeom& s = g.sub[b];
+  const int64_t i = t0 + (int64_t)blockIdx.x * kTile + threadIdx.x;
+  bool keep = false;
+  uint64_t src = 0, dst = 0;
+  if (i < t0 + count) {
+    const int32_t sr = srow[i];
+    if (sr >= 0) {
+      const int32_t slot = sr / g.P;
+      const int32_t r = sr - slot * g.P;
+      if (s.gran == HC_TOKEN_ROWS || r == 0) {
+        const int64_t d = dev_idx[i];
+        if (d >= 0 && d < g.S) {
+          src = layer_base(s, l) + (uint64_t)dev_off(s, d, g.P);
+          dst = (uint64_t)staging + (uint64_t)((int64_t)slot * g.img_bytes + s.img_off +
+                                               (int64_t)l * s.layer_stride +
+                                               (s.gran == HC_TOKEN_ROWS ? (int64_t)r * s.elem : 0));
+          keep = true;
+        } else {
+          atomicOr(err, 1);
+        }
+      }
+    }
+  }
+  int total;
+  const int slot = compact_slot(keep, s_wave, &total);
+  if (keep) {
+    s_src[slot] = src;
+    s_dst[slot] = dst;
+  }
+  __syncthreads();
+  copy_rows(s_src, s_dst, total, s.vecs, s.vec_magic);
+}
+
+// ---------------------------------------------------------------- zero-copy write-back
+// Device rows -> pinned host pool.  Tokens are [0, count) or tok_list[0, count).
+// Units (tile, layer, sub) are walked grid-stride so a capped grid suffices.
+__global__ __launch_bounds__(kThreads) void k_zc_write(Geom g, const int64_t* __restrict__ dev_idx,
+                                                       const int64_t* __restrict__ host_idx,
+                                                       const int32_t* __restrict__ tok_list, int64_t count,
+                                                       uint8_t* __restrict__ host, int32_t* __restrict__ err,
+                                                       int64_t units) {
+  __shared__ uint64_t s_src[kTile];
+  __shared__ uint64_t s_dst[kTile];
+  __shared__ int s_wave[kWaves];
+  const int64_t per_tile = (int64_t)g.L * g.nsub;
+  for (int64_t unit = blockIdx.x; unit < units; unit += gridDim.x) {
+    const int64_t tile = unit / per_tile;
+    const int rem = (int)(unit - tile * per_tile);
+    const int l = rem / g.nsub;
+    const int b = rem - l * g.nsub;
+    const SubGeom& s = g.sub[b];
+    const int64_t j = tile * kTile + threadIdx.x;
+    bool keep = false;
+    uint64_t src = 0, dst = 0;
+    if (j < count) {
+      const int64_t i = tok_list ? (int64_t)tok_list[j] : j;
+      const int64_t d = dev_idx[i];
+      const int64_t h = host_idx[i];
+      const int64_t p = h / g.P;
+      const int r = (int)(h - p * g.P);
+      if (s.gran == HC_TOKEN_ROWS || r == 0) {
+        if (d >= 0 && d < g.S && h >= 0 && h < g.host_tokens) {
+          src = layer_base(s, l) + (uint64_t)dev_off(s, d, g.P);
+          dst = (uint64_t)host + (uint64_t)host_off(s, p, l, r);
+          keep = true;
+        } else {
+          atomicOr(err, 1);
+        }
+      }
+    }
+    int total;
+    const int slot = compact_slot(keep, s_wave, &total);
+    if (keep) {
+      s_src[slot] = src;
+      s_dst[slot] = dst;
+    }
+    __syncthreads();
+    copy_rows(s_src, s_dst, total, s.vecs, s.vec_magic);
+    __syncthreads();  // LDS is rewritten by the next unit
+  }
+}
+
+// ---------------------------------------------------------------- zero-copy load-back (one layer)
+// Pinned host pool -> device rows of layer `layer`.  Indices are device-resident.
+// Units (tile, sub) grid-stride.  With g.validate, page-block sub-buffers also check
+// that each page's rows arrive as one run of P consecutive device slots starting on a
+// page boundary (neighbour compare through a lane shuffle, LDS at wave edges).
+__global__ __launch_bounds__(kThreads) void k_zc_read(Geom g, int32_t layer, const int64_t* __restrict__ host_idx,
+                                                      const int64_t* __restrict__ dev_idx, int64_t n,
+                                                      const uint8_t* __restrict__ host, int32_t* __restrict__ err,
+                                                      int64_t units) {
+  __shared__ uint64_t s_src[kTile];
+  __shared__ uint64_t s_dst[kTile];
+  __shared__ int s_wave[kWaves];
+  for (int64_t unit = blockIdx.x; unit < units; unit += gridDim.x) {
+    const int64_t tile = unit / g.nsub;
+    const int b = (int)(unit - tile * g.nsub);
+    const SubGeom& s = g.sub[b];
+    const int64_t i = tile * kTile + threadIdx.x;
+    bool keep = false;
+    uint64_t src = 0, dst = 0;
+    int64_t d = 0, h = 0;
+    const bool live = i < n;
+    if (live) {
+      d = dev_idx[i];
+      h = host_idx[i];
+    }
+    if (g.validate && s.gran == HC_PAGE_BLOCKS) {
+      // previous token's indices: lane shuffle inside the wave, memory at the wave's first lane
+      int64_t dp = __shfl_up(d, 1);
+      int64_t hp = __shfl_up(h, 1);
+      if ((threadIdx.x & 63) == 0 && live && i > 0) {
+        dp = dev_idx[i - 1];
+        hp = host_idx[i - 1];
+      }
+      if (live) {
+        const bool first_row = (h % g.P) == 0;
+        const bool ok = first_row ? (d % g.P == 0) : (i > 0 && dp + 1 == d && hp + 1 == h);
+        if (!ok) atomicOr(err, 2);
+      }
+    }
+    if (live) {
+      const int64_t p = h / g.P;
+      const int r = (int)(h - p * g.P);
+      if (s.gran == HC_TOKEN_ROWS || r == 0) {
+        if (d >= 0 && d < g.S && h >= 0 && h < g.host_tokens) {
+          src = (uint64_t)host + (uint64_t)host_off(s, p, layer, r);
+          dst = layer_base(s, layer) + (uint64_t)dev_off(s, d, g.P);
+          keep = true;
+        } else {
+          atomicOr(err, 1);
+        }
+      }
+    }
+    int total;
+    const int slot = compact_slot(keep, s_wave, &total);
+    if (keep) {
+      s_src[slot] = src;
+      s_dst[slot] = dst;
+    }
+    __syncthreads();
+    copy_rows(s_src, s_dst, total, s.vecs, s.vec_magic);
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------- shard padding
+// Zeroes [off, off + bytes) of page pages[k] (or page k when pages is null) for k < npages.
+__global__ __launch_bounds__(kThreads) void k_zero_pads(uint8_t* __restrict__ base, const int64_t* __restrict__ pages,
+                                                        int64_t npages, int64_t stride, int64_t off, uint32_t vecs) {
+  const int64_t total = npages * (int64_t)vecs;
+  const v4u z = {0u, 0u, 0u, 0u};
+  for (int64_t u = (int64_t)blockIdx.x * kThreads + threadIdx.x; u < total; u += (int64_t)gridDim.x * kThreads) {
+    const int64_t k = u / vecs;
+    const int64_t v = u - k * vecs;
+    const int64_t p = pages ? pages[k] : k;
+    st16((uint64_t)base + (uint64_t)(p * stride + off + v * 16), z);
+  }
+}
+
+// ---------------------------------------------------------------- round-trip compare
+// grid = (tiles, L, nsub).  Counts rows (or page blocks at a[i] % P == 0) whose bytes
+// at slot a[i] and slot c[i] differ.  One wave compares one row at a time; the row's
+// verdict is the OR of the lanes' verdicts (ballot).
+__global__ __launch_bounds__(kThreads) void k_compare(Geom g, const int64_t* __restrict__ a,
+                                                      const int64_t* __restrict__ c, int64_t n,
+                                                      unsigned long long* __restrict__ counter,
+                                                      int32_t* __restrict__ err) {
+  __shared__ uint64_t s_x[kTile];
+  __shared__ uint64_t s_y[kTile];
+  __shared__ int s_wave[kWaves];
+  const int b = blockIdx.z;
+  const int l = blockIdx.y;
+  const SubGeom& s = g.sub[b];
+  const int64_t i = (int64_t)blockIdx.x * kTile + threadIdx.x;
+  bool keep = false;
+  uint64_t x = 0, y = 0;
+  if (i < n) {
+    const int64_t da = a[i], dc = c[i];
+    if (da >= 0 && da < g.S && dc >= 0 && dc < g.S) {
+      if (s.gran == HC_TOKEN_ROWS || da % g.P == 0) {
+        x = layer_base(s, l) + (uint64_t)dev_off(s, da, g.P);
+        y = layer_base(s, l) + (uint64_t)dev_off(s, dc, g.P);
+        keep = true;
+      }
+    } else {
+      atomicOr(err, 1);
+    }
+  }
+  int total;
+  const int slot = compact_slot(keep, s_wave, &total);
+  if (keep) {
+    s_x[slot] = x;
+    s_y[slot] = y;
+  }
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  unsigned long long bad = 0;
+  for (int q = wave; q < total; q += kWaves) {
+    bool diff = false;
+    for (uint32_t v = lane; v < s.vecs; v += 64) {
+      const v4u p0 = ld16(s_x[q] + (uint64_t)v * 16u);
+      const v4u p1 = ld16(s_y[q] + (uint64_t)v * 16u);
+      diff |= (p0.x != p1.x) | (p0.y != p1.y) | (p0.z != p1.z) | (p0.w != p1.w);
+    }
+    if (__ballot(diff) != 0ull) bad++;
+  }
+  if (lane == 0 && bad) atomicAdd(counter, bad);
+}
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace
+
+hipError_t launch_gather_stage(const Geom& g, const int64_t* dev_idx, const int32_t* srow, int64_t t0,
+                               int64_t count, uint8_t* staging, int32_t* err, hipStream_t stream) {
+  if (count <= 0) return hipSuccess;
+  const int64_t tiles = ceil_div(count, kTile);
+  if (tiles > 0x7fffffff) return hipErrorInvalidValue;
+  dim3 grid((unsigned)tiles, (unsigned)g.L, (unsigned)g.nsub);
+  k_gather_stage<<<grid, kThreads, 0, stream>>>(g, dev_idx, srow, t0, count, staging, err);
+  return hipGetLastError();
+}
+
+hipError_t launch_zc_write(const Geom& g, const int64_t* dev_idx, const int64_t* host_idx, const int32_t* tok_list,
+                           int64_t count, uint8_t* host, int32_t* err, int32_t max_ctas, hipStream_t stream) {
+  if (count <= 0) return hipSuccess;
+  const int64_t units = ceil_div(count, kTile) * g.L * g.nsub;
+  const int64_t grid = units < max_ctas ? units : max_ctas;
+  k_zc_write<<<dim3((unsigned)grid), kThreads, 0, stream>>>(g, dev_idx, host_idx, tok_list, count, host, err, units);
+  return hipGetLastError();
+}
+
+hipError_t launch_zc_read(const Geom& g, int32_t layer, const int64_t* host_idx, const int64_t* dev_idx, int64_t n,
+                          const uint8_t* host, int32_t* err, int32_t max_ctas, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  const int64_t units = ceil_div(n, kTile) * g.nsub;
+  const int64_t grid = units < max_ctas ? units : max_ctas;
+  k_zc_read<<<dim3((unsigned)grid), kThreads, 0, stream>>>(g, layer, host_idx, dev_idx, n, host, err, units);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_pads(uint8_t* base, const int64_t* pages, int64_t npages, int64_t stride, int64_t off,
+                            int64_t bytes, hipStream_t stream) {
+  if (npages <= 0 || bytes <= 0) return hipSuccess;
+  const uint32_t vecs = (uint32_t)(bytes / 16);
+  const int64_t total = npages * (int64_t)vecs;
+  int64_t grid = ceil_div(total, kThreads);
+  if (grid > 4096) grid = 4096;
+  k_zero_pads<<<dim3((unsigned)grid), kThreads, 0, stream>>>(base, pages, npages, stride, off, vecs);
+  return hipGetLastError();
+}
+
+hipError_t launch_compare(const Geom& g, const int64_t* a, const int64_t* c, int64_t n, unsigned long long* counter,
+                          int32_t* err, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  const int64_t tiles = ceil_div(n, kTile);
+  if (tiles > 0x7fffffff) return hipErrorInvalidValue;
+  dim3 grid((unsigned)tiles, (unsigned)g.L, (unsigned)g.nsub);
+  k_compare<<<grid, kThreads, 0, stream>>>(g, a, c, n, counter, err);
+  return hipGetLastError();
+}
+
+}  // namespace hc

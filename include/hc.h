@@ -1,0 +1,220 @@
+/*
+ * hc.h -- C ABI of the HiCache host<->device KV page transfer library (libhc.so),
+ * written for AMD Instinct MI355X (gfx950).
+ *
+ * The library moves KV-cache rows between a layer-first device pool (one buffer
+ * per layer and sub-buffer, indexed by token slot) and a page-first pinned host
+ * pool (indexed by host token = page * page_size + row), in both directions:
+ *
+ *   write-back (device -> host), all layers in one call, the staged
+ *     layer-first -> page-first write-back of the hybrid-pool write-back page
+ *     (prhub summary of sglang PR 28434: implementation breakdown and the
+ *     host-pool / CPU-mock source excerpts);
+ *   load-back (host -> device), one layer per call, each call recording a
+ *     layer-done event so a forward pass can start layer l while later layers
+ *     are still in flight (loader-thread page, sglang PR 38472: Motivation and
+ *     Modifications; rank-sharded host tier page, sglang PR 41984).
+ *
+ * Host layouts:
+ *   HC_LAYOUT_PAGE_FIRST      per sub-buffer [page][layer][row][elem_bytes]
+ *                             (page_first_direct on the loader-thread page);
+ *                             sub-buffer regions follow each other in order.
+ *   HC_LAYOUT_KV_SPLIT_SHARD  [shard = page]{ sub 0 page | sub 1 page | ... | zero pad },
+ *                             each sub page [layer][row][elem_bytes], shard size
+ *                             rounded up to shard_align (CacheStore H2H page,
+ *                             unified-cache-management PR 1292, section
+ *                             "page_first_kv_split support"; Direct I/O uses 4096).
+ * A sub-buffer holds either token rows (HC_TOKEN_ROWS: elem_bytes per token per
+ * layer) or page blocks (HC_PAGE_BLOCKS: elem_bytes per page per layer, e.g. the
+ * DSA indexer-K page of 64 fp8 keys and 64 fp32 scales).  A page block moves
+ * with the token at row 0 of its page, to/from device block slot / page_size.
+ *
+ * Payload bytes are never interpreted: bf16, fp8 and fp32 all move bit-exactly.
+ *
+ * Conventions for every call:
+ *   - Return value: HC_OK (0) or a negative hc_status.  hc_last_error() returns
+ *     a message for the calling thread's last failure.
+ *   - Ownership: the caller owns every buffer, stream and event passed in and
+ *     keeps them alive until the copy stream has drained.  The library owns only
+ *     the pool handle and its small scratch (index plans, counters).
+ *   - Asynchrony: transfer calls enqueue on the pool's copy stream and return.
+ *     Work on the copy stream runs in call order.  A caller whose index lists
+ *     or device rows are produced on another stream must order that stream
+ *     before the call (event record + hipStreamWaitEvent on the copy stream).
+ *   - Indices are int64 token indices.  Device and host indices are each
+ *     distinct and in range; with page-block sub-buffers every page named is
+ *     named whole and maps row by row onto one whole device page.  Transfer
+ *     calls trust device-resident indices (as copy kernels do); pools created
+ *     with HC_FLAG_VALIDATE check them on the device and report a violation as
+ *     HC_ERR_DEVICE at the next hc_round_trip_check or hc_pool_sync.
+ *   - Sizes: elem_bytes is a multiple of 16 (16-byte vectors, the element-size
+ *     rule of the hybrid-pool write-back page) and at most 65536; every device
+ *     layer pointer, the host pool and the staging buffer are 16-byte aligned.
+ */
+#ifndef HC_H
+#define HC_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HC_MAX_SUBBUFS 4
+#define HC_MAX_LAYERS 1024
+#define HC_MAX_ELEM_BYTES 65536
+
+typedef enum hc_status {
+  HC_OK = 0,
+  HC_ERR_INVALID = -1,     /* bad argument: null pointer, negative count, value out of range */
+  HC_ERR_UNSUPPORTED = -2, /* well-formed but not handled: elem_bytes % 16, misalignment, mode */
+  HC_ERR_HIP = -3,         /* a HIP runtime call failed (the message names it) */
+  HC_ERR_NOMEM = -4,       /* the library could not allocate its own scratch */
+  HC_ERR_DEVICE = -5       /* device-side validation flagged an index list (HC_FLAG_VALIDATE) */
+} hc_status;
+
+enum { HC_TOKEN_ROWS = 0, HC_PAGE_BLOCKS = 1 };
+enum { HC_LAYOUT_PAGE_FIRST = 0, HC_LAYOUT_KV_SPLIT_SHARD = 1 };
+/* Transfer modes.  STAGED: device kernels relayout through the device staging
+ * buffer and the copy engines (hipMemcpyAsync) cross the host link.  ZEROCOPY:
+ * kernels read or write the pinned host pool directly.  AUTO: the library's
+ * measured default (see hc_pool_mode). */
+enum { HC_MODE_AUTO = 0, HC_MODE_STAGED = 1, HC_MODE_ZEROCOPY = 2 };
+/* Pool flags. */
+enum { HC_FLAG_VALIDATE = 1, HC_FLAG_PROFILE = 2 };
+
+typedef struct hc_subbuf_desc {
+  int32_t granularity;        /* HC_TOKEN_ROWS or HC_PAGE_BLOCKS */
+  int32_t reserved;           /* must be 0 */
+  int64_t elem_bytes;         /* bytes per token row (or per page block) per layer */
+  void* const* device_layers; /* host array of num_layers device pointers; layer l holds
+                                 device_slots rows (token rows) or device_slots/page_size
+                                 blocks (page blocks) of elem_bytes each.  The array is
+                                 read during hc_pool_create only. */
+} hc_subbuf_desc;
+
+typedef struct hc_pool_desc {
+  int32_t num_layers;   /* L, 1..HC_MAX_LAYERS */
+  int32_t page_size;    /* P tokens per page, >= 1 */
+  int32_t num_subbufs;  /* 1..HC_MAX_SUBBUFS */
+  int32_t layout;       /* HC_LAYOUT_* */
+  hc_subbuf_desc sub[HC_MAX_SUBBUFS];
+  int64_t device_slots; /* S token slots per layer (a multiple of P when a sub-buffer holds page blocks) */
+  int64_t host_pages;   /* H pages (shards) in the host pool */
+  int64_t shard_align;  /* shard layout: power of two >= 16 (4096 for Direct I/O); ignored otherwise */
+  void* host_base;      /* pinned host memory (hc_host_alloc or hipHostMalloc), >= hc_host_pool_bytes */
+  int64_t host_bytes;   /* size of host_base */
+  void* staging;        /* device memory for HC_MODE_STAGED write-back; NULL when no staged mode is used */
+  int64_t staging_bytes;/* size of staging; the chunk is staging_bytes / hc_staging_page_bytes pages */
+  void* copy_stream;    /* hipStream_t every transfer of this pool is enqueued on (NULL: null stream) */
+  int32_t write_back_mode; /* HC_MODE_* */
+  int32_t load_back_mode;  /* HC_MODE_* (load-back is always zero-copy in this version) */
+  int32_t flags;           /* HC_FLAG_* */
+  int32_t max_ctas;        /* cap on workgroups of the zero-copy kernels; 0 = library default */
+} hc_pool_desc;
+
+typedef struct hc_pool hc_pool; /* opaque, library-owned */
+
+/* ---------------------------------------------------------------- layout queries (host only)
+ * These run on the CPU and touch no GPU. */
+
+/* Checks a descriptor's geometry, layout and sizes (not its pointers' memory kinds).
+ * HC_ERR_INVALID / HC_ERR_UNSUPPORTED with a message, else HC_OK. */
+int hc_desc_check(const hc_pool_desc* desc);
+
+/* Bytes the host pool needs for desc's layout: H * (sum of sub-buffer pages) for
+ * page-first, H * shard stride for the shard layout. */
+int hc_host_pool_bytes(const hc_pool_desc* desc, int64_t* out_bytes);
+
+/* Bytes of one page image in the device staging buffer (the shard stride for the
+ * shard layout, the summed sub-buffer pages for page-first). */
+int hc_staging_page_bytes(const hc_pool_desc* desc, int64_t* out_bytes);
+
+/* Byte offset of (sub-buffer, page, layer, row) in the host pool.  For a page-block
+ * sub-buffer the row is ignored.  HC_ERR_INVALID when any coordinate is out of range. */
+int hc_host_offset(const hc_pool_desc* desc, int32_t sub, int64_t page, int32_t layer,
+                   int32_t row, int64_t* out_offset);
+
+/* ---------------------------------------------------------------- pinned host memory */
+
+/* Page-locked host allocation through hipHostMalloc (device-mapped, NUMA node of
+ * the current device).  flags: 0 = coherent, 1 = non-coherent.  The memory is
+ * zero-filled.  *out is 4096-aligned. */
+int hc_host_alloc(int64_t bytes, int32_t flags, void** out);
+int hc_host_free(void* ptr);
+
+/* ---------------------------------------------------------------- pool lifetime */
+
+/* Validates desc, copies the per-layer pointer tables to device memory, and
+ * records the modes.  Touches the current HIP device. */
+int hc_pool_create(const hc_pool_desc* desc, hc_pool** out);
+
+/* Waits for the pool's copy stream, then frees the handle and its scratch.  NULL is a no-op. */
+int hc_pool_destroy(hc_pool* pool);
+
+/* The mode write-back (which = 0) or load-back (which = 1) resolves to
+ * (HC_MODE_STAGED or HC_MODE_ZEROCOPY). */
+int hc_pool_mode(const hc_pool* pool, int32_t which, int32_t* out_mode);
+
+/* Blocks until the copy stream has drained; reports HC_ERR_DEVICE when device-side
+ * validation (HC_FLAG_VALIDATE) flagged an index list since the last report. */
+int hc_pool_sync(hc_pool* pool);
+
+/* ---------------------------------------------------------------- transfers */
+
+/* Write-back of all layers and sub-buffers (device -> host):
+ *   host[sub b][page h/P][layer l][row h%P] <- device[sub b][layer l][slot d]
+ * for every pair (d = device_idx[i], h = host_idx[i]), i < n; page blocks move
+ * with the row-0 token of each page; in the shard layout the pad bytes of every
+ * shard named become zero; nothing else in the host pool changes.
+ *   device_idx: n int64 in device memory (or pinned host memory), read on the GPU.
+ *   host_idx:   n int64 in host memory, read by the CPU during the call (the
+ *               plan of host regions is built once per burst); may be freed
+ *               when the call returns.
+ *   done_event: hipEvent_t recorded on the copy stream after the last byte is
+ *               enqueued, or NULL.
+ * Errors are reported before anything is enqueued; done_event is still
+ * recorded on error when the pool is valid. */
+int hc_write_back_all_layers(hc_pool* pool, const int64_t* device_idx, const int64_t* host_idx,
+                             int64_t n, void* event);
+
+/* Load-back of one layer (host -> device):
+ *   device[sub b][layer][slot d] <- host[sub b][page h/P][layer][row h%P]
+ * for every pair (h = host_idx[i], d = device_idx[i]), i < n, every sub-buffer;
+ * only layer `layer` of the device pool changes.
+ *   host_idx, device_idx: n int64 each, in device memory (or pinned host
+ *               memory), read on the GPU: no CPU-side descriptor is built.
+ *   event:      hipEvent_t recorded on the copy stream once this layer's rows
+ *               are enqueued (the layer-done event), or NULL.
+ * The event is recorded even when the call fails (on the pool's copy stream,
+ * or on the null stream when pool is NULL), so a consumer waiting on it never
+ * hangs; the layer's rows are then stale. */
+int hc_load_back_layer(hc_pool* pool, int32_t layer, const int64_t* host_idx,
+                       const int64_t* device_idx, int64_t n, void* event);
+
+/* Round-trip check: counts the (token, sub-buffer, layer) units whose device
+ * rows at slots idx_a[i] and idx_b[i] differ, over all layers and sub-buffers
+ * (page blocks once per page, at tokens with idx_a[i] % P == 0).  Indices are
+ * device-resident.  Synchronizes the copy stream and writes the count to
+ * *mismatched_units (host memory). */
+int hc_round_trip_check(hc_pool* pool, const int64_t* idx_a, const int64_t* idx_b, int64_t n,
+                        int64_t* mismatched_units);
+
+/* ---------------------------------------------------------------- measurement */
+
+/* Per-kernel timing with HIP events on the copy stream (pools with HC_FLAG_PROFILE).
+ * kind: 0 gather to staging, 1 zero-copy write-back, 2 zero-copy load-back,
+ *       3 pad fill, 4 round-trip compare, 5 staged copy-engine transfers.
+ * Returns the number of timed launches and their summed milliseconds since the
+ * last reset (synchronizes the copy stream).  reset != 0 clears the counters. */
+int hc_pool_kernel_time(hc_pool* pool, int32_t kind, int32_t reset, int64_t* launches,
+                        double* total_ms);
+
+const char* hc_last_error(void);
+int hc_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HC_H */

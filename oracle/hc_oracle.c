@@ -264,3 +264,16 @@ int64_t orc_round_trip_check(const orc_geom* g, uint8_t* const* dev,
   }
   return bad;
 }
+
+/* Host offsets of the rows named by h for one sub-buffer and layer:
+ * out[i] = orc_host_offset(g, b, h[i] / P, layer, h[i] % P).  A plain loop, used
+ * by the tests to locate rows of large pools without one call per row. */
+int orc_host_offsets(const orc_geom* g, int b, int32_t layer, const int64_t* h, int64_t n, int64_t* out) {
+  if (orc_check_geom(g) != ORC_OK || b < 0 || b >= g->nsub || layer < 0 || layer >= g->layers) return ORC_ERR_INVALID;
+  if (n < 0 || (n > 0 && (!h || !out))) return ORC_ERR_INVALID;
+  for (int64_t i = 0; i < n; i++) {
+    if (h[i] < 0 || h[i] >= g->host_pages * g->page_size) return ORC_ERR_INVALID;
+    out[i] = orc_host_offset(g, b, h[i] / g->page_size, layer, (int32_t)(h[i] % g->page_size));
+  }
+  return ORC_OK;
+}

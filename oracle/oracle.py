@@ -75,6 +75,7 @@ def load(path: str = _LIB) -> ctypes.CDLL:
         "orc_write_back": (ctypes.c_int, [G, ctypes.POINTER(_PU8), _PU8, _P64, _P64, ctypes.c_int64]),
         "orc_load_back_layer": (ctypes.c_int, [G, ctypes.c_int32, ctypes.POINTER(_PU8), _PU8, _P64, _P64, ctypes.c_int64]),
         "orc_round_trip_check": (ctypes.c_int64, [G, ctypes.POINTER(_PU8), _P64, _P64, ctypes.c_int64]),
+        "orc_host_offsets": (ctypes.c_int, [G, ctypes.c_int, ctypes.c_int32, _P64, ctypes.c_int64, _P64]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -184,6 +185,15 @@ def host_offset(g: Geometry, b: int, page: int, layer: int, row: int) -> int:
 
 def device_offset(g: Geometry, b: int, slot: int) -> int:
     return lib().orc_device_offset(ctypes.byref(g.c()), b, slot)
+
+
+def host_offsets(g: Geometry, b: int, layer: int, h) -> np.ndarray:
+    """Host byte offsets of the rows named by h (sub-buffer b, one layer)."""
+    h = _i64(h)
+    out = np.empty(h.size, dtype=np.int64)
+    if lib().orc_host_offsets(ctypes.byref(g.c()), b, layer, _pi64(h), h.size, _pi64(out)) != 0:
+        raise ValueError("oracle host_offsets rejected its arguments")
+    return out
 
 
 def check_indices(g: Geometry, d, h) -> bool:

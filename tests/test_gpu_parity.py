@@ -1,0 +1,164 @@
+"""GPU path vs oracle, bit-exact, at sizes the oracle finishes in seconds.
+
+Each case spans several 256-token tiles with a ragged tail, and compares the
+whole host pool after write-back and the whole device pool after per-layer
+load-back with the oracle run on the same seeded inputs.  Modes: zero-copy and
+staged (staging chunks smaller than the burst, so several chunks run)."""
+import numpy as np
+import pytest
+import torch
+
+from host_device_page_amd import binding as B
+from host_device_page_amd import workloads as W
+from gpu_support import Rig, cuda_i64, load_back_and_check, say, write_back_and_check
+
+T, BLK = W.TOKEN_ROWS, W.PAGE_BLOCKS
+PF, SH = W.PAGE_FIRST, W.KV_SPLIT_SHARD
+
+
+def S(name, L, P, subs, slots, pages, layout=PF, align=4096):
+    return W.PoolShape(name, L, P, tuple(subs), slots, pages, layout, align)
+
+
+def has_blocks(shape):
+    return any(g == BLK for g, _ in shape.subs)
+
+
+def burst(shape, seed, kind, pages, partial_rows=0):
+    """(device slots, host tokens) for a case.
+    kind: 'perm' random distinct slots, 'segment' free-list runs, 'aligned' whole device pages,
+    'scatter' no adjacent neighbours, 'requests' partial-page requests."""
+    P = shape.page_size
+    if kind == "requests":
+        h = W.partial_page_requests(seed, shape.host_pages, P, pages)
+    else:
+        pg = W.host_pages(seed, shape.host_pages, pages)
+        h = W.whole_page_tokens(pg, P)
+        if partial_rows:
+            extra = np.setdiff1d(np.arange(shape.host_pages), pg)[0]
+            h = np.concatenate([h, extra * P + np.arange(partial_rows)])
+    n = h.size
+    if kind == "aligned":
+        d = W.page_aligned_slots(seed + 1, shape.device_slots, P, n // P)
+    elif kind == "segment":
+        d = W.segment_slots(seed + 1, shape.device_slots, n)
+    elif kind == "scatter":
+        d = W.scattered_slots(seed + 1, shape.device_slots, n)
+    else:
+        d = W.permutation_slots(seed + 1, shape.device_slots, n)
+    return d, h
+
+
+def fresh(shape, d, seed):
+    P = shape.page_size
+    if has_blocks(shape):
+        return W.page_aligned_slots(seed, shape.device_slots, P, d.size // P, exclude_pages=np.unique(d // P))
+    return W.permutation_slots(seed, shape.device_slots, d.size, exclude=d)
+
+
+CASES = [
+    # name, shape, burst kind, pages, partial rows
+    ("tiny_mha_bf16", W.SHAPES["tiny_mha_bf16"], "perm", 32, 0),
+    ("llama_rows_small", S("llama_rows_small", 4, 64, [(T, 2048)] * 2, 32768, 64), "segment", 12, 41),
+    ("mla_latent_small", S("mla_latent_small", 3, 64, [(T, 1152)], 65536, 64), "segment", 9, 17),
+    ("mla_indexer_small", S("mla_indexer_small", 3, 64, [(T, 1152), (BLK, 8448)], 8192, 32), "aligned", 10, 0),
+    ("shard_kv_small", S("shard_kv_small", 4, 32, [(T, 2048)] * 2, 16384, 64, SH), "requests", 24, 0),
+    ("shard_kv_pad", S("shard_kv_pad", 3, 16, [(T, 1024), (T, 128)], 4096, 40, SH), "requests", 30, 0),
+    ("elem16_rows", S("elem16_rows", 2, 8, [(T, 16)], 4096, 64), "requests", 50, 0),
+    ("elem_max_rows", S("elem_max_rows", 2, 4, [(T, 65536)], 64, 8), "perm", 3, 2),
+    ("page1_rows", S("page1_rows", 3, 1, [(T, 32)], 2048, 1024), "scatter", 700, 0),
+    ("four_subs_one_layer", S("four_subs_one_layer", 1, 16, [(T, 48), (T, 16), (BLK, 32), (T, 64)], 2048, 64),
+     "aligned", 33, 0),
+]
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("mode", ["zerocopy", "staged"])
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_write_back_then_load_back(case, mode):
+    name, shape, kind, pages, partial = case
+    say(f"[parity] {name} mode={mode}")
+    d, h = burst(shape, 11, kind, pages, partial)
+    wb = B.HC_MODE_STAGED if mode == "staged" else B.HC_MODE_ZEROCOPY
+    # staging smaller than the burst: several chunks
+    rig = Rig(shape, seed=5, write_back_mode=wb, staging_pages=max(1, pages // 3) if mode == "staged" else 0)
+    try:
+        assert rig.pool.mode(0) == wb and rig.pool.mode(1) == B.HC_MODE_ZEROCOPY
+        write_back_and_check(rig, d, h)
+        d2 = fresh(shape, d, 23)
+        load_back_and_check(rig, h, d2)
+        assert rig.pool.round_trip_check(cuda_i64(d), cuda_i64(d2)) == 0
+    finally:
+        rig.close()
+
+
+GRID_SHAPE = S("grid_small", 2, 4, [(T, 32)] * 2, 4096, 256)
+GRID_SHARD = S("grid_shard", 2, 4, [(T, 32), (T, 16)], 4096, 256, SH, 256)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("shape", [GRID_SHAPE, GRID_SHARD], ids=lambda s: s.name)
+@pytest.mark.parametrize("pages", [1, 63, 64, 65, 128, 129])
+def test_staged_chunk_boundaries(shape, pages):
+    """Page counts around one and two 64-page staging chunks."""
+    say(f"[chunks] {shape.name} pages={pages}")
+    d, h = burst(shape, pages, "perm", pages)
+    rig = Rig(shape, seed=pages, write_back_mode=B.HC_MODE_STAGED, staging_pages=64)
+    try:
+        write_back_and_check(rig, d, h)
+    finally:
+        rig.close()
+
+
+@pytest.mark.gpu
+def test_staged_interleaved_pages():
+    """Tokens of pages interleaved across chunks: split pages take the zero-copy path."""
+    shape = GRID_SHAPE
+    say("[interleaved] staged")
+    pg = W.host_pages(3, shape.host_pages, 12)
+    h = W.whole_page_tokens(pg, shape.page_size)
+    rng = np.random.default_rng(4)
+    h = h[rng.permutation(h.size)]
+    d = W.permutation_slots(5, shape.device_slots, h.size)
+    rig = Rig(shape, seed=9, write_back_mode=B.HC_MODE_STAGED, staging_pages=4)
+    try:
+        write_back_and_check(rig, d, h)
+        load_back_and_check(rig, h, fresh(shape, d, 6))
+    finally:
+        rig.close()
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("mode", [B.HC_MODE_ZEROCOPY, B.HC_MODE_STAGED])
+def test_empty_and_single(mode):
+    shape = GRID_SHAPE
+    say(f"[edge] empty/single mode={mode}")
+    rig = Rig(shape, seed=1, write_back_mode=mode, staging_pages=2)
+    try:
+        ev = B.HipEvent()
+        e = torch.empty(0, dtype=torch.int64, device="cuda")
+        rig.pool.write_back_all_layers(e, np.empty(0, dtype=np.int64), ev)
+        ev.synchronize()
+        rig.pool.load_back_layer(0, e, e, ev)
+        ev.synchronize()
+        assert rig.pool.round_trip_check(e, e) == 0
+        # the last slot and the last host row
+        last_d = np.array([shape.device_slots - 1])
+        last_h = np.array([shape.host_pages * shape.page_size - 1])
+        write_back_and_check(rig, last_d, last_h)
+        load_back_and_check(rig, last_h, np.array([0]))
+    finally:
+        rig.close()
+
+
+@pytest.mark.gpu
+def test_validate_flag_accepts_whole_pages():
+    shape = CASES[3][1]
+    say("[validate] whole pages")
+    d, h = burst(shape, 2, "aligned", 6)
+    rig = Rig(shape, seed=2, flags=B.HC_FLAG_VALIDATE)
+    try:
+        write_back_and_check(rig, d, h)
+        load_back_and_check(rig, h, fresh(shape, d, 3))
+    finally:
+        rig.close()
