@@ -48,6 +48,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-staged-probe", action="store_true")
+    ap.add_argument("--calibration-copy-mib", type=int, default=0,
+                    help="run one plain device-to-device copy of this size first (a known-size "
+                         "reference for the FETCH_SIZE / WRITE_SIZE counters)")
     return ap.parse_args()
 
 
@@ -74,6 +77,25 @@ def memcpy_peak(hip, host_ptr: int, dev_ptr: int, nbytes: int, stream_ptr: int, 
     hip.hipEventDestroy(e0)
     hip.hipEventDestroy(e1)
     return nbytes / (best * 1e-3) / 1e9
+
+
+def counter_traffic(workload: str, kernel: str):
+    """Bytes per launch that the FETCH_SIZE / WRITE_SIZE counter passes measured for
+    `kernel` (scaled by the known-size copy), from the committed profile summary, or
+    None when the kernel source changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{workload}_counters.json")
+    src = os.path.join(ROOT, "host_device_page_amd", "csrc", "hc_kernels.hip")
+    if not os.path.exists(path):
+        return None
+    prof = json.load(open(path))
+    if prof.get("kernel_source_sha256") != hashlib.sha256(open(src, "rb").read()).hexdigest():
+        return None
+    k = prof["kernels"].get(kernel)
+    if not k:
+        return None
+    return {"bytes": int(k["fetch_bytes"] + k["write_bytes"]), "fetch_bytes": int(k["fetch_bytes"]),
+            "write_bytes": int(k["write_bytes"]), "source": os.path.relpath(path, ROOT)}
 
 
 def burst_bytes(shape, burst) -> tuple[int, int]:
@@ -158,6 +180,15 @@ def main():
                       layout=shape.layout, shard_align=shape.align, staging=staging, write_back_mode=mode,
                       flags=B.HC_FLAG_PROFILE, max_ctas=args.max_ctas)
 
+    if args.calibration_copy_mib:
+        nb = args.calibration_copy_mib << 20
+        src = torch.ones(nb, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copy of {nb} bytes done")
+        del src, dst
     pool = make_pool(wb_mode)
     burst = W.burst_for(shape, seed=1)
     d2 = W.fresh_slots_like(shape, burst, seed=2)
@@ -232,13 +263,18 @@ def main():
     wr_gbs = link_bytes * n_wr / (ms_wr * 1e-3) / 1e9 if n_wr else None
     if n_wr and ms_wr > ms_rd:
         dom = {"kernel": "k_zc_write (zero-copy write-back, all layers)", "achieved": wr_gbs, "peak": peak_d2h,
-               "launches": n_wr, "avg_ms": ms_wr / n_wr, "bytes_per_launch": link_bytes}
+               "launches": n_wr, "avg_ms": ms_wr / n_wr, "bytes_per_launch": link_bytes, "name": "k_zc_write"}
     else:
         dom = {"kernel": "k_zc_read (zero-copy load-back, one layer)", "achieved": rd_gbs, "peak": peak_h2d,
-               "launches": n_rd, "avg_ms": ms_rd / max(1, n_rd), "bytes_per_launch": per_layer_bytes}
+               "launches": n_rd, "avg_ms": ms_rd / max(1, n_rd), "bytes_per_launch": per_layer_bytes,
+               "name": "k_zc_read"}
+    traffic = counter_traffic(shape.name, dom["name"])
     roofline = {"bound": "host_link", "kernel": dom["kernel"], "achieved": round(dom["achieved"], 3),
                 "peak": round(dom["peak"], 3), "unit": "GB/s", "frac": round(dom["achieved"] / dom["peak"], 4),
-                "traffic": None, "avg_launch_ms": round(dom["avg_ms"], 4),
+                "traffic": traffic["bytes"] if traffic else None,
+                "traffic_detail": traffic,
+                "traffic_algorithmic": 2 * dom["bytes_per_launch"],
+                "avg_launch_ms": round(dom["avg_ms"], 4),
                 "bytes_per_launch": dom["bytes_per_launch"],
                 "peak_source": "hipMemcpyAsync pinned<->device 1 GiB best of 5, measured in this run",
                 "pcie5_x16_nominal_GBps": PCIE5_X16_GBS}
@@ -268,9 +304,11 @@ def main():
         chunks = n_g // reps
         gather_bytes = 2 * link_bytes / max(1, chunks)  # read + write per launch (one chunk)
         g_gbs = gather_bytes * n_g / (ms_g * 1e-3) / 1e9
+        gtraffic = counter_traffic(shape.name, "k_gather_stage")
         roofline_hbm = {"bound": "hbm", "kernel": "k_gather_stage (staged lf->pf relayout, one chunk, all layers)",
                         "achieved": round(g_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                        "frac": round(g_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                        "frac": round(g_gbs / HBM_PEAK_GBS, 4),
+                        "traffic": gtraffic["bytes"] if gtraffic else None,
                         "avg_launch_ms": round(ms_g / n_g, 4), "bytes_per_launch": int(gather_bytes),
                         "chunk_pages": args.staging_pages}
         staged = {"write_back_GBps": round(link_bytes / (float(np.median(sms)) * 1e-3) / 1e9, 3),
