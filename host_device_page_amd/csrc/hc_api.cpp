@@ -603,8 +603,9 @@ int hc_pool_sync(hc_pool* p) {
   if (e) {
     HIP_TRY(hipMemsetAsync(p->d_err, 0, sizeof(int32_t), p->stream));
     HIP_TRY(hipStreamSynchronize(p->stream));
-    return set_err(HC_ERR_DEVICE, "device-side check flagged an index list (code %d: %s)", e,
-                   (e & 1) ? "index out of range" : "page-block rows not one whole device page");
+    return set_err(HC_ERR_DEVICE, "device-side check flagged an index list (code %d:%s%s)", e,
+                   (e & 1) ? " index out of range;" : "",
+                   (e & 2) ? " page-block rows not one whole device page;" : "");
   }
   return HC_OK;
 }

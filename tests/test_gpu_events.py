@@ -1,0 +1,190 @@
+"""Layer-done event chain and failure handling on the GPU (small pools).
+
+- a consumer stream that waits on each layer's event sees exactly the oracle's rows;
+- negative control: a consumer that does not wait, while the copy stream is held
+  back by a bounded spin, sees stale rows (so the positive check has teeth);
+- a failing load-back call still records its event, so a waiting consumer is
+  released (the loader-failure rule of the loader-thread page, Modifications);
+- bad indices are rejected on the host (write-back) or skipped and reported by the
+  kernels' own range checks (load-back), never dereferenced."""
+import numpy as np
+import pytest
+import torch
+
+from host_device_page_amd import binding as B
+from host_device_page_amd import workloads as W
+from gpu_support import Rig, cuda_i64, say
+from oracle import oracle as O
+
+T, BLK = W.TOKEN_ROWS, W.PAGE_BLOCKS
+SHAPE = W.PoolShape("event_rows", 6, 16, ((T, 1024), (T, 1024)), 16384, 128)
+BLOCKS = W.PoolShape("event_blocks", 3, 16, ((T, 64), (BLK, 256)), 4096, 64)
+
+
+def expected_layer_sums(rig, h, layer):
+    host = rig.host.np
+    sums = []
+    for b, (gran, e) in enumerate(rig.shape.subs):
+        offs = O.host_offsets(rig.geom, b, layer, h)
+        rows = np.stack([host[o:o + e] for o in offs])
+        sums.append(int(rows.view(np.int32).astype(np.int64).sum()))
+    return sums
+
+
+def consumer_sums(rig, layer, d_t):
+    out = []
+    for b, (gran, e) in enumerate(rig.shape.subs):
+        out.append(rig.dev[b][layer].view(-1, e)[d_t].view(torch.int32).to(torch.int64).sum())
+    return out
+
+
+def prepare(rig, seed):
+    """Write a burst back, so the host pool holds known rows, and pick fresh slots."""
+    pages = W.host_pages(seed, rig.shape.host_pages, 40)
+    h = W.whole_page_tokens(pages, rig.shape.page_size)
+    d = W.permutation_slots(seed + 1, rig.shape.device_slots, h.size)
+    rig.pool.write_back_all_layers(cuda_i64(d), h)
+    rig.pool.sync()
+    d2 = W.permutation_slots(seed + 2, rig.shape.device_slots, h.size, exclude=d)
+    return h, d, d2
+
+
+@pytest.mark.gpu
+def test_consumer_waits_on_each_layer_event():
+    say("[events] consumer with waits")
+    rig = Rig(SHAPE, seed=7)
+    try:
+        h, d, d2 = prepare(rig, 3)
+        h_t, d2_t = cuda_i64(h), cuda_i64(d2)
+        consumer = torch.cuda.Stream()
+        events = [B.HipEvent() for _ in range(SHAPE.layers)]
+        torch.cuda.synchronize()
+        with torch.cuda.stream(rig.stream):
+            torch.cuda._sleep(10_000_000)  # hold the copy stream back; the waits must cover it
+        got = []
+        for l in range(SHAPE.layers):
+            rig.pool.load_back_layer(l, h_t, d2_t, events[l])
+            events[l].wait_on(consumer)
+            with torch.cuda.stream(consumer):
+                got.append(consumer_sums(rig, l, d2_t))
+        consumer.synchronize()
+        rig.pool.sync()
+        for l in range(SHAPE.layers):
+            assert [int(x) for x in got[l]] == expected_layer_sums(rig, h, l), f"layer {l}"
+    finally:
+        rig.close()
+
+
+@pytest.mark.gpu
+def test_negative_control_consumer_without_wait_sees_stale_rows():
+    say("[events] negative control")
+    rig = Rig(SHAPE, seed=8)
+    try:
+        h, d, d2 = prepare(rig, 5)
+        h_t, d2_t = cuda_i64(h), cuda_i64(d2)
+        consumer = torch.cuda.Stream()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(rig.stream):
+            torch.cuda._sleep(50_000_000)  # bounded spin
+        rig.pool.load_back_layer(0, h_t, d2_t, None)
+        with torch.cuda.stream(consumer):
+            early = consumer_sums(rig, 0, d2_t)  # no wait: runs while the copy stream spins
+        consumer.synchronize()
+        rig.pool.sync()
+        want = expected_layer_sums(rig, h, 0)
+        assert [int(x) for x in early] != want, "a consumer that skips the wait was not caught"
+        assert [int(x) for x in consumer_sums(rig, 0, d2_t)] == want
+    finally:
+        rig.close()
+
+
+@pytest.mark.gpu
+def test_failed_load_back_still_records_event():
+    say("[events] failure injection")
+    rig = Rig(SHAPE, seed=9)
+    try:
+        h, d, d2 = prepare(rig, 7)
+        h_t, d2_t = cuda_i64(h), cuda_i64(d2)
+        ev = B.HipEvent()
+        with pytest.raises(B.HcError) as e:
+            rig.pool.load_back_layer(SHAPE.layers, h_t, d2_t, ev)  # layer out of range
+        assert e.value.code == B.HC_ERR_INVALID
+        ev.synchronize()
+        assert ev.query()
+        ev2 = B.HipEvent()
+        rc = B.lib.hc_load_back_layer(rig.pool.handle, 0, None, None, 5, ev2.handle)  # null lists
+        assert rc == B.HC_ERR_INVALID
+        ev2.synchronize()
+        ev3 = B.HipEvent()
+        rc = B.lib.hc_load_back_layer(None, 0, None, None, 5, ev3.handle)  # null pool: null stream
+        assert rc == B.HC_ERR_INVALID
+        ev3.synchronize()
+        # the burst after a failed call is served normally
+        dev0 = [[rig.dev[b][l].cpu().numpy() for l in range(SHAPE.layers)] for b in range(2)]
+        for l in range(SHAPE.layers):
+            rig.pool.load_back_layer(l, h_t, d2_t, None)
+        rig.pool.sync()
+        for l in range(SHAPE.layers):
+            O.load_back_layer(rig.geom, l, dev0, rig.host.np, h, d2)
+        for b in range(2):
+            for l in range(SHAPE.layers):
+                assert np.array_equal(rig.dev[b][l].cpu().numpy(), dev0[b][l])
+    finally:
+        rig.close()
+
+
+@pytest.mark.gpu
+def test_bad_indices_rejected_or_reported():
+    say("[events] bad indices")
+    rig = Rig(SHAPE, seed=10)
+    try:
+        h, d, d2 = prepare(rig, 9)
+        host_before = rig.host.np.copy()
+        # write-back: host list checked on the CPU before anything is enqueued
+        bad_h = h.copy()
+        bad_h[5] = SHAPE.host_pages * SHAPE.page_size
+        with pytest.raises(B.HcError) as e:
+            rig.pool.write_back_all_layers(cuda_i64(d), bad_h)
+        assert e.value.code == B.HC_ERR_INVALID and "out of range" in str(e.value)
+        dup = h.copy()
+        dup[7] = dup[3]
+        with pytest.raises(B.HcError):
+            rig.pool.write_back_all_layers(cuda_i64(d), dup)
+        rig.pool.sync()
+        assert np.array_equal(rig.host.np, host_before)
+        # load-back: device lists; the kernel skips the bad row and reports it
+        bad_d = d2.copy()
+        bad_d[3] = SHAPE.device_slots + 5
+        dev0 = [[rig.dev[b][l].cpu().numpy() for l in range(SHAPE.layers)] for b in range(2)]
+        rig.pool.load_back_layer(0, cuda_i64(h), cuda_i64(bad_d), None)
+        with pytest.raises(B.HcError) as e:
+            rig.pool.sync()
+        assert e.value.code == B.HC_ERR_DEVICE
+        rig.pool.sync()  # the report is cleared once read
+        keep = np.arange(h.size) != 3
+        O.load_back_layer(rig.geom, 0, dev0, rig.host.np, h[keep], bad_d[keep])
+        for b in range(2):
+            assert np.array_equal(rig.dev[b][0].cpu().numpy(), dev0[b][0])
+    finally:
+        rig.close()
+
+
+@pytest.mark.gpu
+def test_validate_flag_reports_misaligned_page_blocks():
+    say("[events] validate page blocks")
+    rig = Rig(BLOCKS, seed=11, flags=B.HC_FLAG_VALIDATE)
+    try:
+        P = BLOCKS.page_size
+        pages = W.host_pages(1, BLOCKS.host_pages, 4)
+        h = W.whole_page_tokens(pages, P)
+        d = W.page_aligned_slots(2, BLOCKS.device_slots, P, 4)
+        d_bad = d.copy()
+        d_bad[P:2 * P] += 1  # second page shifted off its boundary
+        rig.pool.load_back_layer(0, cuda_i64(h), cuda_i64(d_bad), None)
+        with pytest.raises(B.HcError) as e:
+            rig.pool.sync()
+        assert e.value.code == B.HC_ERR_DEVICE and "page-block" in str(e.value)
+        rig.pool.load_back_layer(0, cuda_i64(h), cuda_i64(d), None)
+        rig.pool.sync()
+    finally:
+        rig.close()
