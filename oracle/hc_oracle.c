@@ -35,6 +35,11 @@
  *     blocks (E bytes per page per layer, e.g. the DSA indexer page of 64
  *     fp8 keys followed by 64 fp32 scales).  A PAGE block moves with the
  *     token at row 0 of its page; the device block index is slot / P.
+ *   - Token-major page-first ([P4] host-pool and CPU-mock excerpts: staging is
+ *     (tokens, layers, elements) and the mock writes host[token, layer]): per
+ *     sub-buffer the host rows are [page][row][layer][element], i.e. host token
+ *     t = page * P + row holds all its layers back to back.  Page blocks keep
+ *     [page][layer][element].
  *   - Shard layout ([P2]): shard p starts at p * stride; inside it the
  *     sub-buffers follow each other, each [layer][row][element]; stride is
  *     the summed sub-buffer page bytes rounded up to the alignment; the pad
@@ -53,7 +58,7 @@
 
 enum { ORC_OK = 0, ORC_ERR_INVALID = -1 };
 enum { ORC_TOKEN_ROWS = 0, ORC_PAGE_BLOCKS = 1 };
-enum { ORC_PAGE_FIRST = 0, ORC_KV_SPLIT_SHARD = 1 };
+enum { ORC_PAGE_FIRST = 0, ORC_KV_SPLIT_SHARD = 1, ORC_PAGE_FIRST_TOKEN_MAJOR = 2 };
 
 typedef struct orc_geom {
   int32_t layers;       /* L */
@@ -100,6 +105,8 @@ int64_t orc_host_offset(const orc_geom* g, int b, int64_t p, int32_t l, int32_t 
   int64_t inner;
   if (g->gran[b] == ORC_PAGE_BLOCKS)
     inner = (int64_t)l * g->bytes[b];
+  else if (g->layout == ORC_PAGE_FIRST_TOKEN_MAJOR)
+    inner = ((int64_t)r * g->layers + l) * g->bytes[b];
   else
     inner = ((int64_t)l * g->page_size + r) * g->bytes[b];
 
@@ -132,7 +139,8 @@ int orc_check_geom(const orc_geom* g) {
   if (g->layers <= 0 || g->page_size <= 0 || g->nsub <= 0 || g->nsub > ORC_MAX_SUB)
     return ORC_ERR_INVALID;
   if (g->host_pages <= 0 || g->device_slots <= 0) return ORC_ERR_INVALID;
-  if (g->layout != ORC_PAGE_FIRST && g->layout != ORC_KV_SPLIT_SHARD) return ORC_ERR_INVALID;
+  if (g->layout != ORC_PAGE_FIRST && g->layout != ORC_KV_SPLIT_SHARD && g->layout != ORC_PAGE_FIRST_TOKEN_MAJOR)
+    return ORC_ERR_INVALID;
   if (g->layout == ORC_KV_SPLIT_SHARD && g->align <= 0) return ORC_ERR_INVALID;
   for (int b = 0; b < g->nsub; b++) {
     if (g->bytes[b] <= 0) return ORC_ERR_INVALID;

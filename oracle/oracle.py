@@ -29,6 +29,7 @@ TOKEN_ROWS = 0
 PAGE_BLOCKS = 1
 PAGE_FIRST = 0
 KV_SPLIT_SHARD = 1
+PAGE_FIRST_TOKEN_MAJOR = 2
 MAX_SUB = 4
 
 

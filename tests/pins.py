@@ -38,6 +38,8 @@ GEOMS = {
     "shard_kv_pad": O.Geometry(3, 4, [(T, 32), (T, 16)], 6, 64, O.KV_SPLIT_SHARD, align=256),
     "pf_latent_indexer": O.Geometry(2, 4, [(T, 32), (B, 48)], 6, 64, O.PAGE_FIRST),
     "shard_block_pad": O.Geometry(2, 4, [(T, 16), (B, 32)], 5, 32, O.KV_SPLIT_SHARD, align=128),
+    "tm_kv": O.Geometry(3, 4, [(T, 32), (T, 16)], 6, 64, O.PAGE_FIRST_TOKEN_MAJOR),
+    "tm_latent_indexer": O.Geometry(2, 4, [(T, 32), (B, 48)], 6, 64, O.PAGE_FIRST_TOKEN_MAJOR),
 }
 
 
@@ -53,14 +55,19 @@ def layout_walk(g: O.Geometry):
 
     def page_pieces(b, p):
         gran, e = g.subs[b]
-        for l in range(g.layers):
-            if gran == B:
+        if gran == B:
+            for l in range(g.layers):
                 yield ("blk", b, p, l), e
-            else:
+        elif g.layout == O.PAGE_FIRST_TOKEN_MAJOR:
+            for r in range(g.page_size):
+                for l in range(g.layers):
+                    yield ("row", b, p, l, r), e
+        else:
+            for l in range(g.layers):
                 for r in range(g.page_size):
                     yield ("row", b, p, l, r), e
 
-    if g.layout == O.PAGE_FIRST:
+    if g.layout in (O.PAGE_FIRST, O.PAGE_FIRST_TOKEN_MAJOR):
         for b in range(len(g.subs)):
             for p in range(g.host_pages):
                 yield from page_pieces(b, p)
@@ -232,7 +239,15 @@ def pin_write_back_mock_formula():
         want = np.zeros_like(host)
         L, P, H = g.layers, g.page_size, g.host_pages
         page, row = h // P, h % P
-        if g.layout == O.PAGE_FIRST:
+        if g.layout == O.PAGE_FIRST_TOKEN_MAJOR:
+            # the mock's own indexing: host[token, layer] = device_layer[slot]
+            start = 0
+            for b, (_, e) in enumerate(g.subs):
+                region = want[start:start + H * P * L * e].reshape(H * P, L, e)
+                for l in range(L):
+                    region[h, l] = dev[b][l].reshape(-1, e)[d]
+                start += H * P * L * e
+        elif g.layout == O.PAGE_FIRST:
             start = 0
             for b, (_, e) in enumerate(g.subs):
                 region = want[start:start + H * L * P * e].reshape(H, L, P, e)
@@ -374,8 +389,8 @@ def pin_golden_closed_forms():
         name, geo, q = [x.strip() for x in ln.split("|")]
         layout, L, P, H, S, align, subs = geo.split()
         sub = [((T if s[0] == "T" else B), int(s[1:])) for s in subs.split(",")]
-        g = O.Geometry(int(L), int(P), sub, int(H), int(S),
-                       O.KV_SPLIT_SHARD if layout == "shard" else O.PAGE_FIRST, int(align))
+        lay = {"shard": O.KV_SPLIT_SHARD, "page_first": O.PAGE_FIRST, "token_major": O.PAGE_FIRST_TOKEN_MAJOR}[layout]
+        g = O.Geometry(int(L), int(P), sub, int(H), int(S), lay, int(align))
         lhs, rhs = [x.strip() for x in q.split("=")]
         what, *args = lhs.split()
         args = [int(a) for a in args]

@@ -24,6 +24,9 @@ MUTANTS = [
     ("layer and row transposed in the host offset",
      "inner = ((int64_t)l * g->page_size + r) * g->bytes[b];",
      "inner = ((int64_t)r * g->layers + l) * g->bytes[b];"),
+    ("token-major rows laid out layer-major",
+     "inner = ((int64_t)r * g->layers + l) * g->bytes[b];",
+     "inner = ((int64_t)l * g->page_size + r) * g->bytes[b];"),
     ("shard size not rounded up",
      "if (k * a < s) k = k + 1;", ";"),
     ("sub-buffer region ignores the page count",
