@@ -43,11 +43,13 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="llama3_8b_mha_bf16")
     ap.add_argument("--write-back-mode", choices=["auto", "zerocopy", "staged"], default="auto")
-    ap.add_argument("--staging-pages", type=int, default=64)
+    ap.add_argument("--staging-pages", type=int, default=32)
     ap.add_argument("--max-ctas", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-staged-probe", action="store_true")
+    ap.add_argument("--max-pinned-gib", type=float, default=64.0,
+                    help="cap on the pinned host pool; a larger pool keeps the burst and shrinks the page count")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="run one plain device-to-device copy of this size first (a known-size "
                          "reference for the FETCH_SIZE / WRITE_SIZE counters)")
@@ -155,6 +157,12 @@ def main():
     torch.cuda.set_device(0)
     shape = W.SHAPES[args.workload]
     L, P = shape.layers, shape.page_size
+    one, _k1 = B.make_desc(layers=L, page_size=P, subs=[(g, e, [1] * L) for g, e in shape.subs],
+                           device_slots=shape.device_slots, host_pages=1, layout=shape.layout, shard_align=shape.align)
+    cap_pages = int(args.max_pinned_gib * (1 << 30)) // B.host_pool_bytes(one)
+    if cap_pages < shape.host_pages:
+        log(f"[bench] host pool capped at {cap_pages} of {shape.host_pages} pages ({args.max_pinned_gib} GiB pinned)")
+        shape = W.shape_scaled(shape, shape.name, host_pages=cap_pages)
     log(f"[bench] workload {shape.name}: L={L} P={P} subs={shape.subs} S={shape.device_slots} H={shape.host_pages}")
     t_setup = time.perf_counter()
     gen = torch.Generator(device="cuda")

@@ -13,7 +13,8 @@ import os
 import numpy as np
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libhc.so")
+# HC_LIBRARY points the binding at another build of the same sources (tuning variants).
+LIB_PATH = os.environ.get("HC_LIBRARY") or os.path.join(_PKG, "libhc.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python -m host_device_page_amd.build` "
@@ -31,6 +32,7 @@ HC_TOKEN_ROWS = 0
 HC_PAGE_BLOCKS = 1
 HC_LAYOUT_PAGE_FIRST = 0
 HC_LAYOUT_KV_SPLIT_SHARD = 1
+HC_LAYOUT_PAGE_FIRST_TOKEN_MAJOR = 2
 HC_MODE_AUTO = 0
 HC_MODE_STAGED = 1
 HC_MODE_ZEROCOPY = 2

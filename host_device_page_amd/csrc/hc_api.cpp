@@ -52,6 +52,11 @@ int set_err(int code, const char* fmt, ...) {
 
 constexpr int kKinds = 6;  // gather, zc write, zc read, pads, compare, copy engine
 constexpr int32_t kDefaultMaxCtas = 256;
+// Staging chunks are capped at the MI355X Infinity Cache size (256 MB): the gather
+// writes a chunk and the copy engines read it back right away, so a chunk that
+// fits stays cache-resident between the two (measured: 32 x 8 MiB page images
+// gather at 5.9 TB/s, 64 at 5.4 TB/s, 128 at 5.1 TB/s).
+constexpr int64_t kStagingChunkTarget = (int64_t)256 << 20;
 
 struct PlanBuf {
   uint8_t* h = nullptr;   // pinned
@@ -212,6 +217,7 @@ void fill_geom(hc_pool* p) {
     s.host_region = L.host_region[b];
     s.host_page_stride = L.host_page_stride[b];
     s.layer_stride = L.layer_stride[b];
+    s.row_stride = L.row_stride[b];
     s.img_off = L.img_off[b];
   }
 }
@@ -531,6 +537,7 @@ int hc_pool_create(const hc_pool_desc* desc, hc_pool** out) {
     p->staging = (uint8_t*)desc->staging;
     p->staging_bytes = desc->staging_bytes;
     p->chunk_pages = std::min<int64_t>(desc->staging_bytes / L.stride, (int64_t)1 << 20);
+    p->chunk_pages = std::min<int64_t>(p->chunk_pages, std::max<int64_t>(1, kStagingChunkTarget / L.stride));
     if (p->chunk_pages * L.P >= ((int64_t)1 << 31)) p->chunk_pages = (((int64_t)1 << 31) - 1) / L.P;
   }
   // device tables and scratch

@@ -19,7 +19,8 @@ struct SubGeom {
   uint64_t vec_magic;      // ceil(2^40 / vecs): q = (u * magic) >> 40 == u / vecs for u < 2^20
   int64_t host_region;     // page-first: start of this sub-buffer's region; shard: offset inside a shard
   int64_t host_page_stride;// bytes from page p to page p+1 of this sub-buffer in the host pool
-  int64_t layer_stride;    // bytes from layer l to l+1 inside one page (P*elem rows, elem blocks)
+  int64_t layer_stride;    // bytes from layer l to l+1 inside one page
+  int64_t row_stride;      // bytes from row r to r+1 inside one page and layer (0 for page blocks)
   int64_t img_off;         // offset of this sub-buffer inside one staging page image
 };
 
@@ -48,6 +49,7 @@ struct Layout {
   int64_t host_region[HC_MAX_SUBBUFS] = {};
   int64_t host_page_stride[HC_MAX_SUBBUFS] = {};
   int64_t layer_stride[HC_MAX_SUBBUFS] = {};
+  int64_t row_stride[HC_MAX_SUBBUFS] = {};
   int64_t img_off[HC_MAX_SUBBUFS] = {};
   int64_t host_bytes = 0;
   bool has_blocks = false;

@@ -25,9 +25,25 @@
 namespace hc {
 namespace {
 
+// Build-time tuning knobs (hipcc -D...): loads in flight per thread, and whether
+// row loads / stores carry the non-temporal hint (streamed data is not reused).
+#ifndef HC_UNROLL
+#define HC_UNROLL 8
+#endif
+#ifndef HC_NT_LOAD
+#define HC_NT_LOAD 0
+#endif
+#ifndef HC_NT_STORE
+#define HC_NT_STORE 0
+#endif
+#ifndef HC_TILE
+#define HC_TILE 256
+#endif
+
 constexpr int kThreads = 256;  // 4 waves of 64
-constexpr int kTile = 256;     // tokens per unit: one per thread at intake
-constexpr int kUnroll = 8;     // 16-byte loads in flight per thread
+constexpr int kTile = HC_TILE; // tokens per unit (<= kThreads): one per thread at intake
+static_assert(kTile <= kThreads && kTile % 64 == 0, "tile must be whole waves of one block");
+constexpr int kUnroll = HC_UNROLL;
 constexpr int kWaves = kThreads / 64;
 
 // 16-byte vector in global address space (global_load/store_dwordx4, not flat).
@@ -35,8 +51,20 @@ typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(1))) const v4u* gload_t;
 typedef __attribute__((address_space(1))) v4u* gstore_t;
 
-__device__ __forceinline__ v4u ld16(uint64_t a) { return *reinterpret_cast<gload_t>(a); }
-__device__ __forceinline__ void st16(uint64_t a, v4u v) { *reinterpret_cast<gstore_t>(a) = v; }
+__device__ __forceinline__ v4u ld16(uint64_t a) {
+#if HC_NT_LOAD
+  return __builtin_nontemporal_load(reinterpret_cast<gload_t>(a));
+#else
+  return *reinterpret_cast<gload_t>(a);
+#endif
+}
+__device__ __forceinline__ void st16(uint64_t a, v4u v) {
+#if HC_NT_STORE
+  __builtin_nontemporal_store(v, reinterpret_cast<gstore_t>(a));
+#else
+  *reinterpret_cast<gstore_t>(a) = v;
+#endif
+}
 
 // q = u / vecs for u < 2^20 and vecs <= 2^20 (magic = ceil(2^40 / vecs)).
 __device__ __forceinline__ uint32_t div_vecs(uint32_t u, uint64_t magic) {
@@ -94,9 +122,7 @@ __device__ __forceinline__ uint64_t layer_base(const SubGeom& s, int l) { return
 
 // Host byte offset of (sub s, page p, layer l, row r).
 __device__ __forceinline__ int64_t host_off(const SubGeom& s, int64_t p, int l, int r) {
-  int64_t o = s.host_region + p * s.host_page_stride + (int64_t)l * s.layer_stride;
-  if (s.gran == HC_TOKEN_ROWS) o += (int64_t)r * s.elem;
-  return o;
+  return s.host_region + p * s.host_page_stride + (int64_t)l * s.layer_stride + (int64_t)r * s.row_stride;
 }
 
 // Device byte offset of slot d inside one layer.
@@ -120,7 +146,7 @@ __global__ __launch_bounds__(kThreads) void k_gather_stage(Geom g, const int64_t
   const int64_t i = t0 + (int64_t)blockIdx.x * kTile + threadIdx.x;
   bool keep = false;
   uint64_t src = 0, dst = 0;
-  if (i < t0 + count) {
+  if (threadIdx.x < kTile && i < t0 + count) {
     const int32_t sr = srow[i];
     if (sr >= 0) {
       const int32_t slot = sr / g.P;
@@ -130,8 +156,7 @@ __global__ __launch_bounds__(kThreads) void k_gather_stage(Geom g, const int64_t
         if (d >= 0 && d < g.S) {
           src = layer_base(s, l) + (uint64_t)dev_off(s, d, g.P);
           dst = (uint64_t)staging + (uint64_t)((int64_t)slot * g.img_bytes + s.img_off +
-                                               (int64_t)l * s.layer_stride +
-                                               (s.gran == HC_TOKEN_ROWS ? (int64_t)r * s.elem : 0));
+                                               (int64_t)l * s.layer_stride + (int64_t)r * s.row_stride);
           keep = true;
         } else {
           atomicOr(err, 1);
@@ -170,7 +195,7 @@ __global__ __launch_bounds__(kThreads) void k_zc_write(Geom g, const int64_t* __
     const int64_t j = tile * kTile + threadIdx.x;
     bool keep = false;
     uint64_t src = 0, dst = 0;
-    if (j < count) {
+    if (threadIdx.x < kTile && j < count) {
       const int64_t i = tok_list ? (int64_t)tok_list[j] : j;
       const int64_t d = dev_idx[i];
       const int64_t h = host_idx[i];
@@ -218,7 +243,7 @@ __global__ __launch_bounds__(kThreads) void k_zc_read(Geom g, int32_t layer, con
     bool keep = false;
     uint64_t src = 0, dst = 0;
     int64_t d = 0, h = 0;
-    const bool live = i < n;
+    const bool live = threadIdx.x < kTile && i < n;
     if (live) {
       d = dev_idx[i];
       h = host_idx[i];
@@ -293,7 +318,7 @@ __global__ __launch_bounds__(kThreads) void k_compare(Geom g, const int64_t* __r
   const int64_t i = (int64_t)blockIdx.x * kTile + threadIdx.x;
   bool keep = false;
   uint64_t x = 0, y = 0;
-  if (i < n) {
+  if (threadIdx.x < kTile && i < n) {
     const int64_t da = a[i], dc = c[i];
     if (da >= 0 && da < g.S && dc >= 0 && dc < g.S) {
       if (s.gran == HC_TOKEN_ROWS || da % g.P == 0) {

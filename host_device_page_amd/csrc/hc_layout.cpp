@@ -3,9 +3,11 @@
 //
 // Layouts (see hc.h): page-first [page][layer][row][elem] per sub-buffer, regions
 // back to back (page_first_direct on the loader-thread page, sglang PR 38472,
-// Motivation); shard = one page of every sub-buffer followed by zero padding to
-// the alignment (CacheStore H2H page, unified-cache-management PR 1292, section
-// "page_first_kv_split support").
+// Motivation); token-major page-first [page][row][layer][elem] (hybrid-pool
+// write-back page, host-pool and CPU-mock excerpts); shard = one page of every
+// sub-buffer followed by zero padding to the alignment (CacheStore H2H page,
+// unified-cache-management PR 1292, section "page_first_kv_split support").
+// Every row sits at region + page*page_stride + layer*layer_stride + row*row_stride.
 #include <stdio.h>
 #include <string.h>
 
@@ -44,7 +46,8 @@ int layout_from_desc(const hc_pool_desc* d, Layout* out, char* msg, size_t len) 
     return fail(msg, len, HC_ERR_INVALID, "page_size must be in [1, 2^20]");
   if (d->num_subbufs < 1 || d->num_subbufs > HC_MAX_SUBBUFS)
     return fail(msg, len, HC_ERR_INVALID, "num_subbufs must be in [1, HC_MAX_SUBBUFS]");
-  if (d->layout != HC_LAYOUT_PAGE_FIRST && d->layout != HC_LAYOUT_KV_SPLIT_SHARD)
+  if (d->layout != HC_LAYOUT_PAGE_FIRST && d->layout != HC_LAYOUT_KV_SPLIT_SHARD &&
+      d->layout != HC_LAYOUT_PAGE_FIRST_TOKEN_MAJOR)
     return fail(msg, len, HC_ERR_INVALID, "unknown layout");
   if (d->device_slots < 1 || d->host_pages < 1)
     return fail(msg, len, HC_ERR_INVALID, "device_slots and host_pages must be >= 1");
@@ -84,7 +87,16 @@ int layout_from_desc(const hc_pool_desc* d, Layout* out, char* msg, size_t len) 
     }
     if (!mul_ok(per_layer, L.L, &sp)) return fail(msg, len, HC_ERR_INVALID, "page bytes overflow");
     L.subpage[b] = sp;
-    L.layer_stride[b] = per_layer;
+    if (L.gran[b] == HC_PAGE_BLOCKS) {
+      L.layer_stride[b] = L.elem[b];  // [page][layer]
+      L.row_stride[b] = 0;
+    } else if (L.layout == HC_LAYOUT_PAGE_FIRST_TOKEN_MAJOR) {
+      L.layer_stride[b] = L.elem[b];  // [page][row][layer]
+      L.row_stride[b] = (int64_t)L.L * L.elem[b];
+    } else {
+      L.layer_stride[b] = per_layer;  // [page][layer][row]
+      L.row_stride[b] = L.elem[b];
+    }
     L.img_off[b] = payload;
     if (!add_ok(payload, sp, &payload)) return fail(msg, len, HC_ERR_INVALID, "page bytes overflow");
   }
@@ -120,9 +132,8 @@ int layout_from_desc(const hc_pool_desc* d, Layout* out, char* msg, size_t len) 
 }
 
 int64_t layout_host_offset(const Layout& L, int b, int64_t page, int32_t layer, int32_t row) {
-  int64_t o = L.host_region[b] + page * L.host_page_stride[b] + (int64_t)layer * L.layer_stride[b];
-  if (L.gran[b] == HC_TOKEN_ROWS) o += (int64_t)row * L.elem[b];
-  return o;
+  return L.host_region[b] + page * L.host_page_stride[b] + (int64_t)layer * L.layer_stride[b] +
+         (int64_t)row * L.row_stride[b];
 }
 
 }  // namespace hc

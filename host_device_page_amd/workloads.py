@@ -21,6 +21,7 @@ TOKEN_ROWS = 0
 PAGE_BLOCKS = 1
 PAGE_FIRST = 0
 KV_SPLIT_SHARD = 1
+PAGE_FIRST_TOKEN_MAJOR = 2
 
 
 @dataclass(frozen=True)
@@ -65,6 +66,10 @@ SHAPES = {
     "dsa_mla_indexer_78l": PoolShape("dsa_mla_indexer_78l", 78, 64,
                                      ((TOKEN_ROWS, 576 * 2), (PAGE_BLOCKS, DSA_INDEXER_PAGE_BLOCK)),
                                      524288, 2048, sub_names=("latent", "indexer")),
+    # Llama-3-8B pool with the token-major page-first host layout [page][row][layer].
+    "llama3_8b_mha_bf16_token_major": PoolShape("llama3_8b_mha_bf16_token_major", 32, 64,
+                                                ((TOKEN_ROWS, bf16_row_bytes(8, 128)),) * 2, 262144, 8192,
+                                                layout=PAGE_FIRST_TOKEN_MAJOR, sub_names=("k", "v")),
     # MHA in K page | V page | pad shards: 48 layers, 8 x 128 bf16, 32-token pages.
     "mha_kv_split_shard_bf16": PoolShape("mha_kv_split_shard_bf16", 48, 32,
                                          ((TOKEN_ROWS, bf16_row_bytes(8, 128)),) * 2, 262144, 4096,
@@ -201,7 +206,7 @@ def burst_for(shape: PoolShape, seed: int, purpose: str = "write_back") -> Burst
         pages = host_pages(seed, H, 32)
         h = whole_page_tokens(pages, P)
         d = permutation_slots(seed + 1, S, h.size)
-    elif shape.name == "llama3_8b_mha_bf16":
+    elif shape.name in ("llama3_8b_mha_bf16", "llama3_8b_mha_bf16_token_major"):
         pages = host_pages(seed, H, 256)
         h = whole_page_tokens(pages, P)
         d = segment_slots(seed + 1, S, h.size)
@@ -229,7 +234,7 @@ def fresh_slots_like(shape: PoolShape, burst: Burst, seed: int) -> np.ndarray:
     if any(g == PAGE_BLOCKS for g, _ in shape.subs):
         used_pages = np.unique(burst.device_idx // P)
         return page_aligned_slots(seed, S, P, n // P, exclude_pages=used_pages)
-    if shape.name in ("llama3_8b_mha_bf16", "dsv3_mla_bf16"):
+    if shape.name in ("llama3_8b_mha_bf16", "llama3_8b_mha_bf16_token_major", "dsv3_mla_bf16"):
         return segment_slots(seed, S, n, exclude=burst.device_idx)
     if shape.name == "mha_kv_split_shard_bf16":
         return scattered_slots(seed, S, n, exclude=burst.device_idx)

@@ -24,6 +24,12 @@
  *                             rounded up to shard_align (CacheStore H2H page,
  *                             unified-cache-management PR 1292, section
  *                             "page_first_kv_split support"; Direct I/O uses 4096).
+ *   HC_LAYOUT_PAGE_FIRST_TOKEN_MAJOR
+ *                             per sub-buffer [page][row][layer][elem_bytes], i.e. host
+ *                             token t = page * page_size + row holds its layers back to
+ *                             back (the host-pool staging shape and the CPU mock
+ *                             host[token, layer] of the hybrid-pool write-back page);
+ *                             page blocks stay [page][layer].
  * A sub-buffer holds either token rows (HC_TOKEN_ROWS: elem_bytes per token per
  * layer) or page blocks (HC_PAGE_BLOCKS: elem_bytes per page per layer, e.g. the
  * DSA indexer-K page of 64 fp8 keys and 64 fp32 scales).  A page block moves
@@ -74,7 +80,7 @@ typedef enum hc_status {
 } hc_status;
 
 enum { HC_TOKEN_ROWS = 0, HC_PAGE_BLOCKS = 1 };
-enum { HC_LAYOUT_PAGE_FIRST = 0, HC_LAYOUT_KV_SPLIT_SHARD = 1 };
+enum { HC_LAYOUT_PAGE_FIRST = 0, HC_LAYOUT_KV_SPLIT_SHARD = 1, HC_LAYOUT_PAGE_FIRST_TOKEN_MAJOR = 2 };
 /* Transfer modes.  STAGED: device kernels relayout through the device staging
  * buffer and the copy engines (hipMemcpyAsync) cross the host link.  ZEROCOPY:
  * kernels read or write the pinned host pool directly.  AUTO: the library's
@@ -105,7 +111,8 @@ typedef struct hc_pool_desc {
   void* host_base;      /* pinned host memory (hc_host_alloc or hipHostMalloc), >= hc_host_pool_bytes */
   int64_t host_bytes;   /* size of host_base */
   void* staging;        /* device memory for HC_MODE_STAGED write-back; NULL when no staged mode is used */
-  int64_t staging_bytes;/* size of staging; the chunk is staging_bytes / hc_staging_page_bytes pages */
+  int64_t staging_bytes;/* size of staging; the chunk is staging_bytes / hc_staging_page_bytes pages,
+                           capped so that one chunk fits the 256 MB Infinity Cache (at least 1 page) */
   void* copy_stream;    /* hipStream_t every transfer of this pool is enqueued on (NULL: null stream) */
   int32_t write_back_mode; /* HC_MODE_* */
   int32_t load_back_mode;  /* HC_MODE_* (load-back is always zero-copy in this version) */

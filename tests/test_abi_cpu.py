@@ -96,19 +96,22 @@ GEOMS = [
     dict(layers=1, page_size=16, subs=[(0, 48), (0, 16), (1, 32), (0, 64)], host_pages=64, device_slots=2048, layout=0),
     dict(layers=61, page_size=64, subs=[(0, 1152)], host_pages=16384, device_slots=524288, layout=0),
     dict(layers=5, page_size=7, subs=[(1, 16), (0, 32)], host_pages=9, device_slots=70, layout=1),
+    dict(layers=32, page_size=64, subs=[(0, 2048), (0, 2048)], host_pages=8192, device_slots=262144, layout=2),
+    dict(layers=78, page_size=64, subs=[(0, 1152), (1, 8448)], host_pages=2048, device_slots=524288, layout=2),
+    dict(layers=5, page_size=7, subs=[(1, 16), (0, 32), (0, 48)], host_pages=9, device_slots=70, layout=2),
 ]
 
 
 @pytest.mark.parametrize("gi", range(len(GEOMS)))
 def test_layout_arithmetic_matches_oracle(gi):
     g = GEOMS[gi]
-    og = O.Geometry(g["layers"], g["page_size"], g["subs"], g["host_pages"], g["device_slots"], g["layout"], 4096 if g["layout"] else 4096)
+    og = O.Geometry(g["layers"], g["page_size"], g["subs"], g["host_pages"], g["device_slots"], g["layout"], 4096)
     d, _k = B.make_desc(layers=g["layers"], page_size=g["page_size"],
                         subs=[(gr, e, [0x10000] * g["layers"]) for gr, e in g["subs"]],
                         device_slots=g["device_slots"], host_pages=g["host_pages"], layout=g["layout"],
                         shard_align=4096)
     assert B.host_pool_bytes(d) == O.host_pool_bytes(og)
-    want_img = O.shard_bytes(og) if g["layout"] else O.page_payload_bytes(og)
+    want_img = O.shard_bytes(og) if g["layout"] == 1 else O.page_payload_bytes(og)
     assert B.staging_page_bytes(d) == want_img
     rng = np.random.default_rng(gi)
     for _ in range(300):

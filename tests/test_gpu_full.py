@@ -116,6 +116,8 @@ def round_trip(rig, burst, d2):
 @pytest.mark.parametrize("name,mode", [
     ("llama3_8b_mha_bf16", "zerocopy"),
     ("llama3_8b_mha_bf16", "staged"),
+    ("llama3_8b_mha_bf16_token_major", "zerocopy"),
+    ("llama3_8b_mha_bf16_token_major", "staged"),
     ("dsv3_mla_bf16", "zerocopy"),
     ("mha_kv_split_shard_bf16", "zerocopy"),
     ("mha_kv_split_shard_bf16", "staged"),

@@ -13,7 +13,7 @@ from host_device_page_amd import workloads as W
 from gpu_support import Rig, cuda_i64, load_back_and_check, say, write_back_and_check
 
 T, BLK = W.TOKEN_ROWS, W.PAGE_BLOCKS
-PF, SH = W.PAGE_FIRST, W.KV_SPLIT_SHARD
+PF, SH, TM = W.PAGE_FIRST, W.KV_SPLIT_SHARD, W.PAGE_FIRST_TOKEN_MAJOR
 
 
 def S(name, L, P, subs, slots, pages, layout=PF, align=4096):
@@ -69,6 +69,9 @@ CASES = [
     ("page1_rows", S("page1_rows", 3, 1, [(T, 32)], 2048, 1024), "scatter", 700, 0),
     ("four_subs_one_layer", S("four_subs_one_layer", 1, 16, [(T, 48), (T, 16), (BLK, 32), (T, 64)], 2048, 64),
      "aligned", 33, 0),
+    ("token_major_rows", S("token_major_rows", 4, 64, [(T, 2048)] * 2, 32768, 64, TM), "segment", 12, 41),
+    ("token_major_indexer", S("token_major_indexer", 3, 64, [(T, 1152), (BLK, 8448)], 8192, 32, TM), "aligned", 10, 0),
+    ("token_major_small_rows", S("token_major_small_rows", 5, 8, [(T, 16), (T, 48)], 4096, 64, TM), "requests", 50, 0),
 ]
 
 
