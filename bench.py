@@ -286,6 +286,20 @@ def main():
                 "bytes_per_launch": dom["bytes_per_launch"],
                 "peak_source": "hipMemcpyAsync pinned<->device 1 GiB best of 5, measured in this run",
                 "pcie5_x16_nominal_GBps": PCIE5_X16_GBS}
+    # hand-over cost on the calling thread: the per-layer enqueue inline vs on the loader thread
+    handover = {}
+    for asynchronous in (False, True):
+        ld = B.Loader(pool, L, asynchronous=asynchronous)
+        times = []
+        for _ in range(5):
+            t_s = time.perf_counter()
+            bu = ld.submit(h_t, d2_t, burst.n, layer_events)
+            times.append(time.perf_counter() - t_s)
+            bu.wait()
+            bu.release()
+        ld.close()
+        handover["loader_thread" if asynchronous else "inline"] = round(1e3 * float(np.median(times)), 4)
+    log(f"[bench] load-back hand-over per burst (ms): {handover}")
     pool.close()
 
     # staged relayout kernel (HBM-bound): same burst through the staged write-back
@@ -348,6 +362,7 @@ def main():
         "host_link_peak_GBps": {"h2d": round(peak_h2d, 3), "d2h": round(peak_d2h, 3)},
         "frac_of_link_peak": {"write_back": round(wb_gbs / peak_d2h, 4), "load_back": round(lb_gbs / peak_h2d, 4)},
         "cpu_enqueue_ms_per_step": round(1e3 * float(np.median(enqueue_s)), 3),
+        "load_back_handover_ms": handover,
         "kernel_avg_ms": {"zc_read": round(ms_rd / max(1, n_rd), 4), "zc_write": round(ms_wr / max(1, n_wr), 4)},
         "roofline": roofline,
         "roofline_hbm": roofline_hbm,

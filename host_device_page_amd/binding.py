@@ -9,6 +9,7 @@ from __future__ import annotations
 
 import ctypes
 import os
+import weakref
 
 import numpy as np
 
@@ -64,6 +65,18 @@ class hc_pool_desc(ctypes.Structure):
 
 _D = ctypes.POINTER(hc_pool_desc)
 _V = ctypes.c_void_p
+
+LOAD_LAYER_FN = ctypes.CFUNCTYPE(ctypes.c_int, _V, ctypes.c_int32, _V, _V, ctypes.c_int64, _V)
+WAIT_EVENT_FN = ctypes.CFUNCTYPE(ctypes.c_int, _V, _V)
+RECORD_EVENT_FN = ctypes.CFUNCTYPE(ctypes.c_int, _V, _V)
+SYNC_EVENT_FN = ctypes.CFUNCTYPE(ctypes.c_int, _V, _V)
+STREAM_WAIT_FN = ctypes.CFUNCTYPE(ctypes.c_int, _V, _V, _V)
+
+
+class hc_loader_ops(ctypes.Structure):
+    _fields_ = [("ctx", _V), ("load_layer", LOAD_LAYER_FN), ("wait_event", WAIT_EVENT_FN),
+                ("record_event", RECORD_EVENT_FN), ("sync_event", SYNC_EVENT_FN),
+                ("stream_wait", STREAM_WAIT_FN)]
 _I64P = ctypes.POINTER(ctypes.c_int64)
 _SIGS = {
     "hc_desc_check": (ctypes.c_int, [_D]),
@@ -81,6 +94,16 @@ _SIGS = {
     "hc_round_trip_check": (ctypes.c_int, [_V, _V, _V, ctypes.c_int64, _I64P]),
     "hc_pool_kernel_time": (ctypes.c_int, [_V, ctypes.c_int32, ctypes.c_int32, _I64P,
                                            ctypes.POINTER(ctypes.c_double)]),
+    "hc_loader_create": (ctypes.c_int, [_V, ctypes.POINTER(hc_loader_ops), ctypes.c_int32, ctypes.c_int32,
+                                        ctypes.POINTER(_V)]),
+    "hc_loader_submit": (ctypes.c_int, [_V, _V, _V, ctypes.c_int64, ctypes.POINTER(_V), _V, ctypes.POINTER(_V)]),
+    "hc_burst_wait_layer": (ctypes.c_int, [_V, ctypes.c_int32, _V]),
+    "hc_burst_wait": (ctypes.c_int, [_V]),
+    "hc_burst_query": (ctypes.c_int, [_V, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]),
+    "hc_burst_release": (ctypes.c_int, [_V]),
+    "hc_loader_drain": (ctypes.c_int, [_V]),
+    "hc_loader_info": (ctypes.c_int, [_V, _I64P, ctypes.POINTER(ctypes.c_int32)]),
+    "hc_loader_destroy": (ctypes.c_int, [_V]),
     "hc_last_error": (ctypes.c_char_p, []),
     "hc_version": (ctypes.c_int, []),
 }
@@ -297,6 +320,96 @@ class Pool:
     def close(self) -> None:
         if self.handle.value:
             check(lib.hc_pool_destroy(self.handle), "hc_pool_destroy")
+            self.handle = _V()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+# ---------------------------------------------------------------- asynchronous load-back enqueue
+class Burst:
+    """One submitted load-back burst (hc_burst)."""
+
+    def __init__(self, handle, keep, loader):
+        self.handle = handle
+        self._keep = keep  # index tensors and event array stay alive until release
+        self._loader = loader  # a burst must be released before its loader is destroyed
+
+    def wait_layer(self, layer: int, consumer_stream=None) -> None:
+        """consumer_stream: a torch stream, a raw address (int), or None (block the thread)."""
+        s = consumer_stream
+        if s is not None and not isinstance(s, int):
+            s = s.cuda_stream
+        check(lib.hc_burst_wait_layer(self.handle, layer, _V(s) if s else None), "hc_burst_wait_layer")
+
+    def wait(self) -> None:
+        check(lib.hc_burst_wait(self.handle), "hc_burst_wait")
+
+    def status(self) -> int:
+        return lib.hc_burst_wait(self.handle)
+
+    def query(self):
+        n, done = ctypes.c_int32(), ctypes.c_int32()
+        check(lib.hc_burst_query(self.handle, ctypes.byref(n), ctypes.byref(done)), "hc_burst_query")
+        return n.value, bool(done.value)
+
+    def release(self) -> None:
+        if self.handle.value:
+            check(lib.hc_burst_release(self.handle), "hc_burst_release")
+            self.handle = _V()
+            self._keep = None
+
+    def __del__(self):
+        try:
+            self.release()
+        except Exception:
+            pass
+
+
+class Loader:
+    """hc_loader: per-layer load-back bursts enqueued by a worker thread (async) or inline.
+    pool: a Pool (device operations of that pool) or None with explicit ops."""
+
+    def __init__(self, pool: "Pool | None", num_layers: int, asynchronous: bool = True, ops: hc_loader_ops = None):
+        self.handle = _V()
+        self._pool = pool
+        self._ops = ops
+        self._bursts = weakref.WeakSet()
+        check(lib.hc_loader_create(pool.handle if pool is not None else None,
+                                   ctypes.byref(ops) if ops is not None else None,
+                                   num_layers, 1 if asynchronous else 0, ctypes.byref(self.handle)),
+              "hc_loader_create")
+        self.num_layers = num_layers
+
+    def submit(self, host_idx, device_idx, n: int, layer_events, start_event=None) -> Burst:
+        """layer_events: HipEvent objects or raw handles (ints); start_event likewise or None."""
+        raw = [e.handle.value if isinstance(e, HipEvent) else int(e) for e in layer_events]
+        arr = (_V * len(raw))(*raw)
+        st = start_event.handle.value if isinstance(start_event, HipEvent) else start_event
+        out = _V()
+        check(lib.hc_loader_submit(self.handle, _V(_ptr(host_idx)), _V(_ptr(device_idx)), n, arr,
+                                   _V(st) if st else None, ctypes.byref(out)), "hc_loader_submit")
+        b = Burst(out, (host_idx, device_idx, arr, layer_events, start_event), self)
+        self._bursts.add(b)
+        return b
+
+    def drain(self) -> None:
+        check(lib.hc_loader_drain(self.handle), "hc_loader_drain")
+
+    def info(self):
+        f, r = ctypes.c_int64(), ctypes.c_int32()
+        check(lib.hc_loader_info(self.handle, ctypes.byref(f), ctypes.byref(r)), "hc_loader_info")
+        return f.value, bool(r.value)
+
+    def close(self) -> None:
+        if self.handle.value:
+            check(lib.hc_loader_drain(self.handle), "hc_loader_drain")
+            for b in list(self._bursts):
+                b.release()
+            check(lib.hc_loader_destroy(self.handle), "hc_loader_destroy")
             self.handle = _V()
 
     def __del__(self):

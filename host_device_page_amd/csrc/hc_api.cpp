@@ -22,6 +22,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -34,13 +35,18 @@ namespace {
 
 thread_local std::string g_err;
 
-int set_err(int code, const char* fmt, ...) {
+int vset_err(int code, const char* fmt, va_list ap) {
   char buf[512];
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  g_err = buf;
+  return code;
+}
+
+int set_err(int code, const char* fmt, ...) {
   va_list ap;
   va_start(ap, fmt);
-  vsnprintf(buf, sizeof(buf), fmt, ap);
+  vset_err(code, fmt, ap);
   va_end(ap);
-  g_err = buf;
   return code;
 }
 
@@ -85,6 +91,9 @@ struct TimedLaunch {
 }  // namespace
 
 struct hc_pool {
+  // Serializes the pool's entry points: a loader thread and the caller may use one
+  // pool at the same time.  Recursive because hc_round_trip_check calls hc_pool_sync.
+  std::recursive_mutex mu;
   Layout lay;
   Geom geom;
   int device = 0;
@@ -602,6 +611,7 @@ int hc_pool_mode(const hc_pool* p, int32_t which, int32_t* out_mode) {
 
 int hc_pool_sync(hc_pool* p) {
   if (!p) return set_err(HC_ERR_INVALID, "pool is null");
+  std::lock_guard<std::recursive_mutex> lock(p->mu);
   int rc = use_device(p);
   if (rc != HC_OK) return rc;
   HIP_TRY(hipMemcpyAsync(p->h_err, p->d_err, sizeof(int32_t), hipMemcpyDeviceToHost, p->stream));
@@ -620,6 +630,7 @@ int hc_pool_sync(hc_pool* p) {
 int hc_write_back_all_layers(hc_pool* p, const int64_t* device_idx, const int64_t* host_idx, int64_t n,
                              void* event) {
   if (!p) return set_err(HC_ERR_INVALID, "pool is null");
+  std::lock_guard<std::recursive_mutex> lock(p->mu);
   int rc = use_device(p);
   if (rc != HC_OK) return rc;
   auto finish = [&](int code) {
@@ -709,6 +720,7 @@ int hc_load_back_layer(hc_pool* p, int32_t layer, const int64_t* host_idx, const
     if (event) (void)hipEventRecord((hipEvent_t)event, nullptr);
     return set_err(HC_ERR_INVALID, "pool is null");
   }
+  std::lock_guard<std::recursive_mutex> lock(p->mu);
   int rc = use_device(p);
   auto finish = [&](int code) {
     int r2 = record_event(event, p->stream);
@@ -735,6 +747,7 @@ int hc_load_back_layer(hc_pool* p, int32_t layer, const int64_t* host_idx, const
 int hc_round_trip_check(hc_pool* p, const int64_t* idx_a, const int64_t* idx_b, int64_t n,
                         int64_t* mismatched_units) {
   if (!p || !mismatched_units) return set_err(HC_ERR_INVALID, "null argument");
+  std::lock_guard<std::recursive_mutex> lock(p->mu);
   int rc = use_device(p);
   if (rc != HC_OK) return rc;
   if (n < 0) return set_err(HC_ERR_INVALID, "n must be >= 0");
@@ -754,6 +767,7 @@ int hc_round_trip_check(hc_pool* p, const int64_t* idx_a, const int64_t* idx_b, 
 
 int hc_pool_kernel_time(hc_pool* p, int32_t kind, int32_t reset, int64_t* launches, double* total_ms) {
   if (!p || !launches || !total_ms) return set_err(HC_ERR_INVALID, "null argument");
+  std::lock_guard<std::recursive_mutex> lock(p->mu);
   if (kind < 0 || kind >= kKinds) return set_err(HC_ERR_INVALID, "kind out of range");
   int rc = use_device(p);
   if (rc != HC_OK) return rc;
@@ -771,3 +785,58 @@ int hc_pool_kernel_time(hc_pool* p, int32_t kind, int32_t reset, int64_t* launch
 }
 
 }  // extern "C"
+
+namespace {
+
+int op_load_layer(void* ctx, int32_t layer, const int64_t* h, const int64_t* d, int64_t n, void* ev) {
+  return hc_load_back_layer((hc_pool*)ctx, layer, h, d, n, ev);
+}
+
+int op_wait_event(void* ctx, void* ev) {
+  hc_pool* p = (hc_pool*)ctx;
+  std::lock_guard<std::recursive_mutex> lock(p->mu);
+  HIP_TRY(hipStreamWaitEvent(p->stream, (hipEvent_t)ev, 0));
+  return HC_OK;
+}
+
+int op_record_event(void* ctx, void* ev) {
+  hc_pool* p = (hc_pool*)ctx;
+  std::lock_guard<std::recursive_mutex> lock(p->mu);
+  HIP_TRY(hipEventRecord((hipEvent_t)ev, p->stream));
+  return HC_OK;
+}
+
+int op_sync_event(void*, void* ev) {
+  HIP_TRY(hipEventSynchronize((hipEvent_t)ev));
+  return HC_OK;
+}
+
+int op_stream_wait(void*, void* stream, void* ev) {
+  HIP_TRY(hipStreamWaitEvent((hipStream_t)stream, (hipEvent_t)ev, 0));
+  return HC_OK;
+}
+
+}  // namespace
+
+namespace hc {
+
+int set_error(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vset_err(code, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+void pool_loader_ops(hc_pool* pool, hc_loader_ops* ops) {
+  ops->ctx = pool;
+  ops->load_layer = op_load_layer;
+  ops->wait_event = op_wait_event;
+  ops->record_event = op_record_event;
+  ops->sync_event = op_sync_event;
+  ops->stream_wait = op_stream_wait;
+}
+
+int pool_layers(const hc_pool* pool) { return pool->lay.L; }
+
+}  // namespace hc

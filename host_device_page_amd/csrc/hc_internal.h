@@ -59,6 +59,12 @@ struct Layout {
 int layout_from_desc(const hc_pool_desc* desc, Layout* out, char* msg, size_t msg_len);
 int64_t layout_host_offset(const Layout& lay, int b, int64_t page, int32_t layer, int32_t row);
 
+// Thread-local error message of the C ABI (hc_last_error); returns `code`.
+int set_error(int code, const char* fmt, ...);
+// The pool's own device operations for an hc_loader, and its layer count.
+void pool_loader_ops(hc_pool* pool, hc_loader_ops* ops);
+int pool_layers(const hc_pool* pool);
+
 // Kernel launchers (hc_kernels.hip).  All enqueue on `stream` and return the launch status.
 hipError_t launch_gather_stage(const Geom& g, const int64_t* dev_idx, const int32_t* srow,
                                int64_t t0, int64_t count, uint8_t* staging, int32_t* err,

@@ -207,6 +207,71 @@ int hc_load_back_layer(hc_pool* pool, int32_t layer, const int64_t* host_idx,
 int hc_round_trip_check(hc_pool* pool, const int64_t* idx_a, const int64_t* idx_b, int64_t n,
                         int64_t* mismatched_units);
 
+/* ---------------------------------------------------------------- asynchronous load-back enqueue
+ * A loader runs the per-layer load-back of whole bursts off the caller's thread
+ * (loader-thread page, sglang PR 38472, Modifications): the caller hands over a
+ * burst and returns at once; one FIFO worker thread makes the transfer stream
+ * wait for the burst's start event, enqueues every layer in order and records
+ * each layer's event.  Each layer also has a CPU-side "recorded" flag, because a
+ * stream that waits on an event nobody has recorded yet does not wait at all:
+ * hc_burst_wait_layer first blocks on the flag, then makes the consumer stream
+ * wait on the device event.  Bursts complete in submission order.  If enqueueing
+ * layer k fails, layers k..L-1 still get their events recorded and flags set, so
+ * no consumer hangs, and the burst reports the error (its rows are stale); the
+ * next burst is served normally.  A burst whose layer events are still held by an
+ * earlier, not yet enqueued burst waits for that burst (event reuse backpressure).
+ *
+ * The device side goes through hc_loader_ops.  hc_loader_create with ops == NULL
+ * binds the pool's own operations (hc_load_back_layer, hipStreamWaitEvent,
+ * hipEventRecord, hipEventSynchronize on the pool's copy stream).  Other ops let
+ * the ordering be observed without a GPU. */
+typedef struct hc_loader hc_loader;
+typedef struct hc_burst hc_burst;
+
+typedef struct hc_loader_ops {
+  void* ctx;
+  /* enqueue one layer of a burst and record `event` after it; hc_status */
+  int (*load_layer)(void* ctx, int32_t layer, const int64_t* host_idx, const int64_t* device_idx,
+                    int64_t n, void* event);
+  /* make the transfer stream wait for `event` (the burst's start event) */
+  int (*wait_event)(void* ctx, void* event);
+  /* record `event` on the transfer stream with no transfer before it (failure path) */
+  int (*record_event)(void* ctx, void* event);
+  /* block the calling thread until `event` has completed */
+  int (*sync_event)(void* ctx, void* event);
+  /* make `stream` wait for `event` */
+  int (*stream_wait)(void* ctx, void* stream, void* event);
+} hc_loader_ops;
+
+/* async = 1: one worker thread; async = 0: hc_loader_submit runs the burst inline
+ * on the caller's thread (same call sequence, no thread).  num_layers must equal
+ * the pool's layer count when a pool is given.  ops may be NULL only with a pool. */
+int hc_loader_create(hc_pool* pool, const hc_loader_ops* ops, int32_t num_layers, int32_t async,
+                     hc_loader** out);
+/* Queue one burst.  host_idx / device_idx / n are passed to load_layer unchanged
+ * (device-resident lists for a pool); layer_events: num_layers caller-owned events,
+ * all distinct; start_event: recorded by the producer at hand-over, or NULL.
+ * Returns at once in async mode.  *out is released with hc_burst_release. */
+int hc_loader_submit(hc_loader* loader, const int64_t* host_idx, const int64_t* device_idx, int64_t n,
+                     void* const* layer_events, void* start_event, hc_burst** out);
+/* Block until layer `layer` of the burst is recorded, then make consumer_stream wait
+ * on its event (consumer_stream NULL: block the calling thread until it completes). */
+int hc_burst_wait_layer(hc_burst* burst, int32_t layer, void* consumer_stream);
+/* Block until every layer is enqueued and the last layer's event has completed;
+ * returns the burst's status (HC_OK or the error that stopped its enqueue). */
+int hc_burst_wait(hc_burst* burst);
+/* Non-blocking: layers enqueued so far and whether the burst is fully enqueued. */
+int hc_burst_query(hc_burst* burst, int32_t* layers_enqueued, int32_t* enqueue_done);
+/* Waits for the burst's enqueue to finish, then frees it. */
+int hc_burst_release(hc_burst* burst);
+/* Blocks until every submitted burst is enqueued. */
+int hc_loader_drain(hc_loader* loader);
+/* Number of bursts whose enqueue failed so far, and whether a worker thread runs. */
+int hc_loader_info(hc_loader* loader, int64_t* failed_bursts, int32_t* worker_running);
+/* Drains, joins the worker, frees.  Every burst must be released before.  NULL is a no-op.
+ * Destroy a pool's loaders before the pool. */
+int hc_loader_destroy(hc_loader* loader);
+
 /* ---------------------------------------------------------------- measurement */
 
 /* Per-kernel timing with HIP events on the copy stream (pools with HC_FLAG_PROFILE).

@@ -1,0 +1,77 @@
+"""The asynchronous load-back enqueue with a real pool: a consumer stream waits on
+each layer through the loader's flags and events and checksums the layer; a failed
+burst releases its consumers; the next burst is served."""
+import numpy as np
+import pytest
+import torch
+
+from host_device_page_amd import binding as B
+from host_device_page_amd import workloads as W
+from gpu_support import Rig, cuda_i64, say
+from oracle import oracle as O
+
+T = W.TOKEN_ROWS
+SHAPE = W.PoolShape("loader_rows", 8, 16, ((T, 1024), (T, 512)), 16384, 128)
+
+
+def host_sums(rig, h, layer):
+    out = []
+    for b, (_, e) in enumerate(rig.shape.subs):
+        offs = O.host_offsets(rig.geom, b, layer, h)
+        rows = np.stack([rig.host.np[o:o + e] for o in offs])
+        out.append(int(rows.view(np.int32).astype(np.int64).sum()))
+    return out
+
+
+def dev_sums(rig, layer, d_t):
+    return [rig.dev[b][layer].view(-1, e)[d_t].view(torch.int32).to(torch.int64).sum()
+            for b, (_, e) in enumerate(rig.shape.subs)]
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("asynchronous", [True, False])
+def test_loader_with_consumer_stream(asynchronous):
+    say(f"[loader] async={asynchronous}")
+    rig = Rig(SHAPE, seed=12)
+    loader = None
+    try:
+        pages = W.host_pages(1, SHAPE.host_pages, 48)
+        h = W.whole_page_tokens(pages, SHAPE.page_size)
+        d = W.permutation_slots(2, SHAPE.device_slots, h.size)
+        rig.pool.write_back_all_layers(cuda_i64(d), h)
+        rig.pool.sync()
+        d2 = W.permutation_slots(3, SHAPE.device_slots, h.size, exclude=d)
+        h_t, d2_t = cuda_i64(h), cuda_i64(d2)
+        start = B.HipEvent()
+        start.record(torch.cuda.current_stream())  # the index lists are ready on the producer stream
+        events = [B.HipEvent() for _ in range(SHAPE.layers)]
+        loader = B.Loader(rig.pool, SHAPE.layers, asynchronous=asynchronous)
+        burst = loader.submit(h_t, d2_t, h.size, events, start_event=start)
+        consumer = torch.cuda.Stream()
+        got = []
+        for l in range(SHAPE.layers):
+            burst.wait_layer(l, consumer)
+            with torch.cuda.stream(consumer):
+                got.append(dev_sums(rig, l, d2_t))
+        consumer.synchronize()
+        burst.wait()
+        for l in range(SHAPE.layers):
+            assert [int(x) for x in got[l]] == host_sums(rig, h, l), f"layer {l}"
+        # a failing burst (null host list) still completes every layer event
+        bad_events = [B.HipEvent() for _ in range(SHAPE.layers)]
+        bad = loader.submit(None, d2_t, h.size, bad_events)
+        bad.wait_layer(SHAPE.layers - 1, consumer)
+        consumer.synchronize()
+        with pytest.raises(B.HcError):
+            bad.wait()
+        assert loader.info()[0] == 1
+        # and the next one is served
+        good = loader.submit(h_t, d2_t, h.size, events)
+        good.wait()
+        rig.pool.sync()
+        for l in range(SHAPE.layers):
+            assert [int(x) for x in dev_sums(rig, l, d2_t)] == host_sums(rig, h, l)
+    finally:
+        if loader is not None:
+            loader.close()
+        rig.close()
