@@ -285,3 +285,55 @@ int orc_host_offsets(const orc_geom* g, int b, int32_t layer, const int64_t* h, 
   }
   return ORC_OK;
 }
+
+/* Host-to-host shard copy (CacheStore H2H page, Dump path / Load path and
+ * "page_first_kv_split support"): one host page of a page-first pool is one store
+ * shard laid out like the shard layout (sub-buffer pages back to back, then zero
+ * pad).  Dump copies page src_pages[i] of the page-first pool `pf` into shard
+ * dst_shards[i] of the shard pool `sh`, row by row, and zeroes the shard's pad;
+ * load copies the rows back.  The two geometries must agree on everything but the
+ * layout and the page count. */
+static int same_rows(const orc_geom* pf, const orc_geom* sh) {
+  if (orc_check_geom(pf) != ORC_OK || orc_check_geom(sh) != ORC_OK) return 0;
+  if (pf->layout != ORC_PAGE_FIRST || sh->layout != ORC_KV_SPLIT_SHARD) return 0;
+  if (pf->layers != sh->layers || pf->page_size != sh->page_size || pf->nsub != sh->nsub) return 0;
+  for (int b = 0; b < pf->nsub; b++)
+    if (pf->gran[b] != sh->gran[b] || pf->bytes[b] != sh->bytes[b]) return 0;
+  return 1;
+}
+
+int orc_h2h_dump(const orc_geom* pf, const orc_geom* sh, const uint8_t* host, uint8_t* store,
+                 const int64_t* src_pages, const int64_t* dst_shards, int64_t n) {
+  if (!same_rows(pf, sh) || n < 0 || !host || !store) return ORC_ERR_INVALID;
+  int64_t payload = orc_page_payload_bytes(sh), stride = orc_shard_bytes(sh);
+  for (int64_t i = 0; i < n; i++) {
+    if (src_pages[i] < 0 || src_pages[i] >= pf->host_pages || dst_shards[i] < 0 || dst_shards[i] >= sh->host_pages)
+      return ORC_ERR_INVALID;
+    for (int b = 0; b < pf->nsub; b++) {
+      int32_t rows = pf->gran[b] == ORC_PAGE_BLOCKS ? 1 : pf->page_size;
+      for (int32_t l = 0; l < pf->layers; l++)
+        for (int32_t r = 0; r < rows; r++)
+          memcpy(store + orc_host_offset(sh, b, dst_shards[i], l, r), host + orc_host_offset(pf, b, src_pages[i], l, r),
+                 (size_t)pf->bytes[b]);
+    }
+    memset(store + dst_shards[i] * stride + payload, 0, (size_t)(stride - payload));
+  }
+  return ORC_OK;
+}
+
+int orc_h2h_load(const orc_geom* pf, const orc_geom* sh, uint8_t* host, const uint8_t* store,
+                 const int64_t* src_shards, const int64_t* dst_pages, int64_t n) {
+  if (!same_rows(pf, sh) || n < 0 || !host || !store) return ORC_ERR_INVALID;
+  for (int64_t i = 0; i < n; i++) {
+    if (dst_pages[i] < 0 || dst_pages[i] >= pf->host_pages || src_shards[i] < 0 || src_shards[i] >= sh->host_pages)
+      return ORC_ERR_INVALID;
+    for (int b = 0; b < pf->nsub; b++) {
+      int32_t rows = pf->gran[b] == ORC_PAGE_BLOCKS ? 1 : pf->page_size;
+      for (int32_t l = 0; l < pf->layers; l++)
+        for (int32_t r = 0; r < rows; r++)
+          memcpy(host + orc_host_offset(pf, b, dst_pages[i], l, r), store + orc_host_offset(sh, b, src_shards[i], l, r),
+                 (size_t)pf->bytes[b]);
+    }
+  }
+  return ORC_OK;
+}

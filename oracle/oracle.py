@@ -77,6 +77,8 @@ def load(path: str = _LIB) -> ctypes.CDLL:
         "orc_load_back_layer": (ctypes.c_int, [G, ctypes.c_int32, ctypes.POINTER(_PU8), _PU8, _P64, _P64, ctypes.c_int64]),
         "orc_round_trip_check": (ctypes.c_int64, [G, ctypes.POINTER(_PU8), _P64, _P64, ctypes.c_int64]),
         "orc_host_offsets": (ctypes.c_int, [G, ctypes.c_int, ctypes.c_int32, _P64, ctypes.c_int64, _P64]),
+        "orc_h2h_dump": (ctypes.c_int, [G, G, _PU8, _PU8, _P64, _P64, ctypes.c_int64]),
+        "orc_h2h_load": (ctypes.c_int, [G, G, _PU8, _PU8, _P64, _P64, ctypes.c_int64]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -234,3 +236,23 @@ def round_trip_check(g: Geometry, dev, a, c) -> int:
     if r < 0:
         raise ValueError("oracle round_trip_check rejected its arguments")
     return int(r)
+
+
+def h2h_dump(pf: Geometry, sh: Geometry, host: np.ndarray, store: np.ndarray, src_pages, dst_shards) -> None:
+    """Store shards dst_shards[i] <- host pages src_pages[i] (row by row), pads zeroed.  In place on ``store``."""
+    a, b = _i64(src_pages), _i64(dst_shards)
+    assert a.shape == b.shape and host.nbytes >= host_pool_bytes(pf) and store.nbytes >= host_pool_bytes(sh)
+    rc = lib().orc_h2h_dump(ctypes.byref(pf.c()), ctypes.byref(sh.c()), host.ctypes.data_as(_PU8),
+                            store.ctypes.data_as(_PU8), _pi64(a), _pi64(b), a.size)
+    if rc != 0:
+        raise ValueError("oracle h2h_dump rejected its arguments")
+
+
+def h2h_load(pf: Geometry, sh: Geometry, host: np.ndarray, store: np.ndarray, src_shards, dst_pages) -> None:
+    """Host pages dst_pages[i] <- store shards src_shards[i] (row by row).  In place on ``host``."""
+    a, b = _i64(src_shards), _i64(dst_pages)
+    assert a.shape == b.shape and host.nbytes >= host_pool_bytes(pf) and store.nbytes >= host_pool_bytes(sh)
+    rc = lib().orc_h2h_load(ctypes.byref(pf.c()), ctypes.byref(sh.c()), host.ctypes.data_as(_PU8),
+                            store.ctypes.data_as(_PU8), _pi64(a), _pi64(b), a.size)
+    if rc != 0:
+        raise ValueError("oracle h2h_load rejected its arguments")

@@ -401,10 +401,54 @@ def pin_golden_closed_forms():
         assert got == int(rhs), f"{name}: {lhs} = {got}, closed form {rhs}"
 
 
+def pin_h2h_shard_dump_and_load():
+    """Store shard = the host page's sub-buffer pages back to back (each taken in
+    storage order from the page-first pool), then zeros to the shard size; a load
+    puts the same bytes back; shards and pages not named keep their bytes."""
+    cases = [([(T, 32), (T, 16)], 3, 4, 256), ([(T, 48), (B, 32)], 2, 4, 128), ([(T, 16)], 1, 1, 64)]
+    for k, (subs, L, P, align) in enumerate(cases):
+        rng = np.random.default_rng(700 + k)
+        pf = O.Geometry(L, P, subs, 7, 64, O.PAGE_FIRST)
+        sh = O.Geometry(L, P, subs, 5, 64, O.KV_SPLIT_SHARD, align=align)
+        host = rng.integers(0, 256, O.host_pool_bytes(pf), dtype=np.uint8)
+        store0 = rng.integers(0, 256, O.host_pool_bytes(sh), dtype=np.uint8)
+        store = store0.copy()
+        src, dst = np.array([6, 0, 3]), np.array([4, 1, 2])
+        O.h2h_dump(pf, sh, host, store, src, dst)
+        pos, _ = positions(pf)
+        stride = O.host_pool_bytes(sh) // sh.host_pages
+        for p, q in zip(src, dst):
+            parts = []
+            for b in range(len(subs)):
+                keys = sorted((st, n) for key, (st, n) in pos.items() if key[0] in ("row", "blk")
+                              and key[1] == b and key[2] == p)
+                parts.append(b"".join(host[st:st + n].tobytes() for st, n in keys))
+            img = b"".join(parts)
+            want = img + bytes(stride - len(img))
+            assert store[q * stride:(q + 1) * stride].tobytes() == want, (k, p, q)
+        for q in set(range(sh.host_pages)) - set(dst.tolist()):
+            assert np.array_equal(store[q * stride:(q + 1) * stride], store0[q * stride:(q + 1) * stride]), (k, q)
+        back = rng.integers(0, 256, host.size, dtype=np.uint8)
+        before = back.copy()
+        O.h2h_load(pf, sh, back, store, dst, np.array([1, 5, 6]))
+        page = O.sub_page_bytes
+        for p_src, p_dst in zip(src, [1, 5, 6]):
+            for b in range(len(subs)):
+                a0 = O.host_offset(pf, b, int(p_src), 0, 0)
+                a1 = O.host_offset(pf, b, int(p_dst), 0, 0)
+                n = page(pf, b)
+                assert np.array_equal(back[a1:a1 + n], host[a0:a0 + n]), (k, p_src, p_dst, b)
+        for p_other in set(range(pf.host_pages)) - {1, 5, 6}:
+            for b in range(len(subs)):
+                a1 = O.host_offset(pf, b, p_other, 0, 0)
+                n = page(pf, b)
+                assert np.array_equal(back[a1:a1 + n], before[a1:a1 + n]), (k, p_other)
+
+
 PINS = [pin_sizes_match_structure, pin_offsets_match_structure, pin_write_back_brute_force,
         pin_write_back_mock_formula, pin_load_back_brute_force, pin_round_trip_restores,
         pin_untouched_and_byte_accounting, pin_round_trip_check_counts, pin_index_preconditions,
-        pin_golden_closed_forms]
+        pin_golden_closed_forms, pin_h2h_shard_dump_and_load]
 
 
 def run_all() -> list:

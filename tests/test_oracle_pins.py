@@ -27,6 +27,10 @@ MUTANTS = [
     ("token-major rows laid out layer-major",
      "inner = ((int64_t)r * g->layers + l) * g->bytes[b];",
      "inner = ((int64_t)l * g->page_size + r) * g->bytes[b];"),
+    ("store shard pad left as it was",
+     "memset(store + dst_shards[i] * stride + payload, 0, (size_t)(stride - payload));", ";"),
+    ("store load reads the destination page's shard",
+     "store + orc_host_offset(sh, b, src_shards[i], l, r),", "store + orc_host_offset(sh, b, dst_pages[i] % sh->host_pages, l, r),"),
     ("shard size not rounded up",
      "if (k * a < s) k = k + 1;", ";"),
     ("sub-buffer region ignores the page count",
