@@ -48,6 +48,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-staged-probe", action="store_true")
+    ap.add_argument("--h2h", action="store_true",
+                    help="instead: time host-to-host shard dump/load of the shard workload with 1..16 CPU workers")
     ap.add_argument("--max-pinned-gib", type=float, default=64.0,
                     help="cap on the pinned host pool; a larger pool keeps the burst and shrinks the page count")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
@@ -141,8 +143,52 @@ def cpu_baseline(shape, burst, d2, seconds: float):
                       f"host-RAM replicas of the device pool and the host pool"}
 
 
+def h2h_main(args):
+    """Host-to-host shard dump + load of 512 pages of the 48-layer K|V shard workload
+    (3 MiB + 3 MiB per shard) between two host buffers, for several worker counts."""
+    import numpy as np
+
+    from host_device_page_amd import binding as B
+    from host_device_page_amd import workloads as W
+    shape = W.SHAPES["mha_kv_split_shard_bf16"]
+    L, P = shape.layers, shape.page_size
+    n = 512
+    subs = [(g, e, [16] * L) for g, e in shape.subs]
+    d_pf, _k1 = B.make_desc(layers=L, page_size=P, subs=subs, device_slots=shape.device_slots, host_pages=n,
+                            layout=B.HC_LAYOUT_PAGE_FIRST)
+    d_sh, _k2 = B.make_desc(layers=L, page_size=P, subs=subs, device_slots=shape.device_slots, host_pages=n,
+                            layout=B.HC_LAYOUT_KV_SPLIT_SHARD, shard_align=shape.align)
+    host = np.ones(B.host_pool_bytes(d_pf), dtype=np.uint8)
+    store = np.ones(B.host_pool_bytes(d_sh), dtype=np.uint8)
+    stride = B.staging_page_bytes(d_sh)
+    sizes = [L * P * e for _, e in shape.subs]
+    order = np.random.default_rng(1).permutation(n)
+    pages = [[host.ctypes.data + B.host_offset(d_pf, b, int(p), 0, 0) for b in range(len(sizes))] for p in order]
+    shards = [store.ctypes.data + q * stride for q in range(n)]
+    payload = n * sum(sizes)
+    out = {"metric": "host-to-host shard copy GB/s", "unit": "GB/s", "shards": n, "shard_bytes": stride,
+           "payload_bytes": payload, "cpu_threads_available": len(os.sched_getaffinity(0)), "by_workers": {}}
+    for w in (1, 2, 4, 8, 16):
+        eng = B.H2H(workers=w, queue_depth=4096)
+        eng.wait(eng.submit(B.HC_H2H_DUMP, sizes, pages, shards, stride))  # warm
+        res = {}
+        for name, direction in (("dump", B.HC_H2H_DUMP), ("load", B.HC_H2H_LOAD)):
+            ts = []
+            for _ in range(3):
+                t0 = time.perf_counter()
+                eng.wait(eng.submit(direction, sizes, pages, shards, stride))
+                ts.append(time.perf_counter() - t0)
+            res[name] = round(payload / float(np.median(ts)) / 1e9, 2)
+        eng.close()
+        out["by_workers"][w] = res
+        log(f"[h2h] workers {w}: {res}")
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
+    if args.h2h:
+        return h2h_main(args)
     if args.gpus != 1:
         print(json.dumps({"error": "this path runs on one GPU; --gpus above 1 is not supported. The multi-GPU "
                                    "design (layer-owner sharding with a per-layer broadcast) is described, "

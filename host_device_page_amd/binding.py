@@ -29,6 +29,9 @@ HC_ERR_UNSUPPORTED = -2
 HC_ERR_HIP = -3
 HC_ERR_NOMEM = -4
 HC_ERR_DEVICE = -5
+HC_ERR_BUSY = -6
+HC_H2H_DUMP = 0
+HC_H2H_LOAD = 1
 HC_TOKEN_ROWS = 0
 HC_PAGE_BLOCKS = 1
 HC_LAYOUT_PAGE_FIRST = 0
@@ -104,6 +107,14 @@ _SIGS = {
     "hc_loader_drain": (ctypes.c_int, [_V]),
     "hc_loader_info": (ctypes.c_int, [_V, _I64P, ctypes.POINTER(ctypes.c_int32)]),
     "hc_loader_destroy": (ctypes.c_int, [_V]),
+    "hc_h2h_create": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int64, ctypes.POINTER(_V)]),
+    "hc_h2h_submit": (ctypes.c_int, [_V, ctypes.c_int32, ctypes.c_int32, _I64P, ctypes.POINTER(_V),
+                                     ctypes.POINTER(_V), ctypes.c_int64, ctypes.c_int64, ctypes.POINTER(_V)]),
+    "hc_h2h_wait": (ctypes.c_int, [_V]),
+    "hc_h2h_release": (ctypes.c_int, [_V]),
+    "hc_h2h_outstanding": (ctypes.c_int, [_V, _I64P, _I64P]),
+    "hc_h2h_destroy": (ctypes.c_int, [_V]),
+    "hc_cache_fingerprint": (ctypes.c_int, [_D, ctypes.c_char_p, ctypes.c_int32, ctypes.POINTER(ctypes.c_uint64)]),
     "hc_last_error": (ctypes.c_char_p, []),
     "hc_version": (ctypes.c_int, []),
 }
@@ -417,3 +428,50 @@ class Loader:
             self.close()
         except Exception:
             pass
+
+
+# ---------------------------------------------------------------- host-to-host shard copies
+class H2H:
+    """hc_h2h: CPU copy workers moving host pages to / from store shards."""
+
+    def __init__(self, workers: int = 4, queue_depth: int = 1024):
+        self.handle = _V()
+        check(lib.hc_h2h_create(workers, queue_depth, ctypes.byref(self.handle)), "hc_h2h_create")
+
+    def submit(self, direction: int, tensor_bytes, tensor_pages, shards, shard_bytes: int):
+        """tensor_pages: [n][tensors] addresses; shards: [n] addresses.  Returns a request handle."""
+        T = len(tensor_bytes)
+        n = len(shards)
+        sizes = (ctypes.c_int64 * T)(*tensor_bytes)
+        pages = (_V * max(1, n * T))(*[int(a) for row in tensor_pages for a in row])
+        sh = (_V * max(1, n))(*[int(a) for a in shards])
+        out = _V()
+        check(lib.hc_h2h_submit(self.handle, direction, T, sizes, pages, sh, shard_bytes, n, ctypes.byref(out)),
+              "hc_h2h_submit")
+        return out
+
+    def wait(self, req) -> None:
+        check(lib.hc_h2h_release(req), "hc_h2h_release")
+
+    def outstanding(self):
+        a, b = ctypes.c_int64(), ctypes.c_int64()
+        check(lib.hc_h2h_outstanding(self.handle, ctypes.byref(a), ctypes.byref(b)), "hc_h2h_outstanding")
+        return a.value, b.value
+
+    def close(self) -> None:
+        if self.handle.value:
+            check(lib.hc_h2h_destroy(self.handle), "hc_h2h_destroy")
+            self.handle = _V()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def cache_fingerprint(desc, model: str, tp_size: int) -> int:
+    out = ctypes.c_uint64()
+    check(lib.hc_cache_fingerprint(ctypes.byref(desc), model.encode(), tp_size, ctypes.byref(out)),
+          "hc_cache_fingerprint")
+    return out.value

@@ -76,7 +76,8 @@ typedef enum hc_status {
   HC_ERR_UNSUPPORTED = -2, /* well-formed but not handled: elem_bytes % 16, misalignment, mode */
   HC_ERR_HIP = -3,         /* a HIP runtime call failed (the message names it) */
   HC_ERR_NOMEM = -4,       /* the library could not allocate its own scratch */
-  HC_ERR_DEVICE = -5       /* device-side validation flagged an index list (HC_FLAG_VALIDATE) */
+  HC_ERR_DEVICE = -5,      /* device-side validation flagged an index list (HC_FLAG_VALIDATE) */
+  HC_ERR_BUSY = -6         /* host-to-host queue capacity exhausted; nothing was submitted */
 } hc_status;
 
 enum { HC_TOKEN_ROWS = 0, HC_PAGE_BLOCKS = 1 };
@@ -271,6 +272,51 @@ int hc_loader_info(hc_loader* loader, int64_t* failed_bursts, int32_t* worker_ru
 /* Drains, joins the worker, frees.  Every burst must be released before.  NULL is a no-op.
  * Destroy a pool's loaders before the pool. */
 int hc_loader_destroy(hc_loader* loader);
+
+/* ---------------------------------------------------------------- host-to-host shard copies
+ * The storage side of the shard layout (CacheStore H2H page, unified-cache-management
+ * PR 1292: Dump path, Load path, Queue backpressure, Failure handling,
+ * page_first_kv_split support).  One page is one store shard: the page of every
+ * tensor (sub-buffer) back to back, then zeros up to shard_bytes.  Each shard is one
+ * job for a pool of CPU copy workers: one worker copies a shard's tensors in order,
+ * different shards run concurrently.  Dump and load keep separate counts of
+ * outstanding shards (queued + running); a request reserves capacity for all its
+ * shards or is refused with HC_ERR_BUSY, never submitted in part.  A request with a
+ * null address or a tensor-size mismatch is refused whole with HC_ERR_INVALID.
+ * Every submitted job counts toward its request's completion. */
+typedef struct hc_h2h hc_h2h;
+typedef struct hc_h2h_request hc_h2h_request;
+enum { HC_H2H_DUMP = 0, HC_H2H_LOAD = 1 };
+#define HC_H2H_MAX_TENSORS 16
+
+/* workers >= 1: that many copy threads; workers == 0: no threads, jobs run in the
+ * thread that calls hc_h2h_wait (manual progress).  queue_depth: outstanding-shard
+ * capacity per direction (>= 1). */
+int hc_h2h_create(int32_t workers, int64_t queue_depth, hc_h2h** out);
+/* Queue n shard jobs.  tensor_pages[i * tensors + t]: host address of tensor t's page
+ * for shard i (tensor_bytes[t] contiguous bytes; in a page-first pool that is
+ * hc_host_offset(sub t, page, 0, 0) from host_base).  shards[i]: the shard in the
+ * store buffer, shard_bytes long, sum(tensor_bytes) <= shard_bytes.  Dump: shard <-
+ * tensor pages, rest of the shard zeroed.  Load: tensor pages <- shard.  The arrays
+ * are copied; the memory they point to must stay valid until hc_h2h_wait returns. */
+int hc_h2h_submit(hc_h2h* h2h, int32_t direction, int32_t tensors, const int64_t* tensor_bytes,
+                  void* const* tensor_pages, void* const* shards, int64_t shard_bytes, int64_t n,
+                  hc_h2h_request** out);
+/* Block until every job of the request has finished; returns the request's status. */
+int hc_h2h_wait(hc_h2h_request* request);
+/* Waits like hc_h2h_wait, then frees the request. */
+int hc_h2h_release(hc_h2h_request* request);
+int hc_h2h_outstanding(hc_h2h* h2h, int64_t* dump_shards, int64_t* load_shards);
+/* Runs the remaining jobs, joins the workers, frees.  Release requests first.  NULL is a no-op. */
+int hc_h2h_destroy(hc_h2h* h2h);
+
+/* Cache identity (CacheStore H2H page, page_first_kv_split support: model, host layout,
+ * page size, TP size and tensor sizes, so that incompatible layouts never share
+ * cached data): 64-bit FNV-1a over the text
+ *   "hicache-layout-v1;model=<model>;layout=<page_first|kv_split_shard|page_first_token_major>;
+ *    layers=<L>;page_size=<P>;tp=<tp_size>;tensors=<g>:<bytes>,...;align=<shard_align or 0>"
+ * (no spaces or line breaks; g is 'r' for token rows, 'b' for page blocks). */
+int hc_cache_fingerprint(const hc_pool_desc* desc, const char* model, int32_t tp_size, uint64_t* out);
 
 /* ---------------------------------------------------------------- measurement */
 
