@@ -54,23 +54,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-#define ORC_MAX_SUB 4
-
-enum { ORC_OK = 0, ORC_ERR_INVALID = -1 };
-enum { ORC_TOKEN_ROWS = 0, ORC_PAGE_BLOCKS = 1 };
-enum { ORC_PAGE_FIRST = 0, ORC_KV_SPLIT_SHARD = 1, ORC_PAGE_FIRST_TOKEN_MAJOR = 2 };
-
-typedef struct orc_geom {
-  int32_t layers;       /* L */
-  int32_t page_size;    /* P, tokens per page */
-  int32_t nsub;         /* number of sub-buffers (K, V, latent, indexer ...) */
-  int32_t layout;       /* ORC_PAGE_FIRST or ORC_KV_SPLIT_SHARD */
-  int64_t host_pages;   /* H */
-  int64_t device_slots; /* S, token slots per layer */
-  int64_t align;        /* shard alignment in bytes (shard layout only) */
-  int32_t gran[ORC_MAX_SUB];  /* ORC_TOKEN_ROWS or ORC_PAGE_BLOCKS */
-  int64_t bytes[ORC_MAX_SUB]; /* E_b: bytes per token row or per page block */
-} orc_geom;
+#include "hc_oracle.h"
 
 /* Bytes one sub-buffer holds for one page over all layers. */
 int64_t orc_sub_page_bytes(const orc_geom* g, int b) {

@@ -35,7 +35,7 @@ MAX_SUB = 4
 
 def build(src: str = _SRC, out: str = _LIB) -> str:
     """Compile the C oracle into a shared library with gcc (plain -O2)."""
-    cmd = ["gcc", "-O2", "-std=c99", "-shared", "-fPIC", "-o", out, src]
+    cmd = ["gcc", "-O2", "-std=c99", "-shared", "-fPIC", "-I", _HERE, "-o", out, src]
     subprocess.run(cmd, check=True)
     return out
 
