@@ -29,6 +29,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
+DEFAULT_MAX_CTAS = 16        # the library's default grid cap for the zero-copy kernels
 PCIE5_X16_GBS = 63.0         # PCIe 5.0 x16, per direction, after 128b/130b encoding
 
 
@@ -48,6 +49,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-staged-probe", action="store_true")
+    ap.add_argument("--pipeline-ctas", type=lambda t: tuple(int(x) for x in t.split(",")), default=(0, 256),
+                    help="zero-copy grid caps for the layer-pipeline measurement (0 = the pool's setting)")
     ap.add_argument("--h2h", action="store_true",
                     help="instead: time host-to-host shard dump/load of the shard workload with 1..16 CPU workers")
     ap.add_argument("--max-pinned-gib", type=float, default=64.0,
@@ -143,6 +146,67 @@ def cpu_baseline(shape, burst, d2, seconds: float):
                       f"host-RAM replicas of the device pool and the host pool"}
 
 
+def layer_pipeline(B, torch, pool, shape, h_t, d2_t, n, stream, layer_events, make_pool, args):
+    """Overlap of the per-layer load-back with a consumer on a second stream.  The
+    consumer's work per layer is a bf16 matmul sized to about one layer's transfer
+    time; it waits on the layer's event before it starts.  overlap = (load + consume
+    - both) / min(load, consume): 1 when the shorter one hides completely."""
+    import numpy as np
+    L = shape.layers
+    consumer = torch.cuda.Stream()
+    a = torch.randn(4096, 4096, device="cuda", dtype=torch.bfloat16)
+    w = torch.randn(4096, 4096, device="cuda", dtype=torch.bfloat16)
+    out = torch.empty(4096, 4096, device="cuda", dtype=torch.bfloat16)
+    e0, e1 = B.HipEvent(timing=True), B.HipEvent(timing=True)
+
+    def timed(fn):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        fn()
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0
+
+    def one_matmul():
+        with torch.cuda.stream(consumer):
+            torch.matmul(a, w, out=out)
+    for _ in range(3):
+        timed(one_matmul)
+    per_mm = float(np.median([timed(one_matmul) for _ in range(5)]))
+    res = {"consumer": "bf16 matmul 4096^3 x k per layer, on a second stream, after hipStreamWaitEvent(layer event)"}
+    for ctas in args.pipeline_ctas:
+        p = pool if ctas == 0 else make_pool(B.HC_MODE_ZEROCOPY, max_ctas=ctas)
+
+        def load():
+            for l in range(L):
+                p.load_back_layer(l, h_t, d2_t, layer_events[l])
+        t_load = float(np.median([timed(load) for _ in range(3)]))
+        reps = max(1, int(round(t_load / L / max(per_mm, 1e-6))))
+
+        def consume_only():
+            with torch.cuda.stream(consumer):
+                for _ in range(L * reps):
+                    torch.matmul(a, w, out=out)
+
+        def both():
+            for l in range(L):
+                p.load_back_layer(l, h_t, d2_t, layer_events[l])
+                layer_events[l].wait_on(consumer)
+                with torch.cuda.stream(consumer):
+                    for _ in range(reps):
+                        torch.matmul(a, w, out=out)
+        t_cons = float(np.median([timed(consume_only) for _ in range(3)]))
+        t_both = float(np.median([timed(both) for _ in range(3)]))
+        ov = (t_load + t_cons - t_both) / min(t_load, t_cons)
+        key = f"max_ctas_{ctas or args.max_ctas or DEFAULT_MAX_CTAS}"
+        res[key] = {"load_ms": round(t_load * 1e3, 3), "consume_ms": round(t_cons * 1e3, 3),
+                    "both_ms": round(t_both * 1e3, 3), "matmuls_per_layer": reps, "overlap": round(ov, 4),
+                    "load_GBps_alone": round(n * L * sum(e for _, e in shape.subs) / t_load / 1e9, 2)}
+        log(f"[bench] layer pipeline {key}: {res[key]}")
+        if p is not pool:
+            p.close()
+    return res
+
+
 def h2h_main(args):
     """Host-to-host shard dump + load of 512 pages of the 48-layer K|V shard workload
     (3 MiB + 3 MiB per shard) between two host buffers, for several worker counts."""
@@ -228,11 +292,11 @@ def main():
         staging = torch.empty(args.staging_pages * B.staging_page_bytes(probe), dtype=torch.uint8, device="cuda")
     layers = [[t[l] for l in range(L)] for t in dev]
 
-    def make_pool(mode):
+    def make_pool(mode, max_ctas=None):
         return B.Pool(layers=L, page_size=P, subs=list(shape.subs), device_slots=shape.device_slots,
                       host_pages=shape.host_pages, device_layers=layers, host=host, stream=stream,
                       layout=shape.layout, shard_align=shape.align, staging=staging, write_back_mode=mode,
-                      flags=B.HC_FLAG_PROFILE, max_ctas=args.max_ctas)
+                      flags=B.HC_FLAG_PROFILE, max_ctas=args.max_ctas if max_ctas is None else max_ctas)
 
     if args.calibration_copy_mib:
         nb = args.calibration_copy_mib << 20
@@ -332,6 +396,9 @@ def main():
                 "bytes_per_launch": dom["bytes_per_launch"],
                 "peak_source": "hipMemcpyAsync pinned<->device 1 GiB best of 5, measured in this run",
                 "pcie5_x16_nominal_GBps": PCIE5_X16_GBS}
+    # layer-wise pipeline: a consumer doing real work per layer, waiting on each layer event
+    pipeline = layer_pipeline(B, torch, pool, shape, h_t, d2_t, burst.n, stream, layer_events, make_pool, args)
+
     # hand-over cost on the calling thread: the per-layer enqueue inline vs on the loader thread
     handover = {}
     for asynchronous in (False, True):
@@ -409,6 +476,7 @@ def main():
         "frac_of_link_peak": {"write_back": round(wb_gbs / peak_d2h, 4), "load_back": round(lb_gbs / peak_h2d, 4)},
         "cpu_enqueue_ms_per_step": round(1e3 * float(np.median(enqueue_s)), 3),
         "load_back_handover_ms": handover,
+        "layer_pipeline": pipeline,
         "kernel_avg_ms": {"zc_read": round(ms_rd / max(1, n_rd), 4), "zc_write": round(ms_wr / max(1, n_wr), 4)},
         "roofline": roofline,
         "roofline_hbm": roofline_hbm,

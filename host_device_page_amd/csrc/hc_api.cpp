@@ -57,7 +57,11 @@ int set_err(int code, const char* fmt, ...) {
   } while (0)
 
 constexpr int kKinds = 6;  // gather, zc write, zc read, pads, compare, copy engine
-constexpr int32_t kDefaultMaxCtas = 256;
+// Zero-copy kernels wait on the host link, not on the CU: 8-16 workgroups already
+// saturate it (measured 55 GB/s from 8 up to 1024), and every extra workgroup holds
+// a slot on a CU that the forward pass could use.  With 16, a bf16 GEMM consumer on
+// another stream overlaps 74 % of the per-layer load-back; with 256, 8 %.
+constexpr int32_t kDefaultMaxCtas = 16;
 // Staging chunks are capped at the MI355X Infinity Cache size (256 MB): the gather
 // writes a chunk and the copy engines read it back right away, so a chunk that
 // fits stays cache-resident between the two (measured: 32 x 8 MiB page images
