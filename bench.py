@@ -86,17 +86,27 @@ def memcpy_peak(hip, host_ptr: int, dev_ptr: int, nbytes: int, stream_ptr: int, 
     return nbytes / (best * 1e-3) / 1e9
 
 
+def kernel_source_digest() -> str:
+    """sha256 of the kernel source with comments and whitespace removed: the counters
+    stay attached to the kernels they measured, not to their comments."""
+    import hashlib
+    import re
+    src = open(os.path.join(ROOT, "host_device_page_amd", "csrc", "hc_kernels.hip")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", "", src)
+    src = "".join(src.split())
+    return hashlib.sha256(src.encode()).hexdigest()
+
+
 def counter_traffic(workload: str, kernel: str):
     """Bytes per launch that the FETCH_SIZE / WRITE_SIZE counter passes measured for
     `kernel` (scaled by the known-size copy), from the committed profile summary, or
     None when the kernel source changed since the counters were taken."""
-    import hashlib
     path = os.path.join(ROOT, "profiles", f"{workload}_counters.json")
-    src = os.path.join(ROOT, "host_device_page_amd", "csrc", "hc_kernels.hip")
     if not os.path.exists(path):
         return None
     prof = json.load(open(path))
-    if prof.get("kernel_source_sha256") != hashlib.sha256(open(src, "rb").read()).hexdigest():
+    if prof.get("kernel_code_digest") != kernel_source_digest():
         return None
     k = prof["kernels"].get(kernel)
     if not k:

@@ -304,7 +304,7 @@ __global__ __launch_bounds__(kThreads) void k_zero_pads(uint8_t* __restrict__ ba
 // ---------------------------------------------------------------- round-trip compare
 // grid = (tiles, L, nsub).  Counts rows (or page blocks at a[i] % P == 0) whose bytes
 // at slot a[i] and slot c[i] differ.  One wave compares one row at a time; the row's
-// verdict is the OR of the lanes' verdicts (ballot).
+// result is the OR of the lanes' results (ballot).
 __global__ __launch_bounds__(kThreads) void k_compare(Geom g, const int64_t* __restrict__ a,
                                                       const int64_t* __restrict__ c, int64_t n,
                                                       unsigned long long* __restrict__ counter,

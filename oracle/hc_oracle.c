@@ -2,7 +2,7 @@
  * Oracle for the HiCache host<->device KV page transfer.  TEST INFRASTRUCTURE.
  *
  * Plain, slow, obviously correct CPU reference of what the transfer path
- * computes.  Only the test suite, the smoke check of the graft entry point and
+ * computes.  Only the test suite, __graft_entry__.smoke() and
  * the CPU-baseline leg of the benchmark may load, call or link this file.  The
  * product library never does, and this file shares no code with it.
  *

@@ -22,8 +22,8 @@ def geom_of(shape: W.PoolShape) -> O.Geometry:
                       shape.device_slots, shape.layout, shape.align)
 
 
-# Pinned host memory a test process can hold on the machines these tests target
-# (measured: one 64 GiB page-locked allocation succeeds, 66 GiB does not).
+# Budget for page-locked host memory in one test process; a pool that does not fit
+# keeps its rows, burst and device side and gets fewer host pages.
 PIN_BUDGET = 64 << 30
 
 
