@@ -106,6 +106,7 @@ struct hc_pool {
   int32_t lb_mode = HC_MODE_ZEROCOPY;
   int32_t flags = 0;
   int32_t max_ctas = kDefaultMaxCtas;
+  int32_t num_cus = 0;          // compute units of the pool's device
   uint8_t* host = nullptr;      // host pool (host address == device address on ROCm)
   uint8_t* staging = nullptr;
   int64_t staging_bytes = 0;
@@ -524,6 +525,8 @@ int hc_pool_create(const hc_pool_desc* desc, hc_pool** out) {
     return code;
   };
   if (hipGetDevice(&p->device) != hipSuccess) return bail(set_err(HC_ERR_HIP, "no HIP device"));
+  if (hipDeviceGetAttribute(&p->num_cus, hipDeviceAttributeMultiprocessorCount, p->device) != hipSuccess)
+    return bail(set_err(HC_ERR_HIP, "could not query the compute-unit count"));
   p->stream = (hipStream_t)desc->copy_stream;
   p->flags = desc->flags;
   p->max_ctas = desc->max_ctas > 0 ? desc->max_ctas : kDefaultMaxCtas;
@@ -682,7 +685,8 @@ int hc_write_back_all_layers(hc_pool* p, const int64_t* device_idx, const int64_
     for (const Chunk& c : p->chunks) {
       {
         Timer t(p, 0);
-        e = hc::launch_gather_stage(p->geom, device_idx, d_srow, c.t0, c.t1 - c.t0, p->staging, p->d_err, p->stream);
+        e = hc::launch_gather_stage(p->geom, device_idx, d_srow, c.t0, c.t1 - c.t0, p->staging, p->d_err,
+                                    p->num_cus, p->stream);
         t.done();
       }
       if (e != hipSuccess) return finish(set_err(HC_ERR_HIP, "gather launch failed: %s", hipGetErrorString(e)));

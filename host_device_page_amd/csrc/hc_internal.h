@@ -68,7 +68,7 @@ int pool_layers(const hc_pool* pool);
 // Kernel launchers (hc_kernels.hip).  All enqueue on `stream` and return the launch status.
 hipError_t launch_gather_stage(const Geom& g, const int64_t* dev_idx, const int32_t* srow,
                                int64_t t0, int64_t count, uint8_t* staging, int32_t* err,
-                               hipStream_t stream);
+                               int32_t num_cus, hipStream_t stream);
 hipError_t launch_zc_write(const Geom& g, const int64_t* dev_idx, const int64_t* host_idx,
                            const int32_t* tok_list, int64_t count, uint8_t* host, int32_t* err,
                            int32_t max_ctas, hipStream_t stream);

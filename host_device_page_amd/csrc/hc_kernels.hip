@@ -43,6 +43,14 @@ namespace {
 constexpr int kThreads = 256;  // 4 waves of 64
 constexpr int kTile = HC_TILE; // tokens per unit (<= kThreads): one per thread at intake
 static_assert(kTile <= kThreads && kTile % 64 == 0, "tile must be whole waves of one block");
+#ifndef HC_GATHER_TILE
+#define HC_GATHER_TILE 128
+#endif
+#ifndef HC_GATHER_BLOCKS_PER_CU
+#define HC_GATHER_BLOCKS_PER_CU 4
+#endif
+constexpr int kGatherTile = HC_GATHER_TILE;  // tokens per gather unit
+static_assert(kGatherTile <= kThreads && kGatherTile % 64 == 0, "gather tile must be whole waves");
 constexpr int kUnroll = HC_UNROLL;
 constexpr int kWaves = kThreads / 64;
 
@@ -131,52 +139,63 @@ __device__ __forceinline__ int64_t dev_off(const SubGeom& s, int64_t d, int P) {
 }
 
 // ---------------------------------------------------------------- staged write-back: gather
-// grid = (tiles over [t0, t0+count), L, nsub).  srow[i] = slot * P + row inside the
-// chunk's staging images, or -1 for tokens that do not go through staging.
+// Units of (sub-buffer, kGatherTile tokens of [t0, t0+count), layer), walked grid-stride
+// by a grid of a few workgroups per CU: small units keep every CU streaming until the
+// last unit, where one workgroup per (tile, layer, sub) left 2-3 rounds per CU and a
+// thin tail.  srow[i] = slot * P + row inside the chunk's staging images, or -1 for
+// tokens that do not go through staging.
 __global__ __launch_bounds__(kThreads) void k_gather_stage(Geom g, const int64_t* __restrict__ dev_idx,
                                                            const int32_t* __restrict__ srow, int64_t t0,
                                                            int64_t count, uint8_t* __restrict__ staging,
-                                                           int32_t* __restrict__ err) {
-  __shared__ uint64_t s_src[kTile];
-  __shared__ uint64_t s_dst[kTile];
+                                                           int32_t* __restrict__ err, int64_t units) {
+  __shared__ uint64_t s_src[kGatherTile];
+  __shared__ uint64_t s_dst[kGatherTile];
   __shared__ int s_wave[kWaves];
-  const int b = blockIdx.z;
-  const int l = blockIdx.y;
-  const SubGeom& s = g.sub[b];
-  const int64_t i = t0 + (int64_t)blockIdx.x * kTile + threadIdx.x;
-  bool keep = false;
-  uint64_t src = 0, dst = 0;
-  if (threadIdx.x < kTile && i < t0 + count) {
-    const int32_t sr = srow[i];
-    if (sr >= 0) {
-      const int32_t slot = sr / g.P;
-      const int32_t r = sr - slot * g.P;
-      if (s.gran == HC_TOKEN_ROWS || r == 0) {
-        const int64_t d = dev_idx[i];
-        if (d >= 0 && d < g.S) {
-          src = layer_base(s, l) + (uint64_t)dev_off(s, d, g.P);
-          dst = (uint64_t)staging + (uint64_t)((int64_t)slot * g.img_bytes + s.img_off +
-                                               (int64_t)l * s.layer_stride + (int64_t)r * s.row_stride);
-          keep = true;
-        } else {
-          atomicOr(err, 1);
+  // sub-buffer-major order: a workgroup's stride crosses sub-buffers of different row
+  // sizes instead of staying on one of them
+  const int64_t per_sub = units / g.nsub;
+  for (int64_t unit = blockIdx.x; unit < units; unit += gridDim.x) {
+    const int b = (int)(unit / per_sub);
+    const int64_t rem = unit - (int64_t)b * per_sub;
+    const int64_t tile = rem / g.L;
+    const int l = (int)(rem - tile * g.L);
+    const SubGeom& s = g.sub[b];
+    const int64_t i = t0 + tile * kGatherTile + threadIdx.x;
+    bool keep = false;
+    uint64_t src = 0, dst = 0;
+    if (threadIdx.x < kGatherTile && i < t0 + count) {
+      const int32_t sr = srow[i];
+      if (sr >= 0) {
+        const int32_t slot = sr / g.P;
+        const int32_t r = sr - slot * g.P;
+        if (s.gran == HC_TOKEN_ROWS || r == 0) {
+          const int64_t d = dev_idx[i];
+          if (d >= 0 && d < g.S) {
+            src = layer_base(s, l) + (uint64_t)dev_off(s, d, g.P);
+            dst = (uint64_t)staging + (uint64_t)((int64_t)slot * g.img_bytes + s.img_off +
+                                                 (int64_t)l * s.layer_stride + (int64_t)r * s.row_stride);
+            keep = true;
+          } else {
+            atomicOr(err, 1);
+          }
         }
       }
     }
+    int total;
+    const int slot = compact_slot(keep, s_wave, &total);
+    if (keep) {
+      s_src[slot] = src;
+      s_dst[slot] = dst;
+    }
+    __syncthreads();
+    copy_rows(s_src, s_dst, total, s.vecs, s.vec_magic);
+    __syncthreads();  // LDS is rewritten by the next unit
   }
-  int total;
-  const int slot = compact_slot(keep, s_wave, &total);
-  if (keep) {
-    s_src[slot] = src;
-    s_dst[slot] = dst;
-  }
-  __syncthreads();
-  copy_rows(s_src, s_dst, total, s.vecs, s.vec_magic);
 }
 
 // ---------------------------------------------------------------- zero-copy write-back
 // Device rows -> pinned host pool.  Tokens are [0, count) or tok_list[0, count).
-// Units (tile, layer, sub) are walked grid-stride so a capped grid suffices.
+// Units (sub, tile, layer) are walked grid-stride so a capped grid suffices.
 __global__ __launch_bounds__(kThreads) void k_zc_write(Geom g, const int64_t* __restrict__ dev_idx,
                                                        const int64_t* __restrict__ host_idx,
                                                        const int32_t* __restrict__ tok_list, int64_t count,
@@ -185,12 +204,12 @@ __global__ __launch_bounds__(kThreads) void k_zc_write(Geom g, const int64_t* __
   __shared__ uint64_t s_src[kTile];
   __shared__ uint64_t s_dst[kTile];
   __shared__ int s_wave[kWaves];
-  const int64_t per_tile = (int64_t)g.L * g.nsub;
+  const int64_t per_sub = units / g.nsub;  // sub-buffer-major, as in k_gather_stage
   for (int64_t unit = blockIdx.x; unit < units; unit += gridDim.x) {
-    const int64_t tile = unit / per_tile;
-    const int rem = (int)(unit - tile * per_tile);
-    const int l = rem / g.nsub;
-    const int b = rem - l * g.nsub;
+    const int b = (int)(unit / per_sub);
+    const int64_t rem = unit - (int64_t)b * per_sub;
+    const int64_t tile = rem / g.L;
+    const int l = (int)(rem - tile * g.L);
     const SubGeom& s = g.sub[b];
     const int64_t j = tile * kTile + threadIdx.x;
     bool keep = false;
@@ -225,7 +244,7 @@ __global__ __launch_bounds__(kThreads) void k_zc_write(Geom g, const int64_t* __
 
 // ---------------------------------------------------------------- zero-copy load-back (one layer)
 // Pinned host pool -> device rows of layer `layer`.  Indices are device-resident.
-// Units (tile, sub) grid-stride.  With g.validate, page-block sub-buffers also check
+// Units (sub, tile) grid-stride.  With g.validate, page-block sub-buffers also check
 // that each page's rows arrive as one run of P consecutive device slots starting on a
 // page boundary (neighbour compare through a lane shuffle, LDS at wave edges).
 __global__ __launch_bounds__(kThreads) void k_zc_read(Geom g, int32_t layer, const int64_t* __restrict__ host_idx,
@@ -235,9 +254,10 @@ __global__ __launch_bounds__(kThreads) void k_zc_read(Geom g, int32_t layer, con
   __shared__ uint64_t s_src[kTile];
   __shared__ uint64_t s_dst[kTile];
   __shared__ int s_wave[kWaves];
+  const int64_t per_sub = units / g.nsub;  // sub-buffer-major, as in k_gather_stage
   for (int64_t unit = blockIdx.x; unit < units; unit += gridDim.x) {
-    const int64_t tile = unit / g.nsub;
-    const int b = (int)(unit - tile * g.nsub);
+    const int b = (int)(unit / per_sub);
+    const int64_t tile = unit - (int64_t)b * per_sub;
     const SubGeom& s = g.sub[b];
     const int64_t i = tile * kTile + threadIdx.x;
     bool keep = false;
@@ -357,12 +377,12 @@ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 }  // namespace
 
 hipError_t launch_gather_stage(const Geom& g, const int64_t* dev_idx, const int32_t* srow, int64_t t0,
-                               int64_t count, uint8_t* staging, int32_t* err, hipStream_t stream) {
+                               int64_t count, uint8_t* staging, int32_t* err, int32_t num_cus, hipStream_t stream) {
   if (count <= 0) return hipSuccess;
-  const int64_t tiles = ceil_div(count, kTile);
-  if (tiles > 0x7fffffff) return hipErrorInvalidValue;
-  dim3 grid((unsigned)tiles, (unsigned)g.L, (unsigned)g.nsub);
-  k_gather_stage<<<grid, kThreads, 0, stream>>>(g, dev_idx, srow, t0, count, staging, err);
+  const int64_t units = ceil_div(count, kGatherTile) * g.L * g.nsub;
+  const int64_t cap = (int64_t)(num_cus > 0 ? num_cus : 256) * HC_GATHER_BLOCKS_PER_CU;
+  const int64_t grid = units < cap ? units : cap;
+  k_gather_stage<<<dim3((unsigned)grid), kThreads, 0, stream>>>(g, dev_idx, srow, t0, count, staging, err, units);
   return hipGetLastError();
 }
 
