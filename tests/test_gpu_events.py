@@ -188,3 +188,48 @@ def test_validate_flag_reports_misaligned_page_blocks():
         rig.pool.sync()
     finally:
         rig.close()
+
+
+@pytest.mark.gpu
+def test_negative_controls_corrupted_byte_and_skipped_layer():
+    """The round-trip check catches a flipped host byte and a layer that was never
+    loaded back, with exactly the oracle's count."""
+    say("[controls] corrupted byte, skipped layer")
+    rig = Rig(SHAPE, seed=13)
+    try:
+        h, d, d2 = prepare(rig, 11)
+        # a flipped byte in one row of layer 2, sub-buffer 1
+        off = int(O.host_offsets(rig.geom, 1, 2, h[5:6])[0]) + 17
+        rig.host.np[off] ^= 0x5A
+        skip = 4
+        for l in range(SHAPE.layers):
+            if l != skip:
+                rig.pool.load_back_layer(l, cuda_i64(h), cuda_i64(d2), None)
+        rig.pool.sync()
+        got = rig.pool.round_trip_check(cuda_i64(d), cuda_i64(d2))
+        dev = [[rig.dev[b][l].cpu().numpy() for l in range(SHAPE.layers)] for b in range(2)]
+        want = O.round_trip_check(rig.geom, dev, d, d2)
+        assert got == want
+        assert want == 1 + 2 * h.size, "expected one corrupted row plus the skipped layer's rows"
+    finally:
+        rig.close()
+
+
+@pytest.mark.gpu
+def test_staged_write_back_with_poisoned_staging():
+    """Staging filled with a poison byte before every burst: a copy that read staging
+    before the gather wrote it would leave poison in the host pool."""
+    from gpu_support import write_back_and_check
+    say("[controls] poisoned staging")
+    shape = W.PoolShape("poison_rows", 4, 16, ((T, 1024), (T, 512)), 16384, 128)
+    rig = Rig(shape, seed=14, write_back_mode=B.HC_MODE_STAGED, staging_pages=6)
+    try:
+        for k in range(3):
+            rig.staging.fill_(0xEE)
+            torch.cuda.synchronize()
+            pages = W.host_pages(20 + k, shape.host_pages, 40)
+            h = W.whole_page_tokens(pages, shape.page_size)
+            d = W.permutation_slots(30 + k, shape.device_slots, h.size)
+            write_back_and_check(rig, d, h)
+    finally:
+        rig.close()
