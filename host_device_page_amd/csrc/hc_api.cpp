@@ -176,14 +176,7 @@ struct Timer {
       if (a) (void)hipEventRecord(a, p->stream);
     }
   }
-  void done() {
-    if (!a) return;
-    hipEvent_t b = take_event(p);
-    if (!b) return;
-    (void)hipEventRecord(b, p->stream);
-    p->pending_timed.push_back({kind, a, b});
-    a = nullptr;
-  }
+  void done();
 };
 
 int harvest_timing(hc_pool* p) {
@@ -200,6 +193,20 @@ int harvest_timing(hc_pool* p) {
   }
   p->pending_timed.clear();
   return HC_OK;
+}
+
+// Timed launches are folded into the totals once this many are pending, so a pool
+// that profiles for a long time keeps a bounded number of events.
+constexpr size_t kMaxPendingTimed = 4096;
+
+void Timer::done() {
+  if (!a) return;
+  hipEvent_t b = take_event(p);
+  if (!b) return;
+  (void)hipEventRecord(b, p->stream);
+  p->pending_timed.push_back({kind, a, b});
+  a = nullptr;
+  if (p->pending_timed.size() >= kMaxPendingTimed) (void)harvest_timing(p);
 }
 
 uint64_t magic_for(uint32_t vecs) {
@@ -685,7 +692,7 @@ int hc_write_back_all_layers(hc_pool* p, const int64_t* device_idx, const int64_
     for (const Chunk& c : p->chunks) {
       {
         Timer t(p, 0);
-        e = hc::launch_gather_stage(p->geom, device_idx, d_srow, c.t0, c.t1 - c.t0, p->staging, p->d_err,
+        e = hc::launch_gather_stage(p->geom, device_idx, d_hidx, d_srow, c.t0, c.t1 - c.t0, p->staging, p->d_err,
                                     p->num_cus, p->stream);
         t.done();
       }

@@ -29,7 +29,7 @@ struct Geom {
   int32_t nsub;
   int32_t L;
   int32_t P;
-  int32_t validate;        // HC_FLAG_VALIDATE: page-block row contiguity checks
+  int32_t validate;        // HC_FLAG_VALIDATE: page-block rows checked to form whole device pages
   int64_t S;               // device token slots per layer
   int64_t host_tokens;     // H * P
   int64_t img_bytes;       // one staging page image (shard stride or summed sub pages)
@@ -66,9 +66,9 @@ void pool_loader_ops(hc_pool* pool, hc_loader_ops* ops);
 int pool_layers(const hc_pool* pool);
 
 // Kernel launchers (hc_kernels.hip).  All enqueue on `stream` and return the launch status.
-hipError_t launch_gather_stage(const Geom& g, const int64_t* dev_idx, const int32_t* srow,
-                               int64_t t0, int64_t count, uint8_t* staging, int32_t* err,
-                               int32_t num_cus, hipStream_t stream);
+hipError_t launch_gather_stage(const Geom& g, const int64_t* dev_idx, const int64_t* host_idx,
+                               const int32_t* srow, int64_t t0, int64_t count, uint8_t* staging,
+                               int32_t* err, int32_t num_cus, hipStream_t stream);
 hipError_t launch_zc_write(const Geom& g, const int64_t* dev_idx, const int64_t* host_idx,
                            const int32_t* tok_list, int64_t count, uint8_t* host, int32_t* err,
                            int32_t max_ctas, hipStream_t stream);

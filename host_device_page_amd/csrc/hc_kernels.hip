@@ -138,6 +138,16 @@ __device__ __forceinline__ int64_t dev_off(const SubGeom& s, int64_t d, int P) {
   return (s.gran == HC_TOKEN_ROWS ? d : d / P) * s.elem;
 }
 
+// HC_FLAG_VALIDATE for page-block sub-buffers: token i must either start a page on
+// both sides (h % P == 0 with d % P == 0) or continue the previous token's run on both
+// sides (d = d[i-1] + 1, h = h[i-1] + 1), so that every page moves as one whole device
+// page.  Violations set bit 2 of the error word.
+__device__ __forceinline__ void check_page_row(int64_t i, int64_t d, int64_t h, const int64_t* dev_idx,
+                                               const int64_t* host_idx, int P, int32_t* err) {
+  const bool ok = (h % P == 0) ? (d % P == 0) : (i > 0 && dev_idx[i - 1] + 1 == d && host_idx[i - 1] + 1 == h);
+  if (!ok) atomicOr(err, 2);
+}
+
 // ---------------------------------------------------------------- staged write-back: gather
 // Units of (sub-buffer, kGatherTile tokens of [t0, t0+count), layer), walked grid-stride
 // by a grid of a few workgroups per CU: small units keep every CU streaming until the
@@ -145,6 +155,7 @@ __device__ __forceinline__ int64_t dev_off(const SubGeom& s, int64_t d, int P) {
 // thin tail.  srow[i] = slot * P + row inside the chunk's staging images, or -1 for
 // tokens that do not go through staging.
 __global__ __launch_bounds__(kThreads) void k_gather_stage(Geom g, const int64_t* __restrict__ dev_idx,
+                                                           const int64_t* __restrict__ host_idx,
                                                            const int32_t* __restrict__ srow, int64_t t0,
                                                            int64_t count, uint8_t* __restrict__ staging,
                                                            int32_t* __restrict__ err, int64_t units) {
@@ -168,6 +179,7 @@ __global__ __launch_bounds__(kThreads) void k_gather_stage(Geom g, const int64_t
       if (sr >= 0) {
         const int32_t slot = sr / g.P;
         const int32_t r = sr - slot * g.P;
+        if (g.validate && s.gran == HC_PAGE_BLOCKS) check_page_row(i, dev_idx[i], host_idx[i], dev_idx, host_idx, g.P, err);
         if (s.gran == HC_TOKEN_ROWS || r == 0) {
           const int64_t d = dev_idx[i];
           if (d >= 0 && d < g.S) {
@@ -220,6 +232,7 @@ __global__ __launch_bounds__(kThreads) void k_zc_write(Geom g, const int64_t* __
       const int64_t h = host_idx[i];
       const int64_t p = h / g.P;
       const int r = (int)(h - p * g.P);
+      if (g.validate && s.gran == HC_PAGE_BLOCKS) check_page_row(i, d, h, dev_idx, host_idx, g.P, err);
       if (s.gran == HC_TOKEN_ROWS || r == 0) {
         if (d >= 0 && d < g.S && h >= 0 && h < g.host_tokens) {
           src = layer_base(s, l) + (uint64_t)dev_off(s, d, g.P);
@@ -376,13 +389,15 @@ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 }  // namespace
 
-hipError_t launch_gather_stage(const Geom& g, const int64_t* dev_idx, const int32_t* srow, int64_t t0,
-                               int64_t count, uint8_t* staging, int32_t* err, int32_t num_cus, hipStream_t stream) {
+hipError_t launch_gather_stage(const Geom& g, const int64_t* dev_idx, const int64_t* host_idx, const int32_t* srow,
+                               int64_t t0, int64_t count, uint8_t* staging, int32_t* err, int32_t num_cus,
+                               hipStream_t stream) {
   if (count <= 0) return hipSuccess;
   const int64_t units = ceil_div(count, kGatherTile) * g.L * g.nsub;
   const int64_t cap = (int64_t)(num_cus > 0 ? num_cus : 256) * HC_GATHER_BLOCKS_PER_CU;
   const int64_t grid = units < cap ? units : cap;
-  k_gather_stage<<<dim3((unsigned)grid), kThreads, 0, stream>>>(g, dev_idx, srow, t0, count, staging, err, units);
+  k_gather_stage<<<dim3((unsigned)grid), kThreads, 0, stream>>>(g, dev_idx, host_idx, srow, t0, count, staging, err,
+                                                                 units);
   return hipGetLastError();
 }
 

@@ -233,3 +233,25 @@ def test_staged_write_back_with_poisoned_staging():
             write_back_and_check(rig, d, h)
     finally:
         rig.close()
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("mode", [B.HC_MODE_ZEROCOPY, B.HC_MODE_STAGED])
+def test_validate_flag_reports_misaligned_page_blocks_on_write_back(mode):
+    say(f"[events] validate page blocks on write-back, mode {mode}")
+    rig = Rig(BLOCKS, seed=15, flags=B.HC_FLAG_VALIDATE, write_back_mode=mode, staging_pages=4)
+    try:
+        P = BLOCKS.page_size
+        pages = W.host_pages(3, BLOCKS.host_pages, 4)
+        h = W.whole_page_tokens(pages, P)
+        d = W.page_aligned_slots(4, BLOCKS.device_slots, P, 4)
+        rig.pool.write_back_all_layers(cuda_i64(d), h)
+        rig.pool.sync()  # aligned: no report
+        d_bad = d.copy()
+        d_bad[2 * P:3 * P] -= 1  # third page off its boundary
+        rig.pool.write_back_all_layers(cuda_i64(d_bad), h)
+        with pytest.raises(B.HcError) as e:
+            rig.pool.sync()
+        assert e.value.code == B.HC_ERR_DEVICE and "page-block" in str(e.value)
+    finally:
+        rig.close()
