@@ -445,10 +445,53 @@ def pin_h2h_shard_dump_and_load():
                 assert np.array_equal(back[a1:a1 + n], before[a1:a1 + n]), (k, p_other)
 
 
+def pin_burst_algebra():
+    """The copy has no hidden state: writing a burst back twice equals once; bursts on
+    disjoint host pages commute; a burst equals its split into consecutive parts (the
+    chunking a staged write-back does); load-back of disjoint device slots commutes."""
+    for seed, (name, g) in enumerate(GEOMS.items()):
+        rng = np.random.default_rng(800 + seed)
+        dev = random_device(g, rng)
+        host0 = rng.integers(0, 256, O.host_pool_bytes(g), dtype=np.uint8)
+        d, h = make_burst(g, rng, partial=not has_blocks(g))
+        once = host0.copy()
+        O.write_back(g, dev, once, d, h)
+        twice = once.copy()
+        O.write_back(g, dev, twice, d, h)
+        assert np.array_equal(once, twice), (name, "not idempotent")
+        P = g.page_size
+        pages = np.unique(h // P)
+        half = set(pages[: max(1, pages.size // 2)].tolist())
+        a = np.array([i for i in range(h.size) if h[i] // P in half])
+        b = np.array([i for i in range(h.size) if h[i] // P not in half], dtype=np.int64)
+        ab, ba = host0.copy(), host0.copy()
+        O.write_back(g, dev, ab, d[a], h[a])
+        O.write_back(g, dev, ab, d[b], h[b])
+        O.write_back(g, dev, ba, d[b], h[b])
+        O.write_back(g, dev, ba, d[a], h[a])
+        assert np.array_equal(ab, ba), (name, "disjoint bursts do not commute")
+        assert np.array_equal(ab, once), (name, "split burst differs from the whole burst")
+        if not has_blocks(g):
+            cut = h.size // 3
+            parts = host0.copy()
+            O.write_back(g, dev, parts, d[:cut], h[:cut])
+            O.write_back(g, dev, parts, d[cut:], h[cut:])
+            assert np.array_equal(parts, once), (name, "consecutive parts differ from the whole burst")
+        d2 = fresh_slots(g, rng, d, d.size)
+        x, y = copy_device(dev), copy_device(dev)
+        for layer in range(g.layers):
+            O.load_back_layer(g, layer, x, once, h[a], d2[a])
+            O.load_back_layer(g, layer, x, once, h[b], d2[b])
+        for layer in reversed(range(g.layers)):
+            O.load_back_layer(g, layer, y, once, h[b], d2[b])
+            O.load_back_layer(g, layer, y, once, h[a], d2[a])
+        assert_dev_equal(x, y, f"{name}: load-back order")
+
+
 PINS = [pin_sizes_match_structure, pin_offsets_match_structure, pin_write_back_brute_force,
         pin_write_back_mock_formula, pin_load_back_brute_force, pin_round_trip_restores,
         pin_untouched_and_byte_accounting, pin_round_trip_check_counts, pin_index_preconditions,
-        pin_golden_closed_forms, pin_h2h_shard_dump_and_load]
+        pin_golden_closed_forms, pin_h2h_shard_dump_and_load, pin_burst_algebra]
 
 
 def run_all() -> list:

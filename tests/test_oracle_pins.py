@@ -31,6 +31,12 @@ MUTANTS = [
      "memset(store + dst_shards[i] * stride + payload, 0, (size_t)(stride - payload));", ";"),
     ("store load reads the destination page's shard",
      "store + orc_host_offset(sh, b, src_shards[i], l, r),", "store + orc_host_offset(sh, b, dst_pages[i] % sh->host_pages, l, r),"),
+    ("write-back carries state between calls (pad written only on the first call)",
+     "  if (g->layout == ORC_KV_SPLIT_SHARD) {\n    int64_t payload = orc_page_payload_bytes(g);",
+     "  static int calls = 0;\n  if (g->layout == ORC_KV_SPLIT_SHARD && calls++ == 0) {\n    int64_t payload = orc_page_payload_bytes(g);"),
+    ("write-back drops the last token of a burst",
+     "  for (int64_t i = 0; i < n; i++) {\n    int64_t page = h[i] / P;\n    int32_t row = (int32_t)(h[i] % P);\n    for (int b = 0; b < g->nsub; b++) {\n      if (g->gran[b] == ORC_PAGE_BLOCKS && row != 0) continue;\n      for (int l = 0; l < L; l++) {",
+     "  for (int64_t i = 0; i + 1 < n; i++) {\n    int64_t page = h[i] / P;\n    int32_t row = (int32_t)(h[i] % P);\n    for (int b = 0; b < g->nsub; b++) {\n      if (g->gran[b] == ORC_PAGE_BLOCKS && row != 0) continue;\n      for (int l = 0; l < L; l++) {"),
     ("shard size not rounded up",
      "if (k * a < s) k = k + 1;", ";"),
     ("sub-buffer region ignores the page count",
