@@ -284,7 +284,9 @@ int hc_loader_destroy(hc_loader* loader);
  * outstanding shards (queued + running); a request reserves capacity for all its
  * shards or is refused with HC_ERR_BUSY, never submitted in part.  A request with a
  * null address or a tensor-size mismatch is refused whole with HC_ERR_INVALID.
- * Every submitted job counts toward its request's completion. */
+ * Every submitted job counts toward its request's completion.  The workers form an
+ * unordered executor, not a FIFO stream: jobs (and requests) may finish in any
+ * order, and a caller that needs ordering waits on the earlier request first. */
 typedef struct hc_h2h hc_h2h;
 typedef struct hc_h2h_request hc_h2h_request;
 enum { HC_H2H_DUMP = 0, HC_H2H_LOAD = 1 };

@@ -75,3 +75,48 @@ def test_loader_with_consumer_stream(asynchronous):
         if loader is not None:
             loader.close()
         rig.close()
+
+
+@pytest.mark.gpu
+def test_loader_and_caller_share_a_pool():
+    """A loader thread enqueues one burst's load-back while the calling thread writes
+    another burst back on the same pool; both end bit-exact (the pool serializes its
+    entry points)."""
+    say("[loader] shared pool")
+    rig = Rig(SHAPE, seed=16)
+    loader = None
+    try:
+        P = SHAPE.page_size
+        pages_a = W.host_pages(5, SHAPE.host_pages, 40)
+        h_a = W.whole_page_tokens(pages_a, P)
+        d_a = W.permutation_slots(6, SHAPE.device_slots, h_a.size)
+        rig.pool.write_back_all_layers(cuda_i64(d_a), h_a)
+        rig.pool.sync()
+        free_pages = np.setdiff1d(np.arange(SHAPE.host_pages), pages_a)
+        pages_b = np.random.default_rng(7).choice(free_pages, 40, replace=False)
+        h_b = W.whole_page_tokens(pages_b, P)
+        d_b = W.permutation_slots(8, SHAPE.device_slots, h_b.size, exclude=d_a)
+        d_a2 = W.permutation_slots(9, SHAPE.device_slots, h_a.size, exclude=np.concatenate([d_a, d_b]))
+        dev0 = [[rig.dev[b][l].cpu().numpy() for l in range(SHAPE.layers)] for b in range(2)]
+        host0 = rig.host.np.copy()
+        loader = B.Loader(rig.pool, SHAPE.layers, asynchronous=True)
+        events = [B.HipEvent() for _ in range(SHAPE.layers)]
+        bursts = []
+        for _ in range(4):  # several bursts so the worker runs while the caller writes back
+            bursts.append(loader.submit(cuda_i64(h_a), cuda_i64(d_a2), h_a.size, events))
+            rig.pool.write_back_all_layers(cuda_i64(d_b), h_b)
+        for bu in bursts:
+            bu.wait()
+        rig.pool.sync()
+        want_host = host0.copy()
+        O.write_back(rig.geom, dev0, want_host, d_b, h_b)
+        assert np.array_equal(rig.host.np, want_host), "write-back under a busy loader differs"
+        for l in range(SHAPE.layers):
+            O.load_back_layer(rig.geom, l, dev0, host0, h_a, d_a2)
+        for b in range(2):
+            for l in range(SHAPE.layers):
+                assert np.array_equal(rig.dev[b][l].cpu().numpy(), dev0[b][l]), (b, l)
+    finally:
+        if loader is not None:
+            loader.close()
+        rig.close()
