@@ -41,6 +41,16 @@ namespace {
 #endif
 
 constexpr int kThreads = 256;  // 4 waves of 64
+// The load-back kernel reads over the host link: software-pipelined batches of 4
+// (measured faster there; the HBM-bound kernels keep plain batches of kUnroll).
+#ifndef HC_READ_PIPELINED
+#define HC_READ_PIPELINED 1
+#endif
+#ifndef HC_READ_UNROLL
+#define HC_READ_UNROLL 4
+#endif
+constexpr bool kReadPipelined = HC_READ_PIPELINED != 0;
+constexpr int kReadUnroll = HC_READ_UNROLL;
 constexpr int kTile = HC_TILE; // tokens per unit (<= kThreads): one per thread at intake
 static_assert(kTile <= kThreads && kTile % 64 == 0, "tile must be whole waves of one block");
 #ifndef HC_GATHER_TILE
@@ -102,14 +112,17 @@ __device__ __forceinline__ int compact_slot(bool keep, int* s_wave, int* total) 
 }
 
 // Copies `rows` rows of `vecs` 16-byte vectors: row q from s_src[q] to s_dst[q].
+// Each lane takes batches of U vectors, `kThreads` apart.  PIPELINED issues the loads
+// of batch k+1 before the stores of batch k, so a lane keeps 2U loads in flight while
+// its stores drain: the host-link read kernel gains from it, the HBM kernels lose
+// occupancy to the extra registers and do not.
+template <bool PIPELINED, int U>
 __device__ __forceinline__ void copy_rows(const uint64_t* s_src, const uint64_t* s_dst, int rows,
                                           uint32_t vecs, uint64_t magic) {
   const uint32_t total = (uint32_t)rows * vecs;
-  for (uint32_t u0 = threadIdx.x; u0 < total; u0 += kThreads * kUnroll) {
-    v4u v[kUnroll];
-    uint64_t dst[kUnroll];
+  auto load_batch = [&](uint32_t u0, v4u* v, uint64_t* dst) {
 #pragma unroll
-    for (int k = 0; k < kUnroll; k++) {
+    for (int k = 0; k < U; k++) {
       const uint32_t u = u0 + k * kThreads;
       if (u < total) {
         const uint32_t q = div_vecs(u, magic);
@@ -118,11 +131,39 @@ __device__ __forceinline__ void copy_rows(const uint64_t* s_src, const uint64_t*
         dst[k] = s_dst[q] + off;
       }
     }
+  };
+  auto store_batch = [&](uint32_t u0, const v4u* v, const uint64_t* dst) {
 #pragma unroll
-    for (int k = 0; k < kUnroll; k++) {
+    for (int k = 0; k < U; k++) {
       const uint32_t u = u0 + k * kThreads;
       if (u < total) st16(dst[k], v[k]);
     }
+  };
+  constexpr uint32_t step = kThreads * U;
+  if (!PIPELINED) {
+    for (uint32_t u0 = threadIdx.x; u0 < total; u0 += step) {
+      v4u v[U];
+      uint64_t dst[U];
+      load_batch(u0, v, dst);
+      store_batch(u0, v, dst);
+    }
+    return;
+  }
+  v4u va[U], vb[U];
+  uint64_t da[U], db[U];
+  uint32_t u0 = threadIdx.x;
+  if (u0 >= total) return;
+  load_batch(u0, va, da);
+  for (;;) {
+    const uint32_t u1 = u0 + step;
+    if (u1 < total) load_batch(u1, vb, db);
+    store_batch(u0, va, da);
+    if (u1 >= total) break;
+    const uint32_t u2 = u1 + step;
+    if (u2 < total) load_batch(u2, va, da);
+    store_batch(u1, vb, db);
+    if (u2 >= total) break;
+    u0 = u2;
   }
 }
 
@@ -200,7 +241,7 @@ __global__ __launch_bounds__(kThreads) void k_gather_stage(Geom g, const int64_t
       s_dst[slot] = dst;
     }
     __syncthreads();
-    copy_rows(s_src, s_dst, total, s.vecs, s.vec_magic);
+    copy_rows<false, kUnroll>(s_src, s_dst, total, s.vecs, s.vec_magic);
     __syncthreads();  // LDS is rewritten by the next unit
   }
 }
@@ -250,7 +291,7 @@ __global__ __launch_bounds__(kThreads) void k_zc_write(Geom g, const int64_t* __
       s_dst[slot] = dst;
     }
     __syncthreads();
-    copy_rows(s_src, s_dst, total, s.vecs, s.vec_magic);
+    copy_rows<false, kUnroll>(s_src, s_dst, total, s.vecs, s.vec_magic);
     __syncthreads();  // LDS is rewritten by the next unit
   }
 }
@@ -315,7 +356,7 @@ __global__ __launch_bounds__(kThreads) void k_zc_read(Geom g, int32_t layer, con
       s_dst[slot] = dst;
     }
     __syncthreads();
-    copy_rows(s_src, s_dst, total, s.vecs, s.vec_magic);
+    copy_rows<kReadPipelined, kReadUnroll>(s_src, s_dst, total, s.vecs, s.vec_magic);
     __syncthreads();
   }
 }
