@@ -47,6 +47,8 @@ def parse():
     ap.add_argument("--staging-pages", type=int, default=32)
     ap.add_argument("--max-ctas", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle sample")
+    ap.add_argument("--cpu-threads", type=int, default=0,
+                    help="threads of the second CPU oracle sample (0 = the usable cores, at most 16; 1 = skip it)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-staged-probe", action="store_true")
     ap.add_argument("--pipeline-ctas", type=lambda t: tuple(int(x) for x in t.split(",")), default=(0, 256),
@@ -126,10 +128,38 @@ def burst_bytes(shape, burst) -> tuple[int, int]:
     return L * (n * rows + whole_pages * blocks), 0
 
 
-def cpu_baseline(shape, burst, d2, seconds: float):
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _page_cuts(h, page_size: int, parts: int):
+    """Cut positions of the index list into about `parts` slices, each cut at a
+    change of host page, so no host page (nor its shard pad) is shared."""
+    import numpy as np
+    pg = h // page_size
+    starts = np.flatnonzero(np.r_[True, pg[1:] != pg[:-1]])
+    cuts = sorted({int(starts[np.searchsorted(starts, k * h.size // parts)]) if k * h.size // parts <= starts[-1]
+                   else h.size for k in range(1, parts)})
+    return [0] + [c for c in cuts if 0 < c < h.size] + [h.size]
+
+
+def cpu_baseline(shape, burst, d2, seconds: float, threads: int = 1):
     """The oracle, as written, on host-memory replicas: write-back then load-back of
     the full burst restricted to layer 0 of the pool (1 of L layers), repeated
-    until `seconds` pass.  Single thread."""
+    until `seconds` pass.  With threads > 1 the burst is cut at host-page changes
+    into one slice per thread; every thread calls the same oracle functions on its
+    slice (disjoint rows, pages and slots, so together they do the whole burst),
+    like a pool of CPU copy workers.  The rate counts the bytes of every finished
+    slice pass over the time until the last thread stops."""
+    import threading
+
     import numpy as np
 
     from oracle import oracle as O
@@ -137,23 +167,41 @@ def cpu_baseline(shape, burst, d2, seconds: float):
                     shape.layout, shape.align)
     dev = [[np.ones(g1.device_units(b) * e, dtype=np.uint8)] for b, (_, e) in enumerate(shape.subs)]
     host = np.ones(O.host_pool_bytes(g1), dtype=np.uint8)
-    bytes_per_pass = 0
-    for g, e in shape.subs:
-        bytes_per_pass += burst.n * e if g == 0 else int((burst.host_idx % shape.page_size == 0).sum()) * e
-    done = 0
+
+    def pass_bytes(h):  # write-back + load-back bytes of one pass over these tokens
+        return 2 * sum(h.size * e if g == 0 else int((h % shape.page_size == 0).sum()) * e for g, e in shape.subs)
+
+    cuts = _page_cuts(burst.host_idx, shape.page_size, threads)
+    slices = [(burst.device_idx[a:b], burst.host_idx[a:b], d2[a:b]) for a, b in zip(cuts[:-1], cuts[1:])]
+    done = [0] * len(slices)
     t0 = time.perf_counter()
-    while True:
-        O.write_back(g1, dev, host, burst.device_idx, burst.host_idx)
-        O.load_back_layer(g1, 0, dev, host, burst.host_idx, d2)
-        done += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    gbs = 2 * bytes_per_pass * done / el / 1e9
-    return {"value": round(gbs, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+    deadline = t0 + seconds
+
+    def work(k):
+        d, h, f = slices[k]
+        while True:
+            O.write_back(g1, dev, host, d, h)
+            O.load_back_layer(g1, 0, dev, host, h, f)
+            done[k] += 1
+            if time.perf_counter() >= deadline:
+                return
+
+    if len(slices) == 1:
+        work(0)
+    else:
+        ts = [threading.Thread(target=work, args=(k,)) for k in range(len(slices))]
+        for t in ts:
+            t.start()
+        for t in ts:
+            t.join()
+    el = time.perf_counter() - t0
+    moved = sum(done[k] * pass_bytes(slices[k][1]) for k in range(len(slices)))
+    how = "single thread" if len(slices) == 1 else f"{len(slices)} threads on disjoint page-aligned slices"
+    return {"value": round(moved / el / 1e9, 3), "unit": "GB/s", "cores": len(slices), "kind": "oracle",
+            "cpu_model": _cpu_model(),
             "sample": f"C oracle write-back + load-back of the full {burst.n}-token burst on layer 0 only "
-                      f"(1 of {shape.layers} layers, same rows/pages/index lists), {done} passes in {el:.1f} s, "
-                      f"host-RAM replicas of the device pool and the host pool"}
+                      f"(1 of {shape.layers} layers, same rows/pages/index lists), {sum(done)} slice passes in "
+                      f"{el:.1f} s, {how}, host-RAM replicas of the device pool and the host pool"}
 
 
 def layer_pipeline(B, torch, pool, shape, h_t, d2_t, n, stream, layer_events, make_pool, args):
@@ -462,11 +510,15 @@ def main():
         spool.close()
         log(f"[bench] staged write-back {staged}, gather {g_gbs:.1f} GB/s")
 
-    cpu = None
+    cpu = cpu_mt = None
     if not args.no_cpu_baseline:
         log("[bench] CPU oracle sample ...")
         cpu = cpu_baseline(shape, burst, d2, args.cpu_seconds)
         log(f"[bench] CPU oracle {cpu['value']} GB/s")
+        t = args.cpu_threads or min(16, len(os.sched_getaffinity(0)))
+        if t > 1:
+            cpu_mt = cpu_baseline(shape, burst, d2, args.cpu_seconds / 2, threads=t)
+            log(f"[bench] CPU oracle, {cpu_mt['cores']} threads: {cpu_mt['value']} GB/s")
 
     pages = burst.pages.size
     out = {
@@ -492,6 +544,7 @@ def main():
         "roofline_hbm": roofline_hbm,
         "staged_write_back": staged,
         "cpu_baseline": cpu,
+        "cpu_baseline_threads": cpu_mt,
     }
     host.free()
     print(json.dumps(out), flush=True)
