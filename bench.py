@@ -53,6 +53,9 @@ def parse():
     ap.add_argument("--no-staged-probe", action="store_true")
     ap.add_argument("--pipeline-ctas", type=lambda t: tuple(int(x) for x in t.split(",")), default=(0, 256),
                     help="zero-copy grid caps for the layer-pipeline measurement (0 = the pool's setting)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead: write-back and per-layer load-back time against burst size (prefixes of "
+                         "the workload's burst, 1 page up to all of it)")
     ap.add_argument("--h2h", action="store_true",
                     help="instead: time host-to-host shard dump/load of the shard workload with 1..16 CPU workers")
     ap.add_argument("--max-pinned-gib", type=float, default=64.0,
@@ -307,6 +310,63 @@ def h2h_main(args):
     print(json.dumps(out), flush=True)
 
 
+def burst_size_sweep(B, np, pool, shape, stream, burst, d_t, h_np, h_t, d2_t, args):
+    """Latency and rate against burst size: the first k pages' tokens of the
+    workload's burst, k = 1, 2, 4, ... up to the whole burst.  Write-back: one call
+    bracketed by HIP events on the copy stream, plus its CPU enqueue time.
+    Load-back: one layer alone, and all layers back to back (per-layer average)."""
+    P, L = shape.page_size, shape.layers
+    pg = burst.host_idx // P
+    starts = np.flatnonzero(np.r_[True, pg[1:] != pg[:-1]])
+    ends = np.r_[starts[1:], burst.n]
+    ks = []
+    k = 1
+    while k < starts.size:
+        ks.append(k)
+        k *= 2
+    ks.append(int(starts.size))
+    e0, e1 = B.HipEvent(timing=True), B.HipEvent(timing=True)
+    layer_events = [B.HipEvent() for _ in range(L)]
+    rows = []
+    for k in ks:
+        n = int(ends[k - 1])
+        sub = type(burst)(burst.device_idx[:n], burst.host_idx[:n], burst.pages[:k])
+        link, _ = burst_bytes(shape, sub)
+        d, h, hd, d2 = d_t[:n], h_np[:n], h_t[:n], d2_t[:n]
+        wb, cpu, one, chain = [], [], [], []
+        for rep in range(7):
+            e0.record(stream)
+            t0 = time.perf_counter()
+            pool.write_back_all_layers(d, h)
+            cpu.append(time.perf_counter() - t0)
+            e1.record(stream)
+            e1.synchronize()
+            wb.append(e0.elapsed_ms(e1))
+            e0.record(stream)
+            pool.load_back_layer(0, hd, d2, layer_events[0])
+            e1.record(stream)
+            e1.synchronize()
+            one.append(e0.elapsed_ms(e1))
+            e0.record(stream)
+            for l in range(L):
+                pool.load_back_layer(l, hd, d2, layer_events[l])
+            e1.record(stream)
+            e1.synchronize()
+            chain.append(e0.elapsed_ms(e1))
+        # the first two repetitions warm up
+        wb_ms, cpu_ms = float(np.median(wb[2:])), 1e3 * float(np.median(cpu[2:]))
+        one_ms, chain_ms = float(np.median(one[2:])), float(np.median(chain[2:])) / L
+        rows.append({"pages": k, "tokens": n, "bytes_each_way": link,
+                     "write_back_ms": round(wb_ms, 4), "write_back_GBps": round(link / (wb_ms * 1e6), 2),
+                     "write_back_cpu_ms": round(cpu_ms, 4),
+                     "load_back_one_layer_ms": round(one_ms, 4),
+                     "load_back_ms_per_layer_chained": round(chain_ms, 4),
+                     "load_back_GBps_chained": round(link / L / (chain_ms * 1e6), 2)})
+        log(f"[sweep] {rows[-1]}")
+    pool.sync()
+    return rows
+
+
 def main():
     args = parse()
     if args.h2h:
@@ -375,6 +435,13 @@ def main():
     torch.cuda.synchronize()
     log(f"[bench] setup {time.perf_counter() - t_setup:.1f} s; burst {burst.n} tokens, {burst.pages.size} pages; "
         f"write-back mode {pool.mode(0)} (1 staged, 2 zero-copy), load-back mode {pool.mode(1)}")
+    if args.sweep:
+        rows = burst_size_sweep(B, np, pool, shape, stream, burst, d_t, h_np, h_t, d2_t, args)
+        print(json.dumps({"sweep": "burst size", "workload": shape.name, "write_back_mode": pool.mode(0),
+                          "max_ctas": args.max_ctas or DEFAULT_MAX_CTAS, "rows": rows}), flush=True)
+        pool.close()
+        host.free()
+        return
 
     link_bytes, _ = burst_bytes(shape, burst)
     ev_wb0, ev_wb1, ev_lb1 = B.HipEvent(timing=True), B.HipEvent(timing=True), B.HipEvent(timing=True)

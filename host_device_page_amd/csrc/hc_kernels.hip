@@ -17,6 +17,12 @@
 // consecutive 16-byte vectors of a row, and a run of slots that are adjacent
 // on both sides is one contiguous stream of addresses.  Loads are issued
 // kUnroll deep before the stores to keep enough bytes in flight.
+//
+// The zero-copy kernels shrink the tile to kTile >> tile_shift tokens when a
+// burst is too small to give every workgroup of the grid a unit: a small burst
+// then still spreads over enough workgroups to keep the host link busy (one
+// workgroup alone reads only ~7 GB/s over it), and each unit still moves whole
+// rows, so a run of adjacent rows stays one contiguous stream on the link.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -249,14 +255,16 @@ __global__ __launch_bounds__(kThreads) void k_gather_stage(Geom g, const int64_t
 // ---------------------------------------------------------------- zero-copy write-back
 // Device rows -> pinned host pool.  Tokens are [0, count) or tok_list[0, count).
 // Units (sub, tile, layer) are walked grid-stride so a capped grid suffices.
+// Tiles hold kTile >> tile_shift tokens.
 __global__ __launch_bounds__(kThreads) void k_zc_write(Geom g, const int64_t* __restrict__ dev_idx,
                                                        const int64_t* __restrict__ host_idx,
                                                        const int32_t* __restrict__ tok_list, int64_t count,
                                                        uint8_t* __restrict__ host, int32_t* __restrict__ err,
-                                                       int64_t units) {
+                                                       int64_t units, int tile_shift) {
   __shared__ uint64_t s_src[kTile];
   __shared__ uint64_t s_dst[kTile];
   __shared__ int s_wave[kWaves];
+  const int tile_n = kTile >> tile_shift;
   const int64_t per_sub = units / g.nsub;  // sub-buffer-major, as in k_gather_stage
   for (int64_t unit = blockIdx.x; unit < units; unit += gridDim.x) {
     const int b = (int)(unit / per_sub);
@@ -264,10 +272,10 @@ __global__ __launch_bounds__(kThreads) void k_zc_write(Geom g, const int64_t* __
     const int64_t tile = rem / g.L;
     const int l = (int)(rem - tile * g.L);
     const SubGeom& s = g.sub[b];
-    const int64_t j = tile * kTile + threadIdx.x;
+    const int64_t j = tile * tile_n + threadIdx.x;
     bool keep = false;
     uint64_t src = 0, dst = 0;
-    if (threadIdx.x < kTile && j < count) {
+    if ((int)threadIdx.x < tile_n && j < count) {
       const int64_t i = tok_list ? (int64_t)tok_list[j] : j;
       const int64_t d = dev_idx[i];
       const int64_t h = host_idx[i];
@@ -301,23 +309,25 @@ __global__ __launch_bounds__(kThreads) void k_zc_write(Geom g, const int64_t* __
 // Units (sub, tile) grid-stride.  With g.validate, page-block sub-buffers also check
 // that each page's rows arrive as one run of P consecutive device slots starting on a
 // page boundary (neighbour compare through a lane shuffle, LDS at wave edges).
+// Tiles hold kTile >> tile_shift tokens, as in k_zc_write.
 __global__ __launch_bounds__(kThreads) void k_zc_read(Geom g, int32_t layer, const int64_t* __restrict__ host_idx,
                                                       const int64_t* __restrict__ dev_idx, int64_t n,
                                                       const uint8_t* __restrict__ host, int32_t* __restrict__ err,
-                                                      int64_t units) {
+                                                      int64_t units, int tile_shift) {
   __shared__ uint64_t s_src[kTile];
   __shared__ uint64_t s_dst[kTile];
   __shared__ int s_wave[kWaves];
+  const int tile_n = kTile >> tile_shift;
   const int64_t per_sub = units / g.nsub;  // sub-buffer-major, as in k_gather_stage
   for (int64_t unit = blockIdx.x; unit < units; unit += gridDim.x) {
     const int b = (int)(unit / per_sub);
     const int64_t tile = unit - (int64_t)b * per_sub;
     const SubGeom& s = g.sub[b];
-    const int64_t i = tile * kTile + threadIdx.x;
+    const int64_t i = tile * tile_n + threadIdx.x;
     bool keep = false;
     uint64_t src = 0, dst = 0;
     int64_t d = 0, h = 0;
-    const bool live = threadIdx.x < kTile && i < n;
+    const bool live = (int)threadIdx.x < tile_n && i < n;
     if (live) {
       d = dev_idx[i];
       h = host_idx[i];
@@ -442,21 +452,37 @@ hipError_t launch_gather_stage(const Geom& g, const int64_t* dev_idx, const int6
   return hipGetLastError();
 }
 
+// Tile shift for a zero-copy launch over `count` tokens with `per_tile` units per
+// tile: the smallest shift (at most kMaxTileShift, i.e. 4-token tiles) whose
+// kTile >> shift token tiles give at least `max_ctas` units.
+constexpr int kMaxTileShift = 6;
+
+static int tile_shift_for(int64_t count, int64_t per_tile, int32_t max_ctas) {
+  int shift = 0;
+  while (shift < kMaxTileShift && ceil_div(count, kTile >> shift) * per_tile < (int64_t)max_ctas) shift++;
+  return shift;
+}
+
 hipError_t launch_zc_write(const Geom& g, const int64_t* dev_idx, const int64_t* host_idx, const int32_t* tok_list,
                            int64_t count, uint8_t* host, int32_t* err, int32_t max_ctas, hipStream_t stream) {
   if (count <= 0) return hipSuccess;
-  const int64_t units = ceil_div(count, kTile) * g.L * g.nsub;
+  const int64_t per_tile = (int64_t)g.L * g.nsub;
+  const int shift = tile_shift_for(count, per_tile, max_ctas);
+  const int64_t units = ceil_div(count, kTile >> shift) * per_tile;
   const int64_t grid = units < max_ctas ? units : max_ctas;
-  k_zc_write<<<dim3((unsigned)grid), kThreads, 0, stream>>>(g, dev_idx, host_idx, tok_list, count, host, err, units);
+  k_zc_write<<<dim3((unsigned)grid), kThreads, 0, stream>>>(g, dev_idx, host_idx, tok_list, count, host, err, units,
+                                                             shift);
   return hipGetLastError();
 }
 
 hipError_t launch_zc_read(const Geom& g, int32_t layer, const int64_t* host_idx, const int64_t* dev_idx, int64_t n,
                           const uint8_t* host, int32_t* err, int32_t max_ctas, hipStream_t stream) {
   if (n <= 0) return hipSuccess;
-  const int64_t units = ceil_div(n, kTile) * g.nsub;
+  const int64_t per_tile = g.nsub;
+  const int shift = tile_shift_for(n, per_tile, max_ctas);
+  const int64_t units = ceil_div(n, kTile >> shift) * per_tile;
   const int64_t grid = units < max_ctas ? units : max_ctas;
-  k_zc_read<<<dim3((unsigned)grid), kThreads, 0, stream>>>(g, layer, host_idx, dev_idx, n, host, err, units);
+  k_zc_read<<<dim3((unsigned)grid), kThreads, 0, stream>>>(g, layer, host_idx, dev_idx, n, host, err, units, shift);
   return hipGetLastError();
 }
 

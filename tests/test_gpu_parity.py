@@ -165,3 +165,31 @@ def test_validate_flag_accepts_whole_pages():
         load_back_and_check(rig, h, fresh(shape, d, 3))
     finally:
         rig.close()
+
+
+# Small bursts on grids of 1 to 256 workgroups: the zero-copy kernels shrink their token
+# tile (down to 4 tokens) until the burst gives every workgroup a unit.  Token rows of
+# several sizes, page blocks that only the tile holding a page's row 0 moves, shards.
+SPLIT_SHAPES = [
+    S("split_rows_kv", 3, 16, [(T, 2048)] * 2, 8192, 64),
+    S("split_latent_indexer", 2, 16, [(T, 1152), (BLK, 8448)], 4096, 32),
+    S("split_odd_rows", 2, 8, [(T, 48), (T, 2048)], 4096, 64),
+    S("split_shard", 2, 8, [(T, 1024), (T, 128)], 4096, 64, SH),
+]
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("max_ctas", [1, 16, 64, 256])
+@pytest.mark.parametrize("pages", [1, 3, 20])
+@pytest.mark.parametrize("shape", SPLIT_SHAPES, ids=lambda s: s.name)
+def test_small_bursts_shrink_tiles(shape, pages, max_ctas):
+    """Bursts too small to fill the grid run on shrunk tiles; results stay bit-exact."""
+    say(f"[small] {shape.name} pages={pages} max_ctas={max_ctas}")
+    kind = "aligned" if has_blocks(shape) else ("requests" if shape.layout == SH else "perm")
+    d, h = burst(shape, pages, kind, pages)
+    rig = Rig(shape, seed=pages, max_ctas=max_ctas)
+    try:
+        write_back_and_check(rig, d, h)
+        load_back_and_check(rig, h, fresh(shape, d, pages + 7))
+    finally:
+        rig.close()
