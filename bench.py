@@ -410,11 +410,11 @@ def main():
         staging = torch.empty(args.staging_pages * B.staging_page_bytes(probe), dtype=torch.uint8, device="cuda")
     layers = [[t[l] for l in range(L)] for t in dev]
 
-    def make_pool(mode, max_ctas=None):
+    def make_pool(mode, max_ctas=None, flags=B.HC_FLAG_PROFILE):
         return B.Pool(layers=L, page_size=P, subs=list(shape.subs), device_slots=shape.device_slots,
                       host_pages=shape.host_pages, device_layers=layers, host=host, stream=stream,
                       layout=shape.layout, shard_align=shape.align, staging=staging, write_back_mode=mode,
-                      flags=B.HC_FLAG_PROFILE, max_ctas=args.max_ctas if max_ctas is None else max_ctas)
+                      flags=flags, max_ctas=args.max_ctas if max_ctas is None else max_ctas)
 
     if args.calibration_copy_mib:
         nb = args.calibration_copy_mib << 20
@@ -436,6 +436,9 @@ def main():
     log(f"[bench] setup {time.perf_counter() - t_setup:.1f} s; burst {burst.n} tokens, {burst.pages.size} pages; "
         f"write-back mode {pool.mode(0)} (1 staged, 2 zero-copy), load-back mode {pool.mode(1)}")
     if args.sweep:
+        # no per-launch timing events here: at small bursts their cost (~9 us per launch) would dominate
+        pool.close()
+        pool = make_pool(wb_mode, flags=0)
         rows = burst_size_sweep(B, np, pool, shape, stream, burst, d_t, h_np, h_t, d2_t, args)
         print(json.dumps({"sweep": "burst size", "workload": shape.name, "write_back_mode": pool.mode(0),
                           "max_ctas": args.max_ctas or DEFAULT_MAX_CTAS, "rows": rows}), flush=True)

@@ -179,10 +179,16 @@ class HipEvent:
         _hip_check(_hip.hipEventElapsedTime(ctypes.byref(ms), self.handle, end.handle), "hipEventElapsedTime")
         return float(ms.value)
 
-    def __del__(self):
+    def destroy(self) -> None:
         if getattr(self, "handle", None) and self.handle.value:
             _hip.hipEventDestroy(self.handle)
             self.handle = _V()
+
+    def __del__(self):
+        try:
+            self.destroy()
+        except Exception:  # interpreter shutdown: the HIP module may already be gone
+            pass
 
 
 # ---------------------------------------------------------------- pinned host memory
