@@ -527,10 +527,12 @@ def main():
     # layer-wise pipeline: a consumer doing real work per layer, waiting on each layer event
     pipeline = layer_pipeline(B, torch, pool, shape, h_t, d2_t, burst.n, stream, layer_events, make_pool, args)
 
-    # hand-over cost on the calling thread: the per-layer enqueue inline vs on the loader thread
+    # hand-over cost on the calling thread: the per-layer enqueue inline vs on the loader thread,
+    # on a pool without per-launch timing (a launch that stamps timing events costs more CPU time)
     handover = {}
+    hpool = make_pool(wb_mode, flags=0)
     for asynchronous in (False, True):
-        ld = B.Loader(pool, L, asynchronous=asynchronous)
+        ld = B.Loader(hpool, L, asynchronous=asynchronous)
         times = []
         for _ in range(5):
             t_s = time.perf_counter()
@@ -540,6 +542,7 @@ def main():
             bu.release()
         ld.close()
         handover["loader_thread" if asynchronous else "inline"] = round(1e3 * float(np.median(times)), 4)
+    hpool.close()
     log(f"[bench] load-back hand-over per burst (ms): {handover}")
     pool.close()
 

@@ -165,18 +165,31 @@ hipEvent_t take_event(hc_pool* p) {
   return e;
 }
 
-// Brackets one launch with events when the pool profiles.
+// Times one launch (or, for copy-engine work, one span of the stream) when the pool
+// profiles.  Kernels get the events through hc::LaunchTimer and stamp them with their
+// own start and end; copy-engine spans record them on the stream around the copies.
 struct Timer {
   hc_pool* p;
   int kind;
-  hipEvent_t a = nullptr;
+  hc::LaunchTimer ev;
   Timer(hc_pool* pool, int k) : p(pool), kind(k) {
     if (p->flags & HC_FLAG_PROFILE) {
-      a = take_event(p);
-      if (a) (void)hipEventRecord(a, p->stream);
+      ev.start = take_event(p);
+      ev.stop = ev.start ? take_event(p) : nullptr;
+      if (!ev.stop) {
+        if (ev.start) p->free_events.push_back(ev.start);
+        ev.start = nullptr;
+      }
     }
   }
-  void done();
+  void record_start() {
+    if (ev.start) (void)hipEventRecord(ev.start, p->stream);
+  }
+  void record_stop() {
+    if (ev.stop) (void)hipEventRecord(ev.stop, p->stream);
+  }
+  // launched: the work the events bracket was enqueued (else the events go back unused)
+  void done(bool launched);
 };
 
 int harvest_timing(hc_pool* p) {
@@ -187,6 +200,8 @@ int harvest_timing(hc_pool* p) {
     if (hipEventElapsedTime(&ms, t.a, t.b) == hipSuccess) {
       p->kind_launches[t.kind] += 1;
       p->kind_ms[t.kind] += ms;
+    } else {
+      (void)hipGetLastError();  // an unusable pair is skipped, not left as the thread's last error
     }
     p->free_events.push_back(t.a);
     p->free_events.push_back(t.b);
@@ -199,13 +214,15 @@ int harvest_timing(hc_pool* p) {
 // that profiles for a long time keeps a bounded number of events.
 constexpr size_t kMaxPendingTimed = 4096;
 
-void Timer::done() {
-  if (!a) return;
-  hipEvent_t b = take_event(p);
-  if (!b) return;
-  (void)hipEventRecord(b, p->stream);
-  p->pending_timed.push_back({kind, a, b});
-  a = nullptr;
+void Timer::done(bool launched) {
+  if (!ev.start) return;
+  if (launched) {
+    p->pending_timed.push_back({kind, ev.start, ev.stop});
+  } else {
+    p->free_events.push_back(ev.start);
+    p->free_events.push_back(ev.stop);
+  }
+  ev = hc::LaunchTimer{};
   if (p->pending_timed.size() >= kMaxPendingTimed) (void)harvest_timing(p);
 }
 
@@ -691,38 +708,46 @@ int hc_write_back_all_layers(hc_pool* p, const int64_t* device_idx, const int64_
   if (staged) {
     for (const Chunk& c : p->chunks) {
       {
+        // Recorded events, not launch-stamped ones: right after a launch-stamped kernel the
+        // runtime ran the region copies below as blit kernels on the CUs instead of on the
+        // copy engines (measured), which would take away the staged mode's point.
         Timer t(p, 0);
+        t.record_start();
         e = hc::launch_gather_stage(p->geom, device_idx, d_hidx, d_srow, c.t0, c.t1 - c.t0, p->staging, p->d_err,
-                                    p->num_cus, p->stream);
-        t.done();
+                                    p->num_cus, hc::LaunchTimer{}, p->stream);
+        t.record_stop();
+        t.done(e == hipSuccess);
       }
       if (e != hipSuccess) return finish(set_err(HC_ERR_HIP, "gather launch failed: %s", hipGetErrorString(e)));
       if (c.r1 > c.r0) {
         Timer t(p, 5);
+        t.record_start();
         for (size_t r = c.r0; r < c.r1 && e == hipSuccess; r++) {
           const Region& g = p->regions[r];
           e = hipMemcpyAsync(g.dst, g.src, (size_t)g.len, hipMemcpyDeviceToHost, p->stream);
         }
-        t.done();
+        t.record_stop();
+        t.done(true);
         if (e != hipSuccess) return finish(set_err(HC_ERR_HIP, "hipMemcpyAsync failed: %s", hipGetErrorString(e)));
       }
     }
     if (nz > 0) {
       Timer t(p, 1);
-      e = hc::launch_zc_write(p->geom, device_idx, d_hidx, d_ztok, nz, p->host, p->d_err, p->max_ctas, p->stream);
-      t.done();
+      e = hc::launch_zc_write(p->geom, device_idx, d_hidx, d_ztok, nz, p->host, p->d_err, p->max_ctas, t.ev,
+                              p->stream);
+      t.done(e == hipSuccess);
       if (e != hipSuccess) return finish(set_err(HC_ERR_HIP, "zero-copy launch failed: %s", hipGetErrorString(e)));
     }
   } else {
     Timer t(p, 1);
-    e = hc::launch_zc_write(p->geom, device_idx, d_hidx, nullptr, n, p->host, p->d_err, p->max_ctas, p->stream);
-    t.done();
+    e = hc::launch_zc_write(p->geom, device_idx, d_hidx, nullptr, n, p->host, p->d_err, p->max_ctas, t.ev, p->stream);
+    t.done(e == hipSuccess);
     if (e != hipSuccess) return finish(set_err(HC_ERR_HIP, "zero-copy launch failed: %s", hipGetErrorString(e)));
   }
   if (npads > 0) {
     Timer t(p, 3);
-    e = hc::launch_zero_pads(p->host, d_pads, npads, L.stride, L.payload, L.stride - L.payload, p->stream);
-    t.done();
+    e = hc::launch_zero_pads(p->host, d_pads, npads, L.stride, L.payload, L.stride - L.payload, t.ev, p->stream);
+    t.done(e == hipSuccess);
     if (e != hipSuccess) return finish(set_err(HC_ERR_HIP, "pad launch failed: %s", hipGetErrorString(e)));
   }
   return finish(HC_OK);
@@ -752,8 +777,8 @@ int hc_load_back_layer(hc_pool* p, int32_t layer, const int64_t* host_idx, const
   hipError_t e;
   {
     Timer t(p, 2);
-    e = hc::launch_zc_read(p->geom, layer, host_idx, device_idx, n, p->host, p->d_err, p->max_ctas, p->stream);
-    t.done();
+    e = hc::launch_zc_read(p->geom, layer, host_idx, device_idx, n, p->host, p->d_err, p->max_ctas, t.ev, p->stream);
+    t.done(e == hipSuccess);
   }
   if (e != hipSuccess) return finish(set_err(HC_ERR_HIP, "load-back launch failed: %s", hipGetErrorString(e)));
   return finish(HC_OK);
@@ -770,8 +795,8 @@ int hc_round_trip_check(hc_pool* p, const int64_t* idx_a, const int64_t* idx_b, 
   HIP_TRY(hipMemsetAsync(p->d_counter, 0, sizeof(unsigned long long), p->stream));
   if (n > 0) {
     Timer t(p, 4);
-    hipError_t e = hc::launch_compare(p->geom, idx_a, idx_b, n, p->d_counter, p->d_err, p->stream);
-    t.done();
+    hipError_t e = hc::launch_compare(p->geom, idx_a, idx_b, n, p->d_counter, p->d_err, t.ev, p->stream);
+    t.done(e == hipSuccess);
     if (e != hipSuccess) return set_err(HC_ERR_HIP, "compare launch failed: %s", hipGetErrorString(e));
   }
   HIP_TRY(hipMemcpyAsync(p->h_counter, p->d_counter, sizeof(unsigned long long), hipMemcpyDeviceToHost, p->stream));

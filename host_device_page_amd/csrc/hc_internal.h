@@ -65,19 +65,28 @@ int set_error(int code, const char* fmt, ...);
 void pool_loader_ops(hc_pool* pool, hc_loader_ops* ops);
 int pool_layers(const hc_pool* pool);
 
+// Optional timing of one kernel launch: two timing events that the launch itself
+// stamps with the kernel's start and end (hipExtLaunchKernel), so timing adds no
+// marker packets to the stream.  Both null: untimed.
+struct LaunchTimer {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+
 // Kernel launchers (hc_kernels.hip).  All enqueue on `stream` and return the launch status.
 hipError_t launch_gather_stage(const Geom& g, const int64_t* dev_idx, const int64_t* host_idx,
                                const int32_t* srow, int64_t t0, int64_t count, uint8_t* staging,
-                               int32_t* err, int32_t num_cus, hipStream_t stream);
+                               int32_t* err, int32_t num_cus, const LaunchTimer& t, hipStream_t stream);
 hipError_t launch_zc_write(const Geom& g, const int64_t* dev_idx, const int64_t* host_idx,
                            const int32_t* tok_list, int64_t count, uint8_t* host, int32_t* err,
-                           int32_t max_ctas, hipStream_t stream);
+                           int32_t max_ctas, const LaunchTimer& t, hipStream_t stream);
 hipError_t launch_zc_read(const Geom& g, int32_t layer, const int64_t* host_idx, const int64_t* dev_idx,
                           int64_t n, const uint8_t* host, int32_t* err, int32_t max_ctas,
-                          hipStream_t stream);
+                          const LaunchTimer& t, hipStream_t stream);
 hipError_t launch_zero_pads(uint8_t* base, const int64_t* pages, int64_t npages, int64_t stride,
-                            int64_t off, int64_t bytes, hipStream_t stream);
+                            int64_t off, int64_t bytes, const LaunchTimer& t, hipStream_t stream);
 hipError_t launch_compare(const Geom& g, const int64_t* a, const int64_t* c, int64_t n,
-                          unsigned long long* counter, int32_t* err, hipStream_t stream);
+                          unsigned long long* counter, int32_t* err, const LaunchTimer& t,
+                          hipStream_t stream);
 
 }  // namespace hc

@@ -23,6 +23,7 @@
 // then still spreads over enough workgroups to keep the host link busy (one
 // workgroup alone reads only ~7 GB/s over it), and each unit still moves whole
 // rows, so a run of adjacent rows stays one contiguous stream on the link.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -438,18 +439,28 @@ __global__ __launch_bounds__(kThreads) void k_compare(Geom g, const int64_t* __r
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// One launch of kThreads-wide workgroups; timed through the launch itself when t holds events.
+template <typename... KArgs, typename... Args>
+hipError_t launch(void (*kernel)(KArgs...), dim3 grid, const LaunchTimer& t, hipStream_t stream, Args... args) {
+  (void)hipGetLastError();  // the status read below must be this launch's own
+  if (t.start)
+    hipExtLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, stream, t.start, t.stop, 0, args...);
+  else
+    kernel<<<grid, kThreads, 0, stream>>>(args...);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_gather_stage(const Geom& g, const int64_t* dev_idx, const int64_t* host_idx, const int32_t* srow,
                                int64_t t0, int64_t count, uint8_t* staging, int32_t* err, int32_t num_cus,
-                               hipStream_t stream) {
+                               const LaunchTimer& t, hipStream_t stream) {
   if (count <= 0) return hipSuccess;
   const int64_t units = ceil_div(count, kGatherTile) * g.L * g.nsub;
   const int64_t cap = (int64_t)(num_cus > 0 ? num_cus : 256) * HC_GATHER_BLOCKS_PER_CU;
   const int64_t grid = units < cap ? units : cap;
-  k_gather_stage<<<dim3((unsigned)grid), kThreads, 0, stream>>>(g, dev_idx, host_idx, srow, t0, count, staging, err,
-                                                                 units);
-  return hipGetLastError();
+  return launch(k_gather_stage, dim3((unsigned)grid), t, stream, g, dev_idx, host_idx, srow, t0, count, staging, err,
+                units);
 }
 
 // Tile shift for a zero-copy launch over `count` tokens with `per_tile` units per
@@ -464,47 +475,45 @@ static int tile_shift_for(int64_t count, int64_t per_tile, int32_t max_ctas) {
 }
 
 hipError_t launch_zc_write(const Geom& g, const int64_t* dev_idx, const int64_t* host_idx, const int32_t* tok_list,
-                           int64_t count, uint8_t* host, int32_t* err, int32_t max_ctas, hipStream_t stream) {
+                           int64_t count, uint8_t* host, int32_t* err, int32_t max_ctas, const LaunchTimer& t,
+                           hipStream_t stream) {
   if (count <= 0) return hipSuccess;
   const int64_t per_tile = (int64_t)g.L * g.nsub;
   const int shift = tile_shift_for(count, per_tile, max_ctas);
   const int64_t units = ceil_div(count, kTile >> shift) * per_tile;
   const int64_t grid = units < max_ctas ? units : max_ctas;
-  k_zc_write<<<dim3((unsigned)grid), kThreads, 0, stream>>>(g, dev_idx, host_idx, tok_list, count, host, err, units,
-                                                             shift);
-  return hipGetLastError();
+  return launch(k_zc_write, dim3((unsigned)grid), t, stream, g, dev_idx, host_idx, tok_list, count, host, err, units,
+                shift);
 }
 
 hipError_t launch_zc_read(const Geom& g, int32_t layer, const int64_t* host_idx, const int64_t* dev_idx, int64_t n,
-                          const uint8_t* host, int32_t* err, int32_t max_ctas, hipStream_t stream) {
+                          const uint8_t* host, int32_t* err, int32_t max_ctas, const LaunchTimer& t,
+                          hipStream_t stream) {
   if (n <= 0) return hipSuccess;
   const int64_t per_tile = g.nsub;
   const int shift = tile_shift_for(n, per_tile, max_ctas);
   const int64_t units = ceil_div(n, kTile >> shift) * per_tile;
   const int64_t grid = units < max_ctas ? units : max_ctas;
-  k_zc_read<<<dim3((unsigned)grid), kThreads, 0, stream>>>(g, layer, host_idx, dev_idx, n, host, err, units, shift);
-  return hipGetLastError();
+  return launch(k_zc_read, dim3((unsigned)grid), t, stream, g, layer, host_idx, dev_idx, n, host, err, units, shift);
 }
 
 hipError_t launch_zero_pads(uint8_t* base, const int64_t* pages, int64_t npages, int64_t stride, int64_t off,
-                            int64_t bytes, hipStream_t stream) {
+                            int64_t bytes, const LaunchTimer& t, hipStream_t stream) {
   if (npages <= 0 || bytes <= 0) return hipSuccess;
   const uint32_t vecs = (uint32_t)(bytes / 16);
   const int64_t total = npages * (int64_t)vecs;
   int64_t grid = ceil_div(total, kThreads);
   if (grid > 4096) grid = 4096;
-  k_zero_pads<<<dim3((unsigned)grid), kThreads, 0, stream>>>(base, pages, npages, stride, off, vecs);
-  return hipGetLastError();
+  return launch(k_zero_pads, dim3((unsigned)grid), t, stream, base, pages, npages, stride, off, vecs);
 }
 
 hipError_t launch_compare(const Geom& g, const int64_t* a, const int64_t* c, int64_t n, unsigned long long* counter,
-                          int32_t* err, hipStream_t stream) {
+                          int32_t* err, const LaunchTimer& t, hipStream_t stream) {
   if (n <= 0) return hipSuccess;
   const int64_t tiles = ceil_div(n, kTile);
   if (tiles > 0x7fffffff) return hipErrorInvalidValue;
-  dim3 grid((unsigned)tiles, (unsigned)g.L, (unsigned)g.nsub);
-  k_compare<<<grid, kThreads, 0, stream>>>(g, a, c, n, counter, err);
-  return hipGetLastError();
+  return launch(k_compare, dim3((unsigned)tiles, (unsigned)g.L, (unsigned)g.nsub), t, stream, g, a, c, n, counter,
+                err);
 }
 
 }  // namespace hc
