@@ -95,6 +95,10 @@ _SIGS = {
     "hc_write_back_all_layers": (ctypes.c_int, [_V, _V, _V, ctypes.c_int64, _V]),
     "hc_load_back_layer": (ctypes.c_int, [_V, ctypes.c_int32, _V, _V, ctypes.c_int64, _V]),
     "hc_round_trip_check": (ctypes.c_int, [_V, _V, _V, ctypes.c_int64, _I64P]),
+    "hc_load_back_graph_create": (ctypes.c_int, [_V, _V, _V, ctypes.c_int64, ctypes.POINTER(_V),
+                                                 ctypes.POINTER(_V)]),
+    "hc_load_back_graph_launch": (ctypes.c_int, [_V]),
+    "hc_load_back_graph_destroy": (ctypes.c_int, [_V]),
     "hc_pool_kernel_time": (ctypes.c_int, [_V, ctypes.c_int32, ctypes.c_int32, _I64P,
                                            ctypes.POINTER(ctypes.c_double)]),
     "hc_loader_create": (ctypes.c_int, [_V, ctypes.POINTER(hc_loader_ops), ctypes.c_int32, ctypes.c_int32,
@@ -188,6 +192,34 @@ class HipEvent:
         try:
             self.destroy()
         except Exception:  # interpreter shutdown: the HIP module may already be gone
+            pass
+
+
+class LoadBackGraph:
+    """hc_lb_graph: a captured per-layer load-back burst; launch() enqueues one replay
+    on the pool's copy stream.  Keeps the index tensors and events alive."""
+
+    def __init__(self, pool, host_idx, device_idx, events):
+        n = int(device_idx.numel())
+        assert int(host_idx.numel()) == n
+        arr = (_V * max(1, len(events)))(*[e.handle.value if e is not None else None for e in events])
+        self._refs = (pool, host_idx, device_idx, list(events), arr)
+        self.handle = _V()
+        check(lib.hc_load_back_graph_create(pool.handle, _V(_ptr(host_idx)), _V(_ptr(device_idx)), n, arr,
+                                            ctypes.byref(self.handle)), "hc_load_back_graph_create")
+
+    def launch(self) -> None:
+        check(lib.hc_load_back_graph_launch(self.handle), "hc_load_back_graph_launch")
+
+    def close(self) -> None:
+        if self.handle.value:
+            check(lib.hc_load_back_graph_destroy(self.handle), "hc_load_back_graph_destroy")
+            self.handle = _V()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
             pass
 
 
@@ -316,6 +348,11 @@ class Pool:
         assert int(host_idx.numel()) == n
         check(lib.hc_load_back_layer(self.handle, layer, _V(_ptr(host_idx)), _V(_ptr(device_idx)), n,
                                      event.handle if event else None), "hc_load_back_layer")
+
+    def capture_load_back(self, host_idx, device_idx, events) -> "LoadBackGraph":
+        """Capture the per-layer load-back of (host_idx, device_idx) with one event per
+        layer (None entries: no record) into a replayable graph."""
+        return LoadBackGraph(self, host_idx, device_idx, events)
 
     def round_trip_check(self, idx_a, idx_b) -> int:
         out = ctypes.c_int64()

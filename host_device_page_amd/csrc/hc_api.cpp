@@ -805,6 +805,83 @@ int hc_round_trip_check(hc_pool* p, const int64_t* idx_a, const int64_t* idx_b, 
   return rc;
 }
 
+}  // extern "C"
+
+struct hc_lb_graph {
+  hc_pool* pool = nullptr;
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+};
+
+extern "C" {
+
+int hc_load_back_graph_destroy(hc_lb_graph* g) {
+  if (!g) return HC_OK;
+  int rc = HC_OK;
+  if (g->exec && hipGraphExecDestroy(g->exec) != hipSuccess) rc = set_err(HC_ERR_HIP, "hipGraphExecDestroy failed");
+  if (g->graph && hipGraphDestroy(g->graph) != hipSuccess) rc = set_err(HC_ERR_HIP, "hipGraphDestroy failed");
+  delete g;
+  return rc;
+}
+
+int hc_load_back_graph_create(hc_pool* p, const int64_t* host_idx, const int64_t* device_idx, int64_t n,
+                              void* const* layer_events, hc_lb_graph** out) {
+  if (!out) return set_err(HC_ERR_INVALID, "out is null");
+  *out = nullptr;
+  if (!p || !layer_events) return set_err(HC_ERR_INVALID, "null argument");
+  if (n < 0) return set_err(HC_ERR_INVALID, "n must be >= 0");
+  if (n > 0 && (!host_idx || !device_idx)) return set_err(HC_ERR_INVALID, "null index list");
+  std::lock_guard<std::recursive_mutex> lock(p->mu);
+  if (p->flags & HC_FLAG_PROFILE)
+    return set_err(HC_ERR_UNSUPPORTED, "a pool created with HC_FLAG_PROFILE cannot be captured");
+  int rc = use_device(p);
+  if (rc != HC_OK) return rc;
+  hipStreamCaptureStatus status = hipStreamCaptureStatusNone;
+  HIP_TRY(hipStreamIsCapturing(p->stream, &status));
+  if (status != hipStreamCaptureStatusNone) return set_err(HC_ERR_INVALID, "the pool's stream is already capturing");
+  hc_lb_graph* g = new (std::nothrow) hc_lb_graph();
+  if (!g) return set_err(HC_ERR_NOMEM, "graph handle allocation failed");
+  g->pool = p;
+  hipError_t e = hipStreamBeginCapture(p->stream, hipStreamCaptureModeThreadLocal);
+  if (e != hipSuccess) {
+    delete g;
+    return set_err(HC_ERR_HIP, "hipStreamBeginCapture failed: %s", hipGetErrorString(e));
+  }
+  for (int32_t l = 0; l < p->lay.L && rc == HC_OK; l++)
+    rc = hc_load_back_layer(p, l, host_idx, device_idx, n, layer_events[l]);
+  const std::string layer_err = rc != HC_OK ? g_err : std::string();
+  e = hipStreamEndCapture(p->stream, &g->graph);
+  if (rc != HC_OK) {
+    (void)hipGetLastError();
+    hc_load_back_graph_destroy(g);
+    return set_err(rc, "capture stopped: %s", layer_err.c_str());
+  }
+  if (e != hipSuccess || !g->graph) {
+    (void)hipGetLastError();
+    hc_load_back_graph_destroy(g);
+    return set_err(HC_ERR_HIP, "hipStreamEndCapture failed: %s", hipGetErrorString(e));
+  }
+  e = hipGraphInstantiate(&g->exec, g->graph, nullptr, nullptr, 0);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    g->exec = nullptr;
+    hc_load_back_graph_destroy(g);
+    return set_err(HC_ERR_HIP, "hipGraphInstantiate failed: %s", hipGetErrorString(e));
+  }
+  *out = g;
+  return HC_OK;
+}
+
+int hc_load_back_graph_launch(hc_lb_graph* g) {
+  if (!g) return set_err(HC_ERR_INVALID, "graph is null");
+  hc_pool* p = g->pool;
+  std::lock_guard<std::recursive_mutex> lock(p->mu);
+  int rc = use_device(p);
+  if (rc != HC_OK) return rc;
+  HIP_TRY(hipGraphLaunch(g->exec, p->stream));
+  return HC_OK;
+}
+
 int hc_pool_kernel_time(hc_pool* p, int32_t kind, int32_t reset, int64_t* launches, double* total_ms) {
   if (!p || !launches || !total_ms) return set_err(HC_ERR_INVALID, "null argument");
   std::lock_guard<std::recursive_mutex> lock(p->mu);

@@ -209,6 +209,31 @@ int hc_load_back_layer(hc_pool* pool, int32_t layer, const int64_t* host_idx,
 int hc_round_trip_check(hc_pool* pool, const int64_t* idx_a, const int64_t* idx_b, int64_t n,
                         int64_t* mismatched_units);
 
+/* ---------------------------------------------------------------- captured load-back bursts
+ * The per-layer load-back chain of one burst, captured once into a HIP graph on
+ * the pool's copy stream: L hc_load_back_layer calls, each with its layer-done
+ * event record (loader-thread page, sglang PR 38472, Motivation: the per-layer
+ * enqueue is launch overhead the forward pass waits behind).  A replay re-runs
+ * all L layers with whatever the two index lists hold when it executes; the
+ * lists' addresses, n and the events are fixed at capture.  One graph launch
+ * replaces L kernel launches and L event records on the CPU.
+ *
+ * hc_load_back_graph_create: host_idx / device_idx are device-resident lists of n
+ * entries that stay allocated while the graph lives; layer_events holds L
+ * caller-owned events (entries may be NULL: no record for that layer).  Captures
+ * in thread-local mode, so the pool's stream must not be capturing already and
+ * nothing else may be enqueued on it from this thread meanwhile.  Pools created
+ * with HC_FLAG_PROFILE are refused (HC_ERR_UNSUPPORTED): their per-launch timing is
+ * not part of a graph.  On any failure nothing stays captured and *out is NULL.
+ * hc_load_back_graph_launch enqueues one replay on the pool's copy stream (FIFO
+ * with the pool's other calls).  hc_load_back_graph_destroy frees the graph (NULL
+ * is a no-op); destroy graphs before their pool. */
+typedef struct hc_lb_graph hc_lb_graph;
+int hc_load_back_graph_create(hc_pool* pool, const int64_t* host_idx, const int64_t* device_idx, int64_t n,
+                              void* const* layer_events, hc_lb_graph** out);
+int hc_load_back_graph_launch(hc_lb_graph* graph);
+int hc_load_back_graph_destroy(hc_lb_graph* graph);
+
 /* ---------------------------------------------------------------- asynchronous load-back enqueue
  * A loader runs the per-layer load-back of whole bursts off the caller's thread
  * (loader-thread page, sglang PR 38472, Modifications): the caller hands over a

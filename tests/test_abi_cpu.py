@@ -85,6 +85,12 @@ def test_null_arguments_without_gpu():
     out = ctypes.c_void_p()
     assert B.lib.hc_host_alloc(0, 0, ctypes.byref(out)) == B.HC_ERR_INVALID
     assert B.lib.hc_pool_create(None, ctypes.byref(out)) == B.HC_ERR_INVALID
+    evs = (ctypes.c_void_p * 1)()
+    assert B.lib.hc_load_back_graph_create(None, None, None, 0, evs, ctypes.byref(out)) == B.HC_ERR_INVALID
+    assert out.value is None
+    assert B.lib.hc_load_back_graph_create(None, None, None, 0, evs, None) == B.HC_ERR_INVALID
+    assert B.lib.hc_load_back_graph_launch(None) == B.HC_ERR_INVALID
+    assert B.lib.hc_load_back_graph_destroy(None) == B.HC_OK
 
 
 GEOMS = [
