@@ -310,6 +310,37 @@ def h2h_main(args):
     print(json.dumps(out), flush=True)
 
 
+def load_back_graph_timing(B, np, pool, stream, L, h, d, link_bytes, reps=7):
+    """The per-layer load-back of (h, d) as one captured graph against the same L calls
+    made eagerly, on an unprofiled pool: GPU time per layer (HIP events on the copy
+    stream) and CPU time to enqueue the burst, medians after 2 warm-up repetitions."""
+    events = [B.HipEvent() for _ in range(L)]
+    e0, e1 = B.HipEvent(timing=True), B.HipEvent(timing=True)
+    graph = pool.capture_load_back(h, d, events)
+    g_ms, g_cpu, e_ms, e_cpu = [], [], [], []
+    for _ in range(reps):
+        e0.record(stream)
+        t0 = time.perf_counter()
+        graph.launch()
+        g_cpu.append(time.perf_counter() - t0)
+        e1.record(stream)
+        e1.synchronize()
+        g_ms.append(e0.elapsed_ms(e1))
+        e0.record(stream)
+        t0 = time.perf_counter()
+        for l in range(L):
+            pool.load_back_layer(l, h, d, events[l])
+        e_cpu.append(time.perf_counter() - t0)
+        e1.record(stream)
+        e1.synchronize()
+        e_ms.append(e0.elapsed_ms(e1))
+    graph.close()
+    med = lambda v: float(np.median(v[2:]))
+    return {"graph_ms_per_layer": round(med(g_ms) / L, 4), "eager_ms_per_layer": round(med(e_ms) / L, 4),
+            "graph_GBps": round(link_bytes / (med(g_ms) * 1e6), 3), "eager_GBps": round(link_bytes / (med(e_ms) * 1e6), 3),
+            "graph_cpu_ms_per_burst": round(1e3 * med(g_cpu), 4), "eager_cpu_ms_per_burst": round(1e3 * med(e_cpu), 4)}
+
+
 def burst_size_sweep(B, np, pool, shape, stream, burst, d_t, h_np, h_t, d2_t, args):
     """Latency and rate against burst size: the first k pages' tokens of the
     workload's burst, k = 1, 2, 4, ... up to the whole burst.  Write-back: one call
@@ -354,6 +385,7 @@ def burst_size_sweep(B, np, pool, shape, stream, burst, d_t, h_np, h_t, d2_t, ar
             e1.synchronize()
             chain.append(e0.elapsed_ms(e1))
         # the first two repetitions warm up
+        g = load_back_graph_timing(B, np, pool, stream, L, hd, d2, link)
         wb_ms, cpu_ms = float(np.median(wb[2:])), 1e3 * float(np.median(cpu[2:]))
         one_ms, chain_ms = float(np.median(one[2:])), float(np.median(chain[2:])) / L
         rows.append({"pages": k, "tokens": n, "bytes_each_way": link,
@@ -361,7 +393,10 @@ def burst_size_sweep(B, np, pool, shape, stream, burst, d_t, h_np, h_t, d2_t, ar
                      "write_back_cpu_ms": round(cpu_ms, 4),
                      "load_back_one_layer_ms": round(one_ms, 4),
                      "load_back_ms_per_layer_chained": round(chain_ms, 4),
-                     "load_back_GBps_chained": round(link / L / (chain_ms * 1e6), 2)})
+                     "load_back_GBps_chained": round(link / L / (chain_ms * 1e6), 2),
+                     "load_back_ms_per_layer_graph": g["graph_ms_per_layer"],
+                     "load_back_graph_cpu_ms": g["graph_cpu_ms_per_burst"],
+                     "load_back_eager_cpu_ms": g["eager_cpu_ms_per_burst"]})
         log(f"[sweep] {rows[-1]}")
     pool.sync()
     return rows
@@ -542,6 +577,8 @@ def main():
             bu.release()
         ld.close()
         handover["loader_thread" if asynchronous else "inline"] = round(1e3 * float(np.median(times)), 4)
+    graph = load_back_graph_timing(B, np, hpool, stream, L, h_t, d2_t, link_bytes)
+    log(f"[bench] captured load-back burst: {graph}")
     hpool.close()
     log(f"[bench] load-back hand-over per burst (ms): {handover}")
     pool.close()
@@ -610,6 +647,7 @@ def main():
         "host_link_peak_GBps": {"h2d": round(peak_h2d, 3), "d2h": round(peak_d2h, 3)},
         "frac_of_link_peak": {"write_back": round(wb_gbs / peak_d2h, 4), "load_back": round(lb_gbs / peak_h2d, 4)},
         "cpu_enqueue_ms_per_step": round(1e3 * float(np.median(enqueue_s)), 3),
+        "load_back_graph": graph,
         "load_back_handover_ms": handover,
         "layer_pipeline": pipeline,
         "kernel_avg_ms": {"zc_read": round(ms_rd / max(1, n_rd), 4), "zc_write": round(ms_wr / max(1, n_wr), 4)},
