@@ -1,6 +1,7 @@
-/* A write-back and a per-layer load-back through the C ABI from plain C (HIP
- * runtime for memory and streams, no Python), checked byte for byte against the
- * C oracle.  Built by tests/c/build.py, run by tests/test_c_programs.py on a GPU. */
+/* A write-back, a per-layer load-back and a captured load-back burst replayed into
+ * new slots, through the C ABI from plain C (HIP runtime for memory and streams,
+ * no Python), each checked byte for byte against the C oracle.  Built by
+ * tests/c/build.py, run by tests/test_c_programs.py on a GPU. */
 #include <stdint.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -156,8 +157,36 @@ int main(void) {
   int64_t bad = -1;
   HCCK(hc_round_trip_check(pool, dd, dd2, n, &bad));
   if (bad != 0) return 8;
+
+  /* the load-back captured once, then replayed after the slot list was rewritten in place */
+  hc_lb_graph* graph = NULL;
+  HCCK(hc_load_back_graph_create(pool, dh, dd2, n, (void* const*)ev, &graph));
+  int64_t d3[NPAGES * P];
+  for (int64_t i = 0; i < n; i++) {
+    int s;
+    do s = (int)(next() % S); while (used_slot[s]);
+    used_slot[s] = 1;
+    d3[i] = s;
+  }
+  HIPCK(hipMemcpy(dd2, d3, sizeof(d3), hipMemcpyHostToDevice));
+  HCCK(hc_load_back_graph_launch(graph));
+  for (int l = 0; l < L; l++) HIPCK(hipEventSynchronize(ev[l]));
+  for (int l = 0; l < L; l++)
+    if (orc_load_back_layer(&g, l, hostcopy, want, hidx, d3, n) != ORC_OK) return 9;
+  for (int b = 0; b < NSUB; b++)
+    for (int l = 0; l < L; l++) {
+      size_t nb = (size_t)(S * E[b]);
+      uint8_t* got = (uint8_t*)malloc(nb);
+      HIPCK(hipMemcpy(got, dlayers[b][l], nb, hipMemcpyDeviceToHost));
+      if (memcmp(got, hostcopy[b * L + l], nb) != 0) {
+        fprintf(stderr, "captured load-back differs from the oracle (sub %d layer %d)\n", b, l);
+        return 10;
+      }
+      free(got);
+    }
+  HCCK(hc_load_back_graph_destroy(graph));
   HCCK(hc_pool_destroy(pool));
   HCCK(hc_host_free(host));
-  printf("gpu_roundtrip ok: %lld tokens x %d layers x %d sub-buffers bit-exact\n", (long long)n, L, NSUB);
+  printf("gpu_roundtrip ok: %lld tokens x %d layers x %d sub-buffers bit-exact, eager and captured\n", (long long)n, L, NSUB);
   return 0;
 }
