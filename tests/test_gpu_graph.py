@@ -171,3 +171,42 @@ def test_profiling_pool_is_refused():
         rig.pool.sync()
     finally:
         rig.close()
+
+
+@pytest.mark.gpu
+def test_replay_with_an_out_of_range_slot_is_reported_not_faulted():
+    """Kernels range-check device-resident indices, in a replay as eagerly: the bad row is
+    skipped, the others land, and the next sync reports HC_ERR_DEVICE."""
+    shape = SHAPES[0]
+    say("[graph] out-of-range slot in a replay")
+    rig = Rig(shape, seed=9)
+    graph = None
+    try:
+        randomize_host(rig, 11)
+        L = shape.layers
+        h, d = lists(shape, 3, 50)
+        h_buf, d_buf = cuda_i64(h), cuda_i64(d)
+        events = [B.HipEvent() for _ in range(L)]
+        graph = rig.pool.capture_load_back(h_buf, d_buf, events)
+        bad = d.copy()
+        bad[4] = shape.device_slots + 3
+        d_buf.copy_(cuda_i64(bad))
+        torch.cuda.synchronize()
+        dev0 = rig.dev_np()
+        host0 = rig.host.np.copy()
+        graph.launch()
+        for ev in events:
+            ev.synchronize()
+        with pytest.raises(B.HcError) as ex:
+            rig.pool.sync()
+        assert ex.value.code == B.HC_ERR_DEVICE and "out of range" in str(ex.value)
+        rig.pool.sync()  # the report is cleared once read
+        keep = np.arange(h.size) != 4
+        want = [[a.copy() for a in row] for row in dev0]
+        for l in range(L):
+            O.load_back_layer(rig.geom, l, want, host0, h[keep], bad[keep])
+        assert_dev_equal(rig.dev_np(), want, "replay with one bad slot")
+    finally:
+        if graph is not None:
+            graph.close()
+        rig.close()

@@ -72,6 +72,8 @@ CASES = [
     ("token_major_rows", S("token_major_rows", 4, 64, [(T, 2048)] * 2, 32768, 64, TM), "segment", 12, 41),
     ("token_major_indexer", S("token_major_indexer", 3, 64, [(T, 1152), (BLK, 8448)], 8192, 32, TM), "aligned", 10, 0),
     ("token_major_small_rows", S("token_major_small_rows", 5, 8, [(T, 16), (T, 48)], 4096, 64, TM), "requests", 50, 0),
+    # the largest layer count the descriptor accepts (HC_MAX_LAYERS), rows and page blocks
+    ("max_layers", S("max_layers", 1024, 4, [(T, 16), (BLK, 32)], 256, 8), "aligned", 3, 0),
 ]
 
 
