@@ -15,8 +15,9 @@
 // loop then walks the unit's rows * (elem/16) vectors with all 256 lanes: lane
 // u copies vector u % vecs of row u / vecs, so consecutive lanes touch
 // consecutive 16-byte vectors of a row, and a run of slots that are adjacent
-// on both sides is one contiguous stream of addresses.  Loads are issued
-// kUnroll deep before the stores to keep enough bytes in flight.
+// on both sides is one contiguous stream of addresses.  Loads are issued in
+// batches before their stores to keep enough bytes in flight (depth per kernel
+// below).
 //
 // The zero-copy kernels shrink the tile to kTile >> tile_shift tokens when a
 // burst is too small to give every workgroup of the grid a unit: a small burst
@@ -58,6 +59,17 @@ constexpr int kThreads = 256;  // 4 waves of 64
 #endif
 constexpr bool kReadPipelined = HC_READ_PIPELINED != 0;
 constexpr int kReadUnroll = HC_READ_UNROLL;
+// The write-back kernel reads HBM and writes over the host link, on a small grid: plain
+// batches 16 deep (measured 38.46 ms per 2 GiB burst against 38.60 at 8, flat from 16 to
+// 32; the pipelined loop is slower here, 39.1-40.2 ms).
+#ifndef HC_WRITE_PIPELINED
+#define HC_WRITE_PIPELINED 0
+#endif
+#ifndef HC_WRITE_UNROLL
+#define HC_WRITE_UNROLL 16
+#endif
+constexpr bool kWritePipelined = HC_WRITE_PIPELINED != 0;
+constexpr int kWriteUnroll = HC_WRITE_UNROLL;
 constexpr int kTile = HC_TILE; // tokens per unit (<= kThreads): one per thread at intake
 static_assert(kTile <= kThreads && kTile % 64 == 0, "tile must be whole waves of one block");
 #ifndef HC_GATHER_TILE
@@ -300,7 +312,7 @@ __global__ __launch_bounds__(kThreads) void k_zc_write(Geom g, const int64_t* __
       s_dst[slot] = dst;
     }
     __syncthreads();
-    copy_rows<false, kUnroll>(s_src, s_dst, total, s.vecs, s.vec_magic);
+    copy_rows<kWritePipelined, kWriteUnroll>(s_src, s_dst, total, s.vecs, s.vec_magic);
     __syncthreads();  // LDS is rewritten by the next unit
   }
 }
