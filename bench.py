@@ -43,7 +43,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="llama3_8b_mha_bf16")
-    ap.add_argument("--write-back-mode", choices=["auto", "zerocopy", "staged"], default="auto")
+    ap.add_argument("--write-back-mode", choices=["auto", "zerocopy", "staged"], default="zerocopy",
+                    help="mode of the timed write-back (zero-copy: the highest burst rate; the staged mode, "
+                         "which leaves concurrent compute alone, is measured beside it)")
     ap.add_argument("--staging-pages", type=int, default=32)
     ap.add_argument("--max-ctas", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle sample")
@@ -265,6 +267,48 @@ def layer_pipeline(B, torch, pool, shape, h_t, d2_t, n, stream, layer_events, ma
         log(f"[bench] layer pipeline {key}: {res[key]}")
         if p is not pool:
             p.close()
+    return res
+
+
+def write_back_overlap(B, torch, np, pools, d_t, h_np):
+    """A whole write-back burst next to independent compute (bf16 4096^3 matmuls on a
+    second stream, about as long as the burst), per write-back mode.  overlap =
+    (write-back + compute - both) / min(write-back, compute); compute_slowdown = how
+    much longer the matmuls take beside the burst than alone."""
+    consumer = torch.cuda.Stream()
+    a = torch.randn(4096, 4096, device="cuda", dtype=torch.bfloat16)
+    w = torch.randn(4096, 4096, device="cuda", dtype=torch.bfloat16)
+    out = torch.empty(4096, 4096, device="cuda", dtype=torch.bfloat16)
+
+    def timed(fn):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        fn()
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0
+
+    def matmuls(k):
+        with torch.cuda.stream(consumer):
+            for _ in range(k):
+                torch.matmul(a, w, out=out)
+    for _ in range(3):
+        timed(lambda: matmuls(1))
+    per_mm = float(np.median([timed(lambda: matmuls(1)) for _ in range(5)]))
+    res = {"compute": "bf16 matmul 4096^3 repeated on a second stream, no dependency on the burst"}
+    for mode, p in pools.items():
+        p.write_back_all_layers(d_t, h_np)
+        t_wb = float(np.median([timed(lambda: p.write_back_all_layers(d_t, h_np)) for _ in range(3)]))
+        k = max(1, int(round(t_wb / max(per_mm, 1e-6))))
+        t_c = float(np.median([timed(lambda: matmuls(k)) for _ in range(3)]))
+
+        def both():
+            p.write_back_all_layers(d_t, h_np)
+            matmuls(k)
+        t_both = float(np.median([timed(both) for _ in range(3)]))
+        res[mode] = {"write_back_ms": round(1e3 * t_wb, 3), "compute_ms": round(1e3 * t_c, 3),
+                     "both_ms": round(1e3 * t_both, 3), "matmuls": k,
+                     "overlap": round((t_wb + t_c - t_both) / min(t_wb, t_c), 4)}
+        log(f"[bench] write-back beside compute, {mode}: {res[mode]}")
     return res
 
 
@@ -618,6 +662,11 @@ def main():
                   "copy_engine_ms_per_burst": round(ms_c / reps, 3),
                   "gather_ms_per_burst": round(ms_g / reps, 3)}
         spool.close()
+        # both write-back modes beside independent compute, on pools without timing events
+        ov_pools = {"zerocopy": make_pool(B.HC_MODE_ZEROCOPY, flags=0), "staged": make_pool(B.HC_MODE_STAGED, flags=0)}
+        staged["beside_compute"] = write_back_overlap(B, torch, np, ov_pools, d_t, h_np)
+        for p in ov_pools.values():
+            p.close()
         log(f"[bench] staged write-back {staged}, gather {g_gbs:.1f} GB/s")
 
     cpu = cpu_mt = None

@@ -568,8 +568,12 @@ int hc_pool_create(const hc_pool_desc* desc, hc_pool** out) {
       rc = check_device_ptr(desc->sub[b].device_layers[l], "device layer");
       if (rc != HC_OK) return bail(rc);
     }
-  // modes: zero-copy is the measured default for both directions
-  p->wb_mode = desc->write_back_mode == HC_MODE_STAGED ? HC_MODE_STAGED : HC_MODE_ZEROCOPY;
+  // modes.  AUTO write-back is staged whenever the caller brings staging for it: a
+  // zero-copy write-back that saturates the host link slows compute on other streams
+  // until it barely overlaps, staged write-back leaves that compute alone (measured).
+  const bool auto_staged = desc->write_back_mode == HC_MODE_AUTO && desc->staging &&
+                           desc->staging_bytes >= L.stride && ((uintptr_t)desc->staging) % 16 == 0;
+  p->wb_mode = (desc->write_back_mode == HC_MODE_STAGED || auto_staged) ? HC_MODE_STAGED : HC_MODE_ZEROCOPY;
   p->lb_mode = HC_MODE_ZEROCOPY;
   if (p->wb_mode == HC_MODE_STAGED) {
     rc = check_device_ptr(desc->staging, "staging");

@@ -84,8 +84,14 @@ enum { HC_TOKEN_ROWS = 0, HC_PAGE_BLOCKS = 1 };
 enum { HC_LAYOUT_PAGE_FIRST = 0, HC_LAYOUT_KV_SPLIT_SHARD = 1, HC_LAYOUT_PAGE_FIRST_TOKEN_MAJOR = 2 };
 /* Transfer modes.  STAGED: device kernels relayout through the device staging
  * buffer and the copy engines (hipMemcpyAsync) cross the host link.  ZEROCOPY:
- * kernels read or write the pinned host pool directly.  AUTO: the library's
- * measured default (see hc_pool_mode). */
+ * kernels read or write the pinned host pool directly.  AUTO: write-back is staged
+ * when the descriptor brings a staging buffer of at least one page image, else
+ * zero-copy; load-back is zero-copy (hc_pool_mode reports the choice).
+ * Measured on MI355X: zero-copy write-back reaches ~98 % of the host-link peak, but
+ * while its kernel saturates the link, compute kernels on other streams slow down
+ * until they barely overlap it; staged write-back runs ~12 % slower alone and leaves
+ * concurrent compute almost untouched, because the copy engines carry its host
+ * writes.  Zero-copy load-back overlaps compute well on its default grid. */
 enum { HC_MODE_AUTO = 0, HC_MODE_STAGED = 1, HC_MODE_ZEROCOPY = 2 };
 /* Pool flags. */
 enum { HC_FLAG_VALIDATE = 1, HC_FLAG_PROFILE = 2 };
@@ -111,7 +117,8 @@ typedef struct hc_pool_desc {
   int64_t shard_align;  /* shard layout: power of two >= 16 (4096 for Direct I/O); ignored otherwise */
   void* host_base;      /* pinned host memory (hc_host_alloc or hipHostMalloc), >= hc_host_pool_bytes */
   int64_t host_bytes;   /* size of host_base */
-  void* staging;        /* device memory for HC_MODE_STAGED write-back; NULL when no staged mode is used */
+  void* staging;        /* device memory for staged write-back (HC_MODE_STAGED, or HC_MODE_AUTO when it
+                           holds at least one page image); NULL when no staged mode is used */
   int64_t staging_bytes;/* size of staging; the chunk is staging_bytes / hc_staging_page_bytes pages,
                            capped so that one chunk fits the 256 MB Infinity Cache (at least 1 page) */
   void* copy_stream;    /* hipStream_t every transfer of this pool is enqueued on (NULL: null stream) */

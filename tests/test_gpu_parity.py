@@ -195,3 +195,19 @@ def test_small_bursts_shrink_tiles(shape, pages, max_ctas):
         load_back_and_check(rig, h, fresh(shape, d, pages + 7))
     finally:
         rig.close()
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("staging_pages,want", [(0, B.HC_MODE_ZEROCOPY), (2, B.HC_MODE_STAGED)])
+def test_auto_mode_stages_write_back_when_staging_is_given(staging_pages, want):
+    """HC_MODE_AUTO: staged write-back with a staging buffer, zero-copy without; both bit-exact."""
+    shape = GRID_SHAPE
+    say(f"[auto] staging_pages={staging_pages}")
+    d, h = burst(shape, 3, "perm", 9)
+    rig = Rig(shape, seed=3, write_back_mode=B.HC_MODE_AUTO, staging_pages=staging_pages)
+    try:
+        assert rig.pool.mode(0) == want and rig.pool.mode(1) == B.HC_MODE_ZEROCOPY
+        write_back_and_check(rig, d, h)
+        load_back_and_check(rig, h, fresh(shape, d, 4))
+    finally:
+        rig.close()
