@@ -22,6 +22,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -98,6 +99,7 @@ struct hc_pool {
   // Serializes the pool's entry points: a loader thread and the caller may use one
   // pool at the same time.  Recursive because hc_round_trip_check calls hc_pool_sync.
   std::recursive_mutex mu;
+  std::atomic<int64_t> users{0};  // loaders and captured graphs that hold this pool
   Layout lay;
   Geom geom;
   int device = 0;
@@ -615,6 +617,9 @@ int hc_pool_create(const hc_pool_desc* desc, hc_pool** out) {
 
 int hc_pool_destroy(hc_pool* p) {
   if (!p) return HC_OK;
+  if (p->users.load() > 0)
+    return set_err(HC_ERR_INVALID, "%lld loader(s) or captured graph(s) still use the pool; destroy them first",
+                   (long long)p->users.load());
   int rc = HC_OK;
   if (p->stream || p->d_tables) {
     if (hipStreamSynchronize(p->stream) != hipSuccess) rc = set_err(HC_ERR_HIP, "stream sync failed in destroy");
@@ -813,6 +818,7 @@ int hc_round_trip_check(hc_pool* p, const int64_t* idx_a, const int64_t* idx_b, 
 
 struct hc_lb_graph {
   hc_pool* pool = nullptr;
+  bool held = false;  // counted in pool->users
   hipGraph_t graph = nullptr;
   hipGraphExec_t exec = nullptr;
 };
@@ -824,6 +830,7 @@ int hc_load_back_graph_destroy(hc_lb_graph* g) {
   int rc = HC_OK;
   if (g->exec && hipGraphExecDestroy(g->exec) != hipSuccess) rc = set_err(HC_ERR_HIP, "hipGraphExecDestroy failed");
   if (g->graph && hipGraphDestroy(g->graph) != hipSuccess) rc = set_err(HC_ERR_HIP, "hipGraphDestroy failed");
+  if (g->held) hc::pool_release(g->pool);
   delete g;
   return rc;
 }
@@ -872,6 +879,8 @@ int hc_load_back_graph_create(hc_pool* p, const int64_t* host_idx, const int64_t
     hc_load_back_graph_destroy(g);
     return set_err(HC_ERR_HIP, "hipGraphInstantiate failed: %s", hipGetErrorString(e));
   }
+  hc::pool_hold(p);
+  g->held = true;
   *out = g;
   return HC_OK;
 }
@@ -959,5 +968,9 @@ void pool_loader_ops(hc_pool* pool, hc_loader_ops* ops) {
 }
 
 int pool_layers(const hc_pool* pool) { return pool->lay.L; }
+
+void pool_hold(hc_pool* pool) { pool->users.fetch_add(1); }
+
+void pool_release(hc_pool* pool) { pool->users.fetch_sub(1); }
 
 }  // namespace hc

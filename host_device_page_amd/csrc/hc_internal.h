@@ -64,6 +64,9 @@ int set_error(int code, const char* fmt, ...);
 // The pool's own device operations for an hc_loader, and its layer count.
 void pool_loader_ops(hc_pool* pool, hc_loader_ops* ops);
 int pool_layers(const hc_pool* pool);
+// Loaders and captured graphs that hold a pool: hc_pool_destroy refuses while any do.
+void pool_hold(hc_pool* pool);
+void pool_release(hc_pool* pool);
 
 // Optional timing of one kernel launch: two timing events that the launch itself
 // stamps with the kernel's start and end (hipExtLaunchKernel), so timing adds no

@@ -142,6 +142,7 @@ int hc_loader_create(hc_pool* pool, const hc_loader_ops* ops, int32_t num_layers
     }
     ld->running = true;
   }
+  if (pool) hc::pool_hold(pool);
   *out = ld;
   return HC_OK;
 }
@@ -261,6 +262,7 @@ int hc_loader_destroy(hc_loader* ld) {
     ld->cv.notify_all();
   }
   if (ld->worker.joinable()) ld->worker.join();  // the worker empties its queue first
+  if (ld->pool) hc::pool_release(ld->pool);
   delete ld;
   return HC_OK;
 }

@@ -165,7 +165,9 @@ int hc_host_free(void* ptr);
  * records the modes.  Touches the current HIP device. */
 int hc_pool_create(const hc_pool_desc* desc, hc_pool** out);
 
-/* Waits for the pool's copy stream, then frees the handle and its scratch.  NULL is a no-op. */
+/* Waits for the pool's copy stream, then frees the handle and its scratch.  NULL is a no-op.
+ * Refused (HC_ERR_INVALID, nothing freed) while a loader or a captured load-back graph
+ * created on the pool still exists: destroy those first. */
 int hc_pool_destroy(hc_pool* pool);
 
 /* The mode write-back (which = 0) or load-back (which = 1) resolves to

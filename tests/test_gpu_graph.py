@@ -210,3 +210,26 @@ def test_replay_with_an_out_of_range_slot_is_reported_not_faulted():
         if graph is not None:
             graph.close()
         rig.close()
+
+
+@pytest.mark.gpu
+def test_pool_outlives_its_graphs_and_loaders():
+    """hc_pool_destroy refuses while a captured graph or a loader still holds the pool."""
+    shape = SHAPES[0]
+    say("[graph] pool destroy refused while held")
+    rig = Rig(shape, seed=12)
+    try:
+        h, d = lists(shape, 2, 60)
+        graph = rig.pool.capture_load_back(cuda_i64(h), cuda_i64(d), [B.HipEvent() for _ in range(shape.layers)])
+        loader = B.Loader(rig.pool, shape.layers, asynchronous=True)
+        with pytest.raises(B.HcError) as ex:
+            rig.pool.close()
+        assert ex.value.code == B.HC_ERR_INVALID and "destroy them first" in str(ex.value)
+        graph.close()
+        with pytest.raises(B.HcError):
+            rig.pool.close()
+        loader.close()
+        rig.pool.load_back_layer(0, cuda_i64(h), cuda_i64(d))  # the pool still works
+        rig.pool.sync()
+    finally:
+        rig.close()
