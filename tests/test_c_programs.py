@@ -17,6 +17,21 @@ def test_c_program_without_gpu():
     assert "abi_cpu ok" in r.stdout
 
 
+@pytest.mark.parametrize("kind,banner", [("tsan", "sanitizer: thread"), ("asan", "sanitizer: address")])
+def test_host_machinery_under_sanitizers(kind, banner):
+    """The loader thread and the host-to-host worker pool, stressed from several threads,
+    under ThreadSanitizer and under AddressSanitizer + UndefinedBehaviorSanitizer."""
+    exe = cbuild.build_sanitized(kind)
+    env = dict(os.environ, TSAN_OPTIONS="halt_on_error=1 second_deadlock_stack=1",
+               ASAN_OPTIONS="detect_leaks=1 abort_on_error=0", UBSAN_OPTIONS="halt_on_error=1 print_stacktrace=1")
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=300, env=env)
+    report = "\n".join(ln for ln in r.stderr.splitlines() if "burst enqueue failed" not in ln)
+    assert r.returncode == 0, report[-4000:]
+    assert banner in r.stdout and "sanitize_host ok" in r.stdout
+    assert "WARNING: ThreadSanitizer" not in r.stderr and "ERROR: AddressSanitizer" not in r.stderr
+    assert "runtime error" not in r.stderr
+
+
 @pytest.mark.gpu
 def test_c_program_round_trip_on_gpu():
     exe = os.path.join(HERE, "c", "gpu_roundtrip")
