@@ -28,6 +28,7 @@
 #include <vector>
 
 #include "hc_internal.h"
+#include "hc_plan.h"
 
 using hc::Geom;
 using hc::Layout;
@@ -77,17 +78,6 @@ struct PlanBuf {
   bool pending = false;
 };
 
-struct Region {
-  uint8_t* dst;
-  const uint8_t* src;
-  int64_t len;
-};
-
-struct Chunk {
-  int64_t t0, t1;
-  size_t r0, r1;  // regions [r0, r1)
-};
-
 struct TimedLaunch {
   int kind;
   hipEvent_t a, b;
@@ -118,14 +108,7 @@ struct hc_pool {
   unsigned long long* d_counter = nullptr;
   unsigned long long* h_counter = nullptr;  // pinned
   int32_t* h_err = nullptr;                 // pinned
-  // planner scratch
-  std::vector<int32_t> page_slot;   // [H] staging slot of a page in the open chunk, -1 otherwise
-  std::vector<uint64_t> seen;       // bitmap over host tokens (distinctness)
-  std::vector<uint64_t> page_seen;  // bitmap over host pages
-  std::vector<int64_t> slot_page;
-  std::vector<int32_t> slot_rows;
-  std::vector<Region> regions;
-  std::vector<Chunk> chunks;
+  hc::Planner planner;  // write-back plan, once per burst on the CPU
   PlanBuf plan[2];
   int plan_cur = 0;
   // measurement
@@ -298,135 +281,6 @@ int plan_upload(hc_pool* p, int64_t bytes) {
 }
 
 inline int64_t align16(int64_t x) { return (x + 15) / 16 * 16; }
-
-inline bool test_and_set(std::vector<uint64_t>& bits, int64_t k) {
-  uint64_t& w = bits[(size_t)(k >> 6)];
-  const uint64_t m = (uint64_t)1 << (k & 63);
-  const bool was = (w & m) != 0;
-  w |= m;
-  return was;
-}
-
-inline void clear_bit(std::vector<uint64_t>& bits, int64_t k) { bits[(size_t)(k >> 6)] &= ~((uint64_t)1 << (k & 63)); }
-
-// Range and distinctness of the host index list (CPU-resident for write-back).
-int validate_host_idx(hc_pool* p, const int64_t* h, int64_t n) {
-  const int64_t tokens = p->lay.H * p->lay.P;
-  int64_t bad = -1;
-  int64_t i = 0;
-  for (; i < n; i++) {
-    const int64_t x = h[i];
-    if (x < 0 || x >= tokens) {
-      bad = i;
-      break;
-    }
-    if (test_and_set(p->seen, x)) {
-      bad = i;
-      break;
-    }
-  }
-  for (int64_t j = 0; j < i; j++) clear_bit(p->seen, h[j]);
-  if (bad >= 0) {
-    const int64_t x = h[bad];
-    if (x < 0 || x >= tokens)
-      return set_err(HC_ERR_INVALID, "host_idx[%lld] = %lld out of range [0, %lld)", (long long)bad, (long long)x,
-                     (long long)tokens);
-    return set_err(HC_ERR_INVALID, "host_idx[%lld] = %lld repeats an earlier entry", (long long)bad, (long long)x);
-  }
-  if (p->lay.has_blocks) {
-    // every named page whole: count rows per page
-    std::vector<int32_t> rows;
-    rows.assign((size_t)p->lay.H, 0);
-    for (int64_t j = 0; j < n; j++) rows[(size_t)(h[j] / p->lay.P)]++;
-    for (int64_t j = 0; j < n; j++) {
-      if (rows[(size_t)(h[j] / p->lay.P)] != p->lay.P)
-        return set_err(HC_ERR_INVALID, "page %lld is named partially; page-block sub-buffers need whole pages",
-                       (long long)(h[j] / p->lay.P));
-    }
-  }
-  return HC_OK;
-}
-
-void emit_region(hc_pool* p, uint8_t* dst, const uint8_t* src, int64_t len) {
-  if (!p->regions.empty()) {
-    Region& r = p->regions.back();
-    if (r.dst + r.len == dst && r.src + r.len == src) {
-      r.len += len;
-      return;
-    }
-  }
-  p->regions.push_back({dst, src, len});
-}
-
-// Staged plan: chunks of at most chunk_pages staging slots walked in list order.
-// Writes srow (int32 per token), ztok (tokens of partially named pages) and pads
-// (pages whose shard pad the zero-copy pass must clear) into the pinned plan buffer.
-void plan_staged(hc_pool* p, const int64_t* h, int64_t n, int32_t* srow, int32_t* ztok, int64_t* nz,
-                 int64_t* pads, int64_t* npads) {
-  const Layout& L = p->lay;
-  const int64_t C = p->chunk_pages;
-  p->regions.clear();
-  p->chunks.clear();
-  p->slot_page.assign((size_t)C, -1);
-  p->slot_rows.assign((size_t)C, 0);
-  int64_t nslots = 0, t0 = 0;
-  *nz = 0;
-  *npads = 0;
-  auto close_chunk = [&](int64_t t1) {
-    const size_t r0 = p->regions.size();
-    for (int64_t s = 0; s < nslots; s++) {
-      const int64_t page = p->slot_page[(size_t)s];
-      if (p->slot_rows[(size_t)s] == L.P) {
-        const uint8_t* img = p->staging + s * L.stride;
-        if (L.layout == HC_LAYOUT_KV_SPLIT_SHARD) {
-          emit_region(p, p->host + page * L.stride, img, L.stride);
-        } else {
-          for (int b = 0; b < L.nsub; b++)
-            emit_region(p, p->host + L.host_region[b] + page * L.subpage[b], img + L.img_off[b], L.subpage[b]);
-        }
-      } else if (L.layout == HC_LAYOUT_KV_SPLIT_SHARD && L.stride > L.payload) {
-        pads[(*npads)++] = page;
-      }
-      p->page_slot[(size_t)page] = -1;
-    }
-    for (int64_t i = t0; i < t1; i++) {
-      const int32_t s = srow[i] / L.P;
-      if (p->slot_rows[(size_t)s] != L.P) {
-        srow[i] = -1;
-        ztok[(*nz)++] = (int32_t)i;
-      }
-    }
-    p->chunks.push_back({t0, t1, r0, p->regions.size()});
-    t0 = t1;
-    nslots = 0;
-  };
-  for (int64_t i = 0; i < n; i++) {
-    const int64_t page = h[i] / L.P;
-    const int32_t r = (int32_t)(h[i] - page * L.P);
-    int32_t s = p->page_slot[(size_t)page];
-    if (s < 0) {
-      if (nslots == C) close_chunk(i);
-      s = (int32_t)nslots++;
-      p->page_slot[(size_t)page] = s;
-      p->slot_page[(size_t)s] = page;
-      p->slot_rows[(size_t)s] = 0;
-    }
-    p->slot_rows[(size_t)s]++;
-    srow[i] = s * L.P + r;
-  }
-  close_chunk(n);
-}
-
-// Distinct pages named by h (shard pads for the zero-copy write-back).
-int64_t distinct_pages(hc_pool* p, const int64_t* h, int64_t n, int64_t* pages) {
-  int64_t k = 0;
-  for (int64_t i = 0; i < n; i++) {
-    const int64_t page = h[i] / p->lay.P;
-    if (!test_and_set(p->page_seen, page)) pages[k++] = page;
-  }
-  for (int64_t j = 0; j < k; j++) clear_bit(p->page_seen, pages[j]);
-  return k;
-}
 
 int record_event(void* ev, hipStream_t s) {
   if (!ev) return HC_OK;
@@ -607,9 +461,7 @@ int hc_pool_create(const hc_pool_desc* desc, hc_pool** out) {
       return bail(set_err(HC_ERR_HIP, "staging clear failed"));
   }
   if (hipStreamSynchronize(p->stream) != hipSuccess) return bail(set_err(HC_ERR_HIP, "stream sync failed"));
-  p->page_slot.assign((size_t)L.H, -1);
-  p->seen.assign((size_t)((L.H * L.P + 63) / 64), 0);
-  p->page_seen.assign((size_t)((L.H + 63) / 64), 0);
+  p->planner.reset(L);
   fill_geom(p);
   *out = p;
   return HC_OK;
@@ -681,8 +533,11 @@ int hc_write_back_all_layers(hc_pool* p, const int64_t* device_idx, const int64_
   if (n == 0) return finish(HC_OK);
   if (!device_idx || !host_idx) return finish(set_err(HC_ERR_INVALID, "null index list"));
   if (n >= ((int64_t)1 << 31)) return finish(set_err(HC_ERR_INVALID, "n must be below 2^31"));
-  rc = validate_host_idx(p, host_idx, n);
-  if (rc != HC_OK) return finish(rc);
+  {
+    char msg[256];
+    rc = p->planner.validate(host_idx, n, msg, sizeof(msg));
+    if (rc != HC_OK) return finish(set_err(rc, "%s", msg));
+  }
   const Layout& L = p->lay;
   const bool staged = p->wb_mode == HC_MODE_STAGED;
   // plan buffer layout: hidx int64[n] | pads int64[n] | srow int32[n] | ztok int32[n]
@@ -701,9 +556,9 @@ int hc_write_back_all_layers(hc_pool* p, const int64_t* device_idx, const int64_
   memcpy(hidx, host_idx, (size_t)(8 * n));
   int64_t nz = 0, npads = 0;
   if (staged) {
-    plan_staged(p, host_idx, n, srow, ztok, &nz, pads, &npads);
+    p->planner.plan_staged(host_idx, n, p->chunk_pages, p->host, p->staging, srow, ztok, &nz, pads, &npads);
   } else if (L.layout == HC_LAYOUT_KV_SPLIT_SHARD && L.stride > L.payload) {
-    npads = distinct_pages(p, host_idx, n, pads);
+    npads = p->planner.distinct_pages(host_idx, n, pads);
   }
   const int64_t upload = staged ? bytes : align16(o_pads + 8 * npads);
   rc = plan_upload(p, upload);
@@ -715,7 +570,7 @@ int hc_write_back_all_layers(hc_pool* p, const int64_t* device_idx, const int64_
   p->plan_cur ^= 1;
   hipError_t e = hipSuccess;
   if (staged) {
-    for (const Chunk& c : p->chunks) {
+    for (const hc::Chunk& c : p->planner.chunks) {
       {
         // Recorded events, not launch-stamped ones: right after a launch-stamped kernel the
         // runtime ran the region copies below as blit kernels on the CUs instead of on the
@@ -732,7 +587,7 @@ int hc_write_back_all_layers(hc_pool* p, const int64_t* device_idx, const int64_
         Timer t(p, 5);
         t.record_start();
         for (size_t r = c.r0; r < c.r1 && e == hipSuccess; r++) {
-          const Region& g = p->regions[r];
+          const hc::Region& g = p->planner.regions[r];
           e = hipMemcpyAsync(g.dst, g.src, (size_t)g.len, hipMemcpyDeviceToHost, p->stream);
         }
         t.record_stop();

@@ -1,8 +1,9 @@
 """Builds the plain-C programs that call libhc.so through include/hc.h.
 
 abi_cpu: gcc, host only.  gpu_roundtrip: gcc against the HIP runtime API and the
-C oracle.  sanitize_host_{tsan,asan}: the loader and host-to-host sources built with
-g++ under a sanitizer (host code only).  Binaries land next to their sources
+C oracle.  sanitize_host_{tsan,asan}: the loader and host-to-host sources built under
+a sanitizer; plan_host_asan: the write-back planner under ASan + UBSan (host code
+only).  Binaries land next to their sources
 (git-ignored)."""
 import os
 import subprocess
@@ -35,7 +36,8 @@ SANITIZERS = {
     "tsan": ["-fsanitize=thread"],
     "asan": ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer"],
 }
-HOST_SOURCES = ["hc_loader.cpp", "hc_h2h.cpp", "hc_layout.cpp"]
+HOST_SOURCES = {"sanitize_host": ["hc_loader.cpp", "hc_h2h.cpp", "hc_layout.cpp"],
+                "plan_host": ["hc_plan.cpp", "hc_layout.cpp"]}
 
 
 # ThreadSanitizer comes from ROCm's clang: its runtime intercepts pthread_cond_clockwait,
@@ -44,16 +46,16 @@ HOST_SOURCES = ["hc_loader.cpp", "hc_h2h.cpp", "hc_layout.cpp"]
 COMPILERS = {"tsan": os.path.join(ROCM, "llvm", "bin", "clang++"), "asan": "g++"}
 
 
-def build_sanitized(kind: str) -> str:
-    out = os.path.join(HERE, f"sanitize_host_{kind}")
+def build_sanitized(kind: str, program: str = "sanitize_host") -> str:
+    out = os.path.join(HERE, f"{program}_{kind}")
     csrc = os.path.join(PKG, "csrc")
     cmd = [COMPILERS[kind], "-std=c++17", "-g", "-O1", "-pthread", "-Wall", *SANITIZERS[kind],
            "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"), "-I", csrc,
-           "-I", os.path.join(ROCM, "include"), os.path.join(HERE, "sanitize_host.cpp"),
-           *[os.path.join(csrc, s) for s in HOST_SOURCES], "-o", out]
+           "-I", os.path.join(ROCM, "include"), os.path.join(HERE, program + ".cpp"),
+           *[os.path.join(csrc, s) for s in HOST_SOURCES[program]], "-o", out]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError(f"building sanitize_host ({kind}) failed:\n{r.stderr}")
+        raise RuntimeError(f"building {program} ({kind}) failed:\n{r.stderr}")
     return out
 
 

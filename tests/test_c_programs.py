@@ -32,6 +32,16 @@ def test_host_machinery_under_sanitizers(kind, banner):
     assert "runtime error" not in r.stderr
 
 
+def test_write_back_planner_under_sanitizers():
+    """The staged write-back planner, executed on host buffers by a model of the device
+    side for 1200 random lists, layouts and chunk sizes, under ASan + UBSan."""
+    exe = cbuild.build_sanitized("asan", "plan_host")
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1", UBSAN_OPTIONS="halt_on_error=1 print_stacktrace=1")
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=300, env=env)
+    assert r.returncode == 0, r.stderr[-4000:]
+    assert "plan_host ok" in r.stdout and "runtime error" not in r.stderr
+
+
 @pytest.mark.gpu
 def test_c_program_round_trip_on_gpu():
     exe = os.path.join(HERE, "c", "gpu_roundtrip")

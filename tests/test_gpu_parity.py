@@ -211,3 +211,31 @@ def test_auto_mode_stages_write_back_when_staging_is_given(staging_pages, want):
         load_back_and_check(rig, h, fresh(shape, d, 4))
     finally:
         rig.close()
+
+
+# A chunk's last whole page and the next chunk's first whole page sit in consecutive
+# staging slots and on consecutive host pages, with partly named pages between them:
+# their copy-engine regions are adjacent on both sides but must stay separate, because
+# the second page's image is gathered only with the second chunk.
+MERGE_SHAPES = [
+    S("merge_shards", 2, 8, [(T, 64), (T, 64)], 4096, 32, SH, 256),
+    S("merge_shards_pad", 2, 8, [(T, 64), (T, 48)], 4096, 32, SH, 4096),
+    S("merge_one_sub", 2, 8, [(T, 64)], 4096, 32),
+]
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("shape", MERGE_SHAPES, ids=lambda s: s.name)
+def test_staged_regions_stay_inside_their_chunk(shape):
+    say(f"[chunks] adjacent regions across chunks {shape.name}")
+    P = shape.page_size
+    whole = lambda p: list(range(p * P, (p + 1) * P))
+    h = np.array(whole(5) + [20 * P + r for r in range(3)] + [9 * P + r for r in range(2)] + whole(6), dtype=np.int64)
+    d = W.permutation_slots(3, shape.device_slots, h.size)
+    rig = Rig(shape, seed=21, write_back_mode=B.HC_MODE_STAGED, staging_pages=2)
+    try:
+        for _ in range(2):  # the second burst finds the staging slots holding the first one's images
+            write_back_and_check(rig, d, h)
+            d = W.permutation_slots(4, shape.device_slots, h.size)
+    finally:
+        rig.close()
