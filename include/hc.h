@@ -49,10 +49,13 @@
  *     before the call (event record + hipStreamWaitEvent on the copy stream).
  *   - Indices are int64 token indices.  Device and host indices are each
  *     distinct and in range; with page-block sub-buffers every page named is
- *     named whole and maps row by row onto one whole device page.  Transfer
- *     calls trust device-resident indices (as copy kernels do); pools created
- *     with HC_FLAG_VALIDATE check them on the device and report a violation as
- *     HC_ERR_DEVICE at the next hc_round_trip_check or hc_pool_sync.
+ *     named whole and maps row by row onto one whole device page.  A host list
+ *     read on the CPU is checked before anything is enqueued.  Device-resident
+ *     lists are read by the kernels, which range-check every index, skip an
+ *     out-of-range row and report it as HC_ERR_DEVICE at the next
+ *     hc_round_trip_check or hc_pool_sync; distinctness of device-resident lists
+ *     is trusted.  Pools created with HC_FLAG_VALIDATE also check, on the device,
+ *     that page-block rows form whole device pages (reported the same way).
  *   - Sizes: elem_bytes is a multiple of 16 (16-byte vectors, the element-size
  *     rule of the hybrid-pool write-back page) and at most 65536; every device
  *     layer pointer, the host pool and the staging buffer are 16-byte aligned.
@@ -155,9 +158,9 @@ int hc_host_offset(const hc_pool_desc* desc, int32_t sub, int64_t page, int32_t 
 
 /* ---------------------------------------------------------------- pinned host memory */
 
-/* Page-locked host allocation through hipHostMalloc (device-mapped, NUMA node of
- * the current device).  flags: 0 = coherent, 1 = non-coherent.  The memory is
- * zero-filled.  *out is 4096-aligned. */
+/* Page-locked host allocation through hipHostMalloc (device-mapped).  flags: 0 =
+ * coherent, 1 = non-coherent.  The memory is zero-filled (through the device
+ * mapping).  *out is 4096-aligned. */
 int hc_host_alloc(int64_t bytes, int32_t flags, void** out);
 int hc_host_free(void* ptr);
 
