@@ -179,8 +179,10 @@ int hc_pool_destroy(hc_pool* pool);
  * (HC_MODE_STAGED or HC_MODE_ZEROCOPY). */
 int hc_pool_mode(const hc_pool* pool, int32_t which, int32_t* out_mode);
 
-/* Blocks until the copy stream has drained; reports HC_ERR_DEVICE when device-side
- * validation (HC_FLAG_VALIDATE) flagged an index list since the last report. */
+/* Blocks until the copy stream has drained; reports HC_ERR_DEVICE when a kernel
+ * flagged an index list since the last report (an out-of-range index, or with
+ * HC_FLAG_VALIDATE page-block rows that do not form whole device pages); the
+ * report is cleared once returned. */
 int hc_pool_sync(hc_pool* pool);
 
 /* ---------------------------------------------------------------- transfers */
