@@ -23,7 +23,6 @@ def random_case(seed):
     H = int(rng.integers(4, 40))
     S = P * int(rng.integers(H + 8, 4 * H + 16))
     align = int(rng.choice([16, 256, 4096]))
-    shape = W.PoolShape(f"rand{seed}", L, P, tuple(subs), S, H, layout, align)
     pages = rng.choice(H, size=int(rng.integers(1, H)), replace=False)
     toks = []
     for p in pages:
@@ -33,6 +32,9 @@ def random_case(seed):
     h = np.concatenate(toks).astype(np.int64)
     if not blocks and rng.random() < 0.5:
         h = h[rng.permutation(h.size)]
+    # room for two disjoint slot sets (write-back slots and fresh load-back slots)
+    S = max(S, P * (2 * pages.size + 1))
+    shape = W.PoolShape(f"rand{seed}", L, P, tuple(subs), S, H, layout, align)
     if blocks:
         dp = rng.choice(S // P, size=pages.size, replace=False)
         d = (dp[:, None] * P + np.arange(P)[None, :]).reshape(-1).astype(np.int64)
@@ -48,7 +50,7 @@ def random_case(seed):
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("seed", range(120))
+@pytest.mark.parametrize("seed", range(600))
 def test_random_pool(seed):
     shape, d, h, d2, mode, staging_pages = random_case(seed)
     say(f"[random {seed}] L={shape.layers} P={shape.page_size} subs={shape.subs} layout={shape.layout} "
