@@ -208,6 +208,63 @@ __device__ __forceinline__ void check_page_row(int64_t i, int64_t d, int64_t h, 
   if (!ok) atomicOr(err, 2);
 }
 
+// Zero-copy units.  A sub-buffer's units walk list positions j * stride: stride 1 for
+// token rows; for page blocks, stride P when the list holds whole pages in row order
+// (the row-0 token of every page then sits at a multiple of P), so a unit carries up
+// to tile_n blocks instead of tile_n / P.  Units are sub-buffer-major (page blocks
+// first, see unit_sub); `mult` counts
+// the units per tile (the layer count for the all-layer write-back, 1 for a layer).
+__host__ __device__ __forceinline__ int64_t sub_positions(const SubGeom& s, int64_t n, int blk_stride) {
+  return s.gran == HC_PAGE_BLOCKS ? (n + blk_stride - 1) / blk_stride : n;
+}
+
+// Page blocks walked with the block stride take tile_n >> HC_BLOCK_TILE_SHIFT blocks per
+// unit (at least 1).  Measured on the 78-layer MLA + indexer load-back: a full tile of
+// 256 blocks (2.1 MiB per unit, 4 units per layer) 1.56 ms per layer, the token-strided
+// walk 1.50 ms, 64 blocks per unit 1.47 ms (99 % of the host link), 32 or 16 the same.
+#ifndef HC_BLOCK_TILE_SHIFT
+#define HC_BLOCK_TILE_SHIFT 2
+#endif
+#ifndef HC_BLOCK_STRIDE_ON
+#define HC_BLOCK_STRIDE_ON 1
+#endif
+__host__ __device__ __forceinline__ int sub_tile(const SubGeom& s, int blk_stride, int tile_n) {
+  if (s.gran == HC_PAGE_BLOCKS && blk_stride > 1) {
+    const int t = tile_n >> HC_BLOCK_TILE_SHIFT;
+    return t > 0 ? t : 1;
+  }
+  return tile_n;
+}
+
+__host__ __device__ __forceinline__ int64_t sub_units(const SubGeom& s, int64_t n, int blk_stride, int tile_n,
+                                                      int64_t mult) {
+  const int t = sub_tile(s, blk_stride, tile_n);
+  return (sub_positions(s, n, blk_stride) + t - 1) / t * mult;
+}
+
+// Sub-buffer of `unit`, and the unit's index inside that sub-buffer's units.  Page-block
+// sub-buffers come first: with the block stride their units are the largest (a tile of
+// whole-page blocks), and taken last they left a few workgroups running alone at the
+// end of a layer.
+__device__ __forceinline__ int unit_sub(const Geom& g, int64_t n, int blk_stride, int tile_n, int64_t mult,
+                                        int64_t unit, int64_t* rem) {
+  int64_t acc = 0;
+  for (int pass = 0; pass < 2; pass++) {
+    for (int b = 0; b < g.nsub; b++) {
+      if ((g.sub[b].gran == HC_PAGE_BLOCKS) != (pass == 0)) continue;
+      const int64_t ub = sub_units(g.sub[b], n, blk_stride, tile_n, mult);
+      if (unit < acc + ub) {
+        *rem = unit - acc;
+        return b;
+      }
+      acc += ub;
+    }
+  }
+  // not reached for unit < units; a position past sub-buffer 0's last leaves every lane idle
+  *rem = sub_units(g.sub[0], n, blk_stride, tile_n, mult);
+  return 0;
+}
+
 // ---------------------------------------------------------------- staged write-back: gather
 // Units of (sub-buffer, kGatherTile tokens of [t0, t0+count), layer), walked grid-stride
 // by a grid of a few workgroups per CU: small units keep every CU streaming until the
@@ -268,28 +325,29 @@ __global__ __launch_bounds__(kThreads) void k_gather_stage(Geom g, const int64_t
 // ---------------------------------------------------------------- zero-copy write-back
 // Device rows -> pinned host pool.  Tokens are [0, count) or tok_list[0, count).
 // Units (sub, tile, layer) are walked grid-stride so a capped grid suffices.
-// Tiles hold kTile >> tile_shift tokens.
+// Tiles hold kTile >> tile_shift list positions (see sub_units for page blocks).
 __global__ __launch_bounds__(kThreads) void k_zc_write(Geom g, const int64_t* __restrict__ dev_idx,
                                                        const int64_t* __restrict__ host_idx,
                                                        const int32_t* __restrict__ tok_list, int64_t count,
                                                        uint8_t* __restrict__ host, int32_t* __restrict__ err,
-                                                       int64_t units, int tile_shift) {
+                                                       int64_t units, int tile_shift, int blk_stride) {
   __shared__ uint64_t s_src[kTile];
   __shared__ uint64_t s_dst[kTile];
   __shared__ int s_wave[kWaves];
   const int tile_n = kTile >> tile_shift;
-  const int64_t per_sub = units / g.nsub;  // sub-buffer-major, as in k_gather_stage
   for (int64_t unit = blockIdx.x; unit < units; unit += gridDim.x) {
-    const int b = (int)(unit / per_sub);
-    const int64_t rem = unit - (int64_t)b * per_sub;
+    int64_t rem;
+    const int b = unit_sub(g, count, blk_stride, tile_n, g.L, unit, &rem);
     const int64_t tile = rem / g.L;
     const int l = (int)(rem - tile * g.L);
     const SubGeom& s = g.sub[b];
-    const int64_t j = tile * tile_n + threadIdx.x;
+    const int st = sub_tile(s, blk_stride, tile_n);
+    const int64_t j = tile * st + threadIdx.x;
+    const int stride = s.gran == HC_PAGE_BLOCKS ? blk_stride : 1;
     bool keep = false;
     uint64_t src = 0, dst = 0;
-    if ((int)threadIdx.x < tile_n && j < count) {
-      const int64_t i = tok_list ? (int64_t)tok_list[j] : j;
+    if ((int)threadIdx.x < st && j < sub_positions(s, count, blk_stride)) {
+      const int64_t i = tok_list ? (int64_t)tok_list[j] : j * stride;
       const int64_t d = dev_idx[i];
       const int64_t h = host_idx[i];
       const int64_t p = h / g.P;
@@ -322,25 +380,26 @@ __global__ __launch_bounds__(kThreads) void k_zc_write(Geom g, const int64_t* __
 // Units (sub, tile) grid-stride.  With g.validate, page-block sub-buffers also check
 // that each page's rows arrive as one run of P consecutive device slots starting on a
 // page boundary (neighbour compare through a lane shuffle, LDS at wave edges).
-// Tiles hold kTile >> tile_shift tokens, as in k_zc_write.
+// Tiles hold kTile >> tile_shift list positions, as in k_zc_write.
 __global__ __launch_bounds__(kThreads) void k_zc_read(Geom g, int32_t layer, const int64_t* __restrict__ host_idx,
                                                       const int64_t* __restrict__ dev_idx, int64_t n,
                                                       const uint8_t* __restrict__ host, int32_t* __restrict__ err,
-                                                      int64_t units, int tile_shift) {
+                                                      int64_t units, int tile_shift, int blk_stride) {
   __shared__ uint64_t s_src[kTile];
   __shared__ uint64_t s_dst[kTile];
   __shared__ int s_wave[kWaves];
   const int tile_n = kTile >> tile_shift;
-  const int64_t per_sub = units / g.nsub;  // sub-buffer-major, as in k_gather_stage
   for (int64_t unit = blockIdx.x; unit < units; unit += gridDim.x) {
-    const int b = (int)(unit / per_sub);
-    const int64_t tile = unit - (int64_t)b * per_sub;
+    int64_t tile;
+    const int b = unit_sub(g, n, blk_stride, tile_n, 1, unit, &tile);
     const SubGeom& s = g.sub[b];
-    const int64_t i = tile * tile_n + threadIdx.x;
+    const int st = sub_tile(s, blk_stride, tile_n);
+    const int64_t j = tile * st + threadIdx.x;
+    const int64_t i = j * (s.gran == HC_PAGE_BLOCKS ? blk_stride : 1);
     bool keep = false;
     uint64_t src = 0, dst = 0;
     int64_t d = 0, h = 0;
-    const bool live = (int)threadIdx.x < tile_n && i < n;
+    const bool live = (int)threadIdx.x < st && j < sub_positions(s, n, blk_stride);
     if (live) {
       d = dev_idx[i];
       h = host_idx[i];
@@ -475,38 +534,55 @@ hipError_t launch_gather_stage(const Geom& g, const int64_t* dev_idx, const int6
                 units);
 }
 
-// Tile shift for a zero-copy launch over `count` tokens with `per_tile` units per
-// tile: the smallest shift (at most kMaxTileShift, i.e. 4-token tiles) whose
-// kTile >> shift token tiles give at least `max_ctas` units.
+// Units of a zero-copy launch over list positions [0, count): summed over sub-buffers.
+static int64_t zc_units(const Geom& g, int64_t count, int blk_stride, int tile_n, int64_t mult) {
+  int64_t units = 0;
+  for (int b = 0; b < g.nsub; b++) units += sub_units(g.sub[b], count, blk_stride, tile_n, mult);
+  return units;
+}
+
+// Tile shift: the smallest (at most kMaxTileShift, i.e. 4-position tiles) whose
+// kTile >> shift tiles give at least `max_ctas` units.
 constexpr int kMaxTileShift = 6;
 
-static int tile_shift_for(int64_t count, int64_t per_tile, int32_t max_ctas) {
+static int tile_shift_for(const Geom& g, int64_t count, int blk_stride, int64_t mult, int32_t max_ctas) {
   int shift = 0;
-  while (shift < kMaxTileShift && ceil_div(count, kTile >> shift) * per_tile < (int64_t)max_ctas) shift++;
+  while (shift < kMaxTileShift && zc_units(g, count, blk_stride, kTile >> shift, mult) < (int64_t)max_ctas) shift++;
   return shift;
+}
+
+// Page blocks take only the positions k * P when the list is known to hold whole pages
+// in row order: always by contract without HC_FLAG_VALIDATE (with it, every position
+// is visited so the order can be checked), never for a token sub-list.
+static int block_stride(const Geom& g, bool full_list) {
+  if (!HC_BLOCK_STRIDE_ON || g.validate || !full_list) return 1;
+  for (int b = 0; b < g.nsub; b++)
+    if (g.sub[b].gran == HC_PAGE_BLOCKS) return g.P;
+  return 1;
 }
 
 hipError_t launch_zc_write(const Geom& g, const int64_t* dev_idx, const int64_t* host_idx, const int32_t* tok_list,
                            int64_t count, uint8_t* host, int32_t* err, int32_t max_ctas, const LaunchTimer& t,
                            hipStream_t stream) {
   if (count <= 0) return hipSuccess;
-  const int64_t per_tile = (int64_t)g.L * g.nsub;
-  const int shift = tile_shift_for(count, per_tile, max_ctas);
-  const int64_t units = ceil_div(count, kTile >> shift) * per_tile;
+  const int bs = block_stride(g, tok_list == nullptr);
+  const int shift = tile_shift_for(g, count, bs, g.L, max_ctas);
+  const int64_t units = zc_units(g, count, bs, kTile >> shift, g.L);
   const int64_t grid = units < max_ctas ? units : max_ctas;
   return launch(k_zc_write, dim3((unsigned)grid), t, stream, g, dev_idx, host_idx, tok_list, count, host, err, units,
-                shift);
+                shift, bs);
 }
 
 hipError_t launch_zc_read(const Geom& g, int32_t layer, const int64_t* host_idx, const int64_t* dev_idx, int64_t n,
                           const uint8_t* host, int32_t* err, int32_t max_ctas, const LaunchTimer& t,
                           hipStream_t stream) {
   if (n <= 0) return hipSuccess;
-  const int64_t per_tile = g.nsub;
-  const int shift = tile_shift_for(n, per_tile, max_ctas);
-  const int64_t units = ceil_div(n, kTile >> shift) * per_tile;
+  const int bs = block_stride(g, true);
+  const int shift = tile_shift_for(g, n, bs, 1, max_ctas);
+  const int64_t units = zc_units(g, n, bs, kTile >> shift, 1);
   const int64_t grid = units < max_ctas ? units : max_ctas;
-  return launch(k_zc_read, dim3((unsigned)grid), t, stream, g, layer, host_idx, dev_idx, n, host, err, units, shift);
+  return launch(k_zc_read, dim3((unsigned)grid), t, stream, g, layer, host_idx, dev_idx, n, host, err, units, shift,
+                bs);
 }
 
 hipError_t launch_zero_pads(uint8_t* base, const int64_t* pages, int64_t npages, int64_t stride, int64_t off,

@@ -49,7 +49,9 @@
  *     before the call (event record + hipStreamWaitEvent on the copy stream).
  *   - Indices are int64 token indices.  Device and host indices are each
  *     distinct and in range; with page-block sub-buffers every page named is
- *     named whole and maps row by row onto one whole device page.  A host list
+ *     named whole, as P consecutive list entries in row order (rows 0..P-1)
+ *     that map onto one whole device page the same way, so the row-0 tokens sit
+ *     at list positions k * P.  A host list
  *     read on the CPU is checked before anything is enqueued.  Device-resident
  *     lists are read by the kernels, which range-check every index, skip an
  *     out-of-range row and report it as HC_ERR_DEVICE at the next
