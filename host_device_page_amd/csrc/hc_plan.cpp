@@ -48,6 +48,18 @@ int Planner::validate(const int64_t* h, int64_t n, char* msg, size_t msg_len) {
     return HC_ERR_INVALID;
   }
   if (lay_.has_blocks) {
+    // every named page as P consecutive entries in row order (the kernels find a page's
+    // block at the list position of its row 0, a multiple of P)
+    for (int64_t j = 0; j < n; j++) {
+      const bool ok = (j % lay_.P == 0) ? (h[j] % lay_.P == 0) : (h[j] == h[j - 1] + 1);
+      if (!ok) {
+        snprintf(msg, msg_len,
+                 "host_idx[%lld] = %lld: with page-block sub-buffers the list names whole pages, each as %d "
+                 "consecutive entries in row order",
+                 (long long)j, (long long)h[j], lay_.P);
+        return HC_ERR_INVALID;
+      }
+    }
     // every named page whole: count rows per page
     int rc = HC_OK;
     for (int64_t j = 0; j < n; j++) page_rows_[(size_t)(h[j] / lay_.P)]++;

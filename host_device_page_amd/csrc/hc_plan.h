@@ -32,8 +32,8 @@ class Planner {
   void reset(const Layout& lay);
 
   // Range and distinctness of the host token list, and, with page-block
-  // sub-buffers, that every named page is named whole.  HC_OK, or HC_ERR_INVALID
-  // with a message in msg.
+  // sub-buffers, that the list is whole pages, each as P consecutive entries in row
+  // order.  HC_OK, or HC_ERR_INVALID with a message in msg.
   int validate(const int64_t* host_idx, int64_t n, char* msg, size_t msg_len);
 
   // Staged plan: the list in order, cut into chunks of at most chunk_pages staging

@@ -216,6 +216,10 @@ static void validate_rejects() {
   CHECK(pl.validate(h.data(), (int64_t)h.size(), msg, sizeof(msg)) == HC_ERR_INVALID && strstr(msg, "partially"));
   h.push_back(11);  // and whole again: the scratch of the failed calls was cleared
   CHECK(pl.validate(h.data(), (int64_t)h.size(), msg, sizeof(msg)) == HC_OK);
+  std::vector<int64_t> swapped = {0, 2, 1, 3, 8, 9, 10, 11};  // whole pages, rows out of order
+  CHECK(pl.validate(swapped.data(), 8, msg, sizeof(msg)) == HC_ERR_INVALID && strstr(msg, "row order"));
+  std::vector<int64_t> interleaved = {0, 1, 8, 9, 2, 3, 10, 11};  // whole pages, interleaved
+  CHECK(pl.validate(interleaved.data(), 8, msg, sizeof(msg)) == HC_ERR_INVALID && strstr(msg, "row order"));
   std::vector<int64_t> neg = {-1};
   CHECK(pl.validate(neg.data(), 1, msg, sizeof(msg)) == HC_ERR_INVALID);
 }

@@ -13,7 +13,7 @@ import torch
 
 from host_device_page_amd import binding as B
 from host_device_page_amd import workloads as W
-from gpu_support import Rig, cuda_i64, say
+from gpu_support import Rig, cuda_i64, say, write_back_and_check
 from oracle import oracle as O
 
 T, BLK = W.TOKEN_ROWS, W.PAGE_BLOCKS
@@ -253,5 +253,29 @@ def test_validate_flag_reports_misaligned_page_blocks_on_write_back(mode):
         with pytest.raises(B.HcError) as e:
             rig.pool.sync()
         assert e.value.code == B.HC_ERR_DEVICE and "page-block" in str(e.value)
+    finally:
+        rig.close()
+
+
+@pytest.mark.gpu
+def test_block_pool_write_back_rejects_out_of_order_pages():
+    """Whole pages whose rows are interleaved or out of order are refused on the CPU,
+    before anything is enqueued: the kernels find a page's block at its row-0 position."""
+    say("[events] page-block write-back, rows out of order")
+    rig = Rig(BLOCKS, seed=16)
+    try:
+        P = BLOCKS.page_size
+        pages = W.host_pages(5, BLOCKS.host_pages, 3)
+        h = W.whole_page_tokens(pages, P)
+        d = W.page_aligned_slots(6, BLOCKS.device_slots, P, 3)
+        host_before = rig.host.np.copy()
+        inter = np.concatenate([h[:P // 2], h[P:P + P // 2], h[P // 2:P], h[P + P // 2:2 * P], h[2 * P:]])
+        for bad in (inter, np.concatenate([h[1:2], h[0:1], h[2:]])):
+            with pytest.raises(B.HcError) as e:
+                rig.pool.write_back_all_layers(cuda_i64(d), bad)
+            assert e.value.code == B.HC_ERR_INVALID and "row order" in str(e.value)
+        rig.pool.sync()
+        assert np.array_equal(rig.host.np, host_before)
+        write_back_and_check(rig, d, h)  # the same pages in order go through
     finally:
         rig.close()
