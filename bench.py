@@ -58,6 +58,9 @@ def parse():
     ap.add_argument("--sweep", action="store_true",
                     help="instead: write-back and per-layer load-back time against burst size (prefixes of "
                          "the workload's burst, 1 page up to all of it)")
+    ap.add_argument("--beside-compute", action="store_true",
+                    help="instead: only the write-back burst next to independent matmuls, zero-copy and staged "
+                         "(for a kernel and memory-copy trace)")
     ap.add_argument("--h2h", action="store_true",
                     help="instead: time host-to-host shard dump/load of the shard workload with 1..16 CPU workers")
     ap.add_argument("--max-pinned-gib", type=float, default=64.0,
@@ -514,6 +517,16 @@ def main():
     torch.cuda.synchronize()
     log(f"[bench] setup {time.perf_counter() - t_setup:.1f} s; burst {burst.n} tokens, {burst.pages.size} pages; "
         f"write-back mode {pool.mode(0)} (1 staged, 2 zero-copy), load-back mode {pool.mode(1)}")
+    if args.beside_compute:
+        pool.close()
+        pools = {"zerocopy": make_pool(B.HC_MODE_ZEROCOPY, flags=0), "staged": make_pool(B.HC_MODE_STAGED, flags=0)}
+        res = write_back_overlap(B, torch, np, pools, d_t, h_np)
+        for p in pools.values():
+            p.close()
+        print(json.dumps({"beside_compute": res, "workload": shape.name,
+                          "burst_bytes_each_way": burst_bytes(shape, burst)[0]}), flush=True)
+        host.free()
+        return
     if args.sweep:
         # no per-launch timing events here: at small bursts their cost (~9 us per launch) would dominate
         pool.close()
