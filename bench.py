@@ -634,6 +634,20 @@ def main():
             bu.release()
         ld.close()
         handover["loader_thread" if asynchronous else "inline"] = round(1e3 * float(np.median(times)), 4)
+    # the same burst captured once and handed to the loader thread as a replay
+    g_events = [B.HipEvent() for _ in range(L)]
+    cap = hpool.capture_load_back(h_t, d2_t, g_events)
+    ld = B.Loader(hpool, L, asynchronous=True)
+    times = []
+    for _ in range(5):
+        t_s = time.perf_counter()
+        bu = ld.submit_graph(cap, g_events)
+        times.append(time.perf_counter() - t_s)
+        bu.wait()
+        bu.release()
+    ld.close()
+    cap.close()
+    handover["loader_thread_captured"] = round(1e3 * float(np.median(times)), 4)
     graph = load_back_graph_timing(B, np, hpool, stream, L, h_t, d2_t, link_bytes)
     log(f"[bench] captured load-back burst: {graph}")
     hpool.close()

@@ -74,12 +74,13 @@ WAIT_EVENT_FN = ctypes.CFUNCTYPE(ctypes.c_int, _V, _V)
 RECORD_EVENT_FN = ctypes.CFUNCTYPE(ctypes.c_int, _V, _V)
 SYNC_EVENT_FN = ctypes.CFUNCTYPE(ctypes.c_int, _V, _V)
 STREAM_WAIT_FN = ctypes.CFUNCTYPE(ctypes.c_int, _V, _V, _V)
+LAUNCH_GRAPH_FN = ctypes.CFUNCTYPE(ctypes.c_int, _V, _V)
 
 
 class hc_loader_ops(ctypes.Structure):
     _fields_ = [("ctx", _V), ("load_layer", LOAD_LAYER_FN), ("wait_event", WAIT_EVENT_FN),
                 ("record_event", RECORD_EVENT_FN), ("sync_event", SYNC_EVENT_FN),
-                ("stream_wait", STREAM_WAIT_FN)]
+                ("stream_wait", STREAM_WAIT_FN), ("launch_graph", LAUNCH_GRAPH_FN)]
 _I64P = ctypes.POINTER(ctypes.c_int64)
 _SIGS = {
     "hc_desc_check": (ctypes.c_int, [_D]),
@@ -104,6 +105,7 @@ _SIGS = {
     "hc_loader_create": (ctypes.c_int, [_V, ctypes.POINTER(hc_loader_ops), ctypes.c_int32, ctypes.c_int32,
                                         ctypes.POINTER(_V)]),
     "hc_loader_submit": (ctypes.c_int, [_V, _V, _V, ctypes.c_int64, ctypes.POINTER(_V), _V, ctypes.POINTER(_V)]),
+    "hc_loader_submit_graph": (ctypes.c_int, [_V, _V, ctypes.POINTER(_V), _V, ctypes.POINTER(_V)]),
     "hc_burst_wait_layer": (ctypes.c_int, [_V, ctypes.c_int32, _V]),
     "hc_burst_wait": (ctypes.c_int, [_V]),
     "hc_burst_query": (ctypes.c_int, [_V, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]),
@@ -447,6 +449,20 @@ class Loader:
         check(lib.hc_loader_submit(self.handle, _V(_ptr(host_idx)), _V(_ptr(device_idx)), n, arr,
                                    _V(st) if st else None, ctypes.byref(out)), "hc_loader_submit")
         b = Burst(out, (host_idx, device_idx, arr, layer_events, start_event), self)
+        self._bursts.add(b)
+        return b
+
+    def submit_graph(self, graph, layer_events, start_event=None) -> Burst:
+        """graph: a LoadBackGraph of this loader's pool (or a raw handle for custom ops);
+        layer_events: the events it was captured with, in layer order."""
+        raw = [e.handle.value if isinstance(e, HipEvent) else int(e) for e in layer_events]
+        arr = (_V * len(raw))(*raw)
+        st = start_event.handle.value if isinstance(start_event, HipEvent) else start_event
+        gh = graph.handle if isinstance(graph, LoadBackGraph) else _V(graph)
+        out = _V()
+        check(lib.hc_loader_submit_graph(self.handle, gh, arr, _V(st) if st else None, ctypes.byref(out)),
+              "hc_loader_submit_graph")
+        b = Burst(out, (graph, arr, layer_events, start_event), self)
         self._bursts.add(b)
         return b
 

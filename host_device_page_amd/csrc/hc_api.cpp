@@ -801,6 +801,12 @@ int op_stream_wait(void*, void* stream, void* ev) {
   return HC_OK;
 }
 
+int op_launch_graph(void* ctx, void* graph) {
+  hc_lb_graph* g = (hc_lb_graph*)graph;
+  if (g->pool != (hc_pool*)ctx) return set_err(HC_ERR_INVALID, "the graph was captured on another pool");
+  return hc_load_back_graph_launch(g);
+}
+
 }  // namespace
 
 namespace hc {
@@ -820,6 +826,7 @@ void pool_loader_ops(hc_pool* pool, hc_loader_ops* ops) {
   ops->record_event = op_record_event;
   ops->sync_event = op_sync_event;
   ops->stream_wait = op_stream_wait;
+  ops->launch_graph = op_launch_graph;
 }
 
 int pool_layers(const hc_pool* pool) { return pool->lay.L; }

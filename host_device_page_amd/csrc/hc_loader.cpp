@@ -27,6 +27,7 @@ struct hc_burst {
   int64_t n = 0;
   std::vector<void*> events;
   void* start_event = nullptr;
+  void* graph = nullptr;  // a captured burst to replay instead of per-layer enqueues
   // guarded by loader->mu
   int32_t flagged = 0;  // layers [0, flagged) have their event recorded
   bool done = false;    // every layer flagged (enqueue finished or failed)
@@ -65,7 +66,15 @@ void run_burst(hc_loader* ld, hc_burst* b) {
   int st = HC_OK;
   if (b->start_event) st = ld->ops.wait_event(ctx, b->start_event);
   int32_t l = 0;
-  for (; st == HC_OK && l < ld->L; l++) {
+  if (b->graph) {
+    // one replay enqueues and records every layer
+    if (st == HC_OK) st = ld->ops.launch_graph(ctx, b->graph);
+    if (st == HC_OK) {
+      l = ld->L;
+      flag_layers(ld, b, l);
+    }
+  }
+  for (; !b->graph && st == HC_OK && l < ld->L; l++) {
     st = ld->ops.load_layer(ctx, l, b->host_idx, b->device_idx, b->n, b->events[(size_t)l]);
     if (st != HC_OK) break;
     flag_layers(ld, b, l + 1);
@@ -147,11 +156,35 @@ int hc_loader_create(hc_pool* pool, const hc_loader_ops* ops, int32_t num_layers
   return HC_OK;
 }
 
+namespace {
+
+int submit_burst(hc_loader* ld, const int64_t* host_idx, const int64_t* device_idx, int64_t n, void* graph,
+                 void* const* layer_events, void* start_event, hc_burst** out);
+
+}  // namespace
+
 int hc_loader_submit(hc_loader* ld, const int64_t* host_idx, const int64_t* device_idx, int64_t n,
                      void* const* layer_events, void* start_event, hc_burst** out) {
   if (!ld || !out || !layer_events) return loader_err(HC_ERR_INVALID, "null argument");
   *out = nullptr;
   if (n < 0) return loader_err(HC_ERR_INVALID, "n must be >= 0");
+  return submit_burst(ld, host_idx, device_idx, n, nullptr, layer_events, start_event, out);
+}
+
+int hc_loader_submit_graph(hc_loader* ld, void* graph, void* const* layer_events, void* start_event,
+                           hc_burst** out) {
+  if (!ld || !out || !layer_events || !graph) return loader_err(HC_ERR_INVALID, "null argument");
+  *out = nullptr;
+  if (!ld->ops.launch_graph) return loader_err(HC_ERR_UNSUPPORTED, "the loader's ops cannot launch a graph");
+  return submit_burst(ld, nullptr, nullptr, 0, graph, layer_events, start_event, out);
+}
+
+}  // extern "C"
+
+namespace {
+
+int submit_burst(hc_loader* ld, const int64_t* host_idx, const int64_t* device_idx, int64_t n, void* graph,
+                 void* const* layer_events, void* start_event, hc_burst** out) {
   std::vector<void*> evs(layer_events, layer_events + ld->L);
   for (size_t i = 0; i < evs.size(); i++) {
     if (!evs[i]) return loader_err(HC_ERR_INVALID, "null layer event");
@@ -164,6 +197,7 @@ int hc_loader_submit(hc_loader* ld, const int64_t* host_idx, const int64_t* devi
   b->host_idx = host_idx;
   b->device_idx = device_idx;
   b->n = n;
+  b->graph = graph;
   b->events = std::move(evs);
   b->start_event = start_event;
   {
@@ -185,6 +219,10 @@ int hc_loader_submit(hc_loader* ld, const int64_t* host_idx, const int64_t* devi
   *out = b;
   return HC_OK;
 }
+
+}  // namespace
+
+extern "C" {
 
 int hc_burst_wait_layer(hc_burst* b, int32_t layer, void* consumer_stream) {
   if (!b) return loader_err(HC_ERR_INVALID, "burst is null");

@@ -286,6 +286,9 @@ typedef struct hc_loader_ops {
   int (*sync_event)(void* ctx, void* event);
   /* make `stream` wait for `event` */
   int (*stream_wait)(void* ctx, void* stream, void* event);
+  /* enqueue one replay of a captured burst (hc_loader_submit_graph); may be NULL when
+   * the loader never receives one */
+  int (*launch_graph)(void* ctx, void* graph);
 } hc_loader_ops;
 
 /* async = 1: one worker thread; async = 0: hc_loader_submit runs the burst inline
@@ -299,6 +302,16 @@ int hc_loader_create(hc_pool* pool, const hc_loader_ops* ops, int32_t num_layers
  * Returns at once in async mode.  *out is released with hc_burst_release. */
 int hc_loader_submit(hc_loader* loader, const int64_t* host_idx, const int64_t* device_idx, int64_t n,
                      void* const* layer_events, void* start_event, hc_burst** out);
+/* Queue one replay of a captured load-back burst (hc_load_back_graph_create on the
+ * loader's pool, or any graph the loader's launch_graph op accepts).  layer_events:
+ * the num_layers events the graph was captured with, in layer order (the graph
+ * records them; the loader needs them for its flags and for hc_burst_wait_layer).
+ * The worker makes the transfer stream wait for start_event (if any), launches the
+ * graph and flags every layer at once; on failure it records every layer event, as
+ * hc_loader_submit does.  Bursts of both kinds share one FIFO and one event-reuse
+ * rule.  HC_ERR_UNSUPPORTED when the loader's ops have no launch_graph. */
+int hc_loader_submit_graph(hc_loader* loader, void* graph, void* const* layer_events, void* start_event,
+                           hc_burst** out);
 /* Block until layer `layer` of the burst is recorded, then make consumer_stream wait
  * on its event (consumer_stream NULL: block the calling thread until it completes). */
 int hc_burst_wait_layer(hc_burst* burst, int32_t layer, void* consumer_stream);

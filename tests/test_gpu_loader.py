@@ -120,3 +120,53 @@ def test_loader_and_caller_share_a_pool():
         if loader is not None:
             loader.close()
         rig.close()
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("asynchronous", [True, False])
+def test_loader_replays_a_captured_burst(asynchronous):
+    """Captured bursts handed to the loader: each replay follows the index buffers, a
+    consumer waits per layer through the loader, and replays queue behind eager bursts."""
+    say(f"[loader] captured bursts async={asynchronous}")
+    rig = Rig(SHAPE, seed=13)
+    loader = graph = None
+    try:
+        pages = W.host_pages(4, SHAPE.host_pages, 40)
+        h = W.whole_page_tokens(pages, SHAPE.page_size)
+        d = W.permutation_slots(5, SHAPE.device_slots, h.size)
+        rig.pool.write_back_all_layers(cuda_i64(d), h)
+        rig.pool.sync()
+        h_t = cuda_i64(h)
+        d_buf = cuda_i64(W.permutation_slots(6, SHAPE.device_slots, h.size, exclude=d))
+        events = [B.HipEvent() for _ in range(SHAPE.layers)]
+        graph = rig.pool.capture_load_back(h_t, d_buf, events)
+        loader = B.Loader(rig.pool, SHAPE.layers, asynchronous=asynchronous)
+        consumer = torch.cuda.Stream()
+        for r in range(3):
+            d2 = W.permutation_slots(10 + r, SHAPE.device_slots, h.size, exclude=d)
+            d_buf.copy_(cuda_i64(d2))
+            start = B.HipEvent()
+            start.record(torch.cuda.current_stream())  # the rewritten slot list is ready
+            burst = loader.submit_graph(graph, events, start_event=start)
+            got = []
+            for l in range(SHAPE.layers):
+                burst.wait_layer(l, consumer)
+                with torch.cuda.stream(consumer):
+                    got.append(dev_sums(rig, l, d_buf))
+            consumer.synchronize()
+            burst.wait()
+            burst.release()
+            for l in range(SHAPE.layers):
+                assert [int(x) for x in got[l]] == host_sums(rig, h, l), f"replay {r} layer {l}"
+            # an eager burst between replays, on other events
+            other = [B.HipEvent() for _ in range(SHAPE.layers)]
+            eager = loader.submit(h_t, cuda_i64(d2), h.size, other)
+            eager.wait()
+            eager.release()
+        rig.pool.sync()
+    finally:
+        if loader is not None:
+            loader.close()
+        if graph is not None:
+            graph.close()
+        rig.close()

@@ -31,9 +31,10 @@ class Fake:
         self.fail = {}      # (host_idx, layer) -> status to return
         self.ops = B.hc_loader_ops()
         self._fns = [B.LOAD_LAYER_FN(self._load), B.WAIT_EVENT_FN(self._wait), B.RECORD_EVENT_FN(self._record),
-                     B.SYNC_EVENT_FN(self._sync), B.STREAM_WAIT_FN(self._stream_wait)]
+                     B.SYNC_EVENT_FN(self._sync), B.STREAM_WAIT_FN(self._stream_wait),
+                     B.LAUNCH_GRAPH_FN(self._launch_graph)]
         (self.ops.load_layer, self.ops.wait_event, self.ops.record_event, self.ops.sync_event,
-         self.ops.stream_wait) = self._fns
+         self.ops.stream_wait, self.ops.launch_graph) = self._fns
         self.ops.ctx = None
 
     def _log(self, *c):
@@ -62,6 +63,13 @@ class Fake:
     def _stream_wait(self, ctx, stream, ev):
         self._log("stream_wait", stream, ev)
         return 0
+
+    def _launch_graph(self, ctx, graph):
+        gate = self.gates.get(("graph", graph))
+        if gate is not None:
+            assert gate.wait(10), "test gate never opened"
+        self._log("graph", graph)
+        return self.fail.get(("graph", graph), 0)
 
     def seq(self):
         with self.lock:
@@ -222,4 +230,53 @@ def test_argument_errors():
     with pytest.raises(B.HcError):
         ld.submit(0, 0, 1, [EV[0], 0, EV[2], EV[3]])
     assert B.lib.hc_burst_wait_layer(None, 0, None) == B.HC_ERR_INVALID
+    ld.close()
+
+
+def test_graph_bursts_share_the_fifo_and_flag_all_layers_at_once():
+    f = Fake()
+    gate = f.gates[("graph", 0x500)] = threading.Event()
+    ld = B.Loader(None, L, asynchronous=True, ops=f.ops)
+    g1 = ld.submit_graph(0x500, EV, start_event=0x99)
+    b2 = ld.submit(0x30, 0x40, 5, EV2)
+    time.sleep(0.05)
+    assert g1.query() == (0, False), "the graph burst was flagged before its launch"
+    gate.set()
+    g1.wait_layer(L - 1, 0x77)
+    ld.drain()
+    assert g1.query() == (L, True)
+    seq = f.seq()
+    assert seq[:2] == [("wait_start", 0x99), ("graph", 0x500)]
+    assert [c for c in seq if c[0] == "load"] == [("load", l, 0x30, 0x40, 5, EV2[l]) for l in range(L)]
+    assert seq.index(("graph", 0x500)) < seq.index(("load", 0, 0x30, 0x40, 5, EV2[0])), "FIFO order broken"
+    assert ("stream_wait", 0x77, EV[L - 1]) in seq
+    g1.release()
+    b2.release()
+    ld.close()
+
+
+def test_failed_graph_launch_completes_every_layer():
+    f = Fake()
+    f.fail[("graph", 0x600)] = B.HC_ERR_HIP
+    ld = B.Loader(None, L, asynchronous=True, ops=f.ops)
+    g = ld.submit_graph(0x600, EV)
+    with pytest.raises(B.HcError) as e:
+        g.wait()
+    assert e.value.code == B.HC_ERR_HIP
+    for l in range(L):
+        assert ("record", EV[l]) in f.seq(), f"layer {l} event not completed after the failed launch"
+    assert ld.info()[0] == 1
+    g.release()
+    ld.close()
+
+
+def test_graph_submit_needs_a_launch_op():
+    f = Fake()
+    f.ops.launch_graph = B.LAUNCH_GRAPH_FN()  # null
+    ld = B.Loader(None, L, asynchronous=False, ops=f.ops)
+    with pytest.raises(B.HcError) as e:
+        ld.submit_graph(0x700, EV)
+    assert e.value.code == B.HC_ERR_UNSUPPORTED
+    out = ctypes.c_void_p()
+    assert B.lib.hc_loader_submit_graph(None, None, None, None, ctypes.byref(out)) == B.HC_ERR_INVALID
     ld.close()
