@@ -89,6 +89,13 @@ int op_stream_wait(void*, void*, void*) {
   g_rec.stream_waits.fetch_add(1);
   return HC_OK;
 }
+// A captured burst: the graph handle is the address of its producer's event row; one
+// launch records every layer event of that row.
+int op_launch_graph(void*, void* graph) {
+  const int p = producer_of(graph);
+  for (int l = 0; l < kL; l++) g_rec.records[p][l].fetch_add(1);
+  return HC_OK;
+}
 
 void loader_stress(int async) {
   for (auto& row : g_rec.records)
@@ -99,6 +106,7 @@ void loader_stress(int async) {
   ops.record_event = op_record;
   ops.sync_event = op_sync;
   ops.stream_wait = op_stream_wait;
+  ops.launch_graph = op_launch_graph;
   hc_loader* ld = nullptr;
   CHECK(hc_loader_create(nullptr, &ops, kL, async, &ld) == HC_OK);
   std::atomic<int> failed{0};
@@ -119,14 +127,19 @@ void loader_stress(int async) {
       for (int b = 0; b < kBursts; b++) {
         hc_burst* burst = nullptr;
         const int64_t tag = (int64_t)p * 1000 + b;
-        // the same events for every burst of this producer: reuse waits for the previous one
-        CHECK(hc_loader_submit(ld, (const int64_t*)(intptr_t)tag, nullptr, 1, evs, b % 2 ? evs[0] : nullptr,
-                               &burst) == HC_OK);
+        // the same events for every burst of this producer: reuse waits for the previous one;
+        // every third burst is a captured one
+        if (b % 3 == 1) {
+          CHECK(hc_loader_submit_graph(ld, evs[0], evs, nullptr, &burst) == HC_OK);
+        } else {
+          CHECK(hc_loader_submit(ld, (const int64_t*)(intptr_t)tag, nullptr, 1, evs, b % 2 ? evs[0] : nullptr,
+                                 &burst) == HC_OK);
+        }
         for (int l = 0; l < kL; l += 3) CHECK(hc_burst_wait_layer(burst, l, (void*)(intptr_t)(p + 1)) == HC_OK);
         int32_t enq = 0, fin = 0;
         CHECK(hc_burst_query(burst, &enq, &fin) == HC_OK);
         const int rc = hc_burst_wait(burst);
-        if (b % 7 == 3) {
+        if (b % 7 == 3 && b % 3 != 1) {
           CHECK(rc == HC_ERR_HIP);
           failed.fetch_add(1);
         } else {
