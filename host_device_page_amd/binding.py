@@ -203,8 +203,11 @@ class LoadBackGraph:
 
     def __init__(self, pool, host_idx, device_idx, events):
         n = int(device_idx.numel())
-        assert int(host_idx.numel()) == n
-        arr = (_V * max(1, len(events)))(*[e.handle.value if e is not None else None for e in events])
+        if int(host_idx.numel()) != n:
+            raise ValueError("host_idx and device_idx differ in length")
+        if len(events) != pool.layers:
+            raise ValueError(f"{len(events)} layer events for a pool of {pool.layers} layers")
+        arr = (_V * len(events))(*[e.handle.value if e is not None else None for e in events])
         self._refs = (pool, host_idx, device_idx, list(events), arr)
         self.handle = _V()
         check(lib.hc_load_back_graph_create(pool.handle, _V(_ptr(host_idx)), _V(_ptr(device_idx)), n, arr,
@@ -321,6 +324,7 @@ class Pool:
                  write_back_mode=HC_MODE_AUTO, load_back_mode=HC_MODE_AUTO, flags=0, max_ctas=0):
         sub_specs = [(g, e, [_ptr(t) for t in device_layers[b]]) for b, (g, e) in enumerate(subs)]
         self.stream = stream
+        self.layers = layers
         self.desc, self._keep = make_desc(
             layers=layers, page_size=page_size, subs=sub_specs, device_slots=device_slots,
             host_pages=host_pages, layout=layout, shard_align=shard_align, host_ptr=_ptr(host),
@@ -440,10 +444,16 @@ class Loader:
               "hc_loader_create")
         self.num_layers = num_layers
 
+    def _event_array(self, layer_events):
+        # the library reads exactly num_layers entries
+        if len(layer_events) != self.num_layers:
+            raise ValueError(f"{len(layer_events)} layer events for a loader of {self.num_layers} layers")
+        raw = [e.handle.value if isinstance(e, HipEvent) else int(e) for e in layer_events]
+        return (_V * len(raw))(*raw)
+
     def submit(self, host_idx, device_idx, n: int, layer_events, start_event=None) -> Burst:
         """layer_events: HipEvent objects or raw handles (ints); start_event likewise or None."""
-        raw = [e.handle.value if isinstance(e, HipEvent) else int(e) for e in layer_events]
-        arr = (_V * len(raw))(*raw)
+        arr = self._event_array(layer_events)
         st = start_event.handle.value if isinstance(start_event, HipEvent) else start_event
         out = _V()
         check(lib.hc_loader_submit(self.handle, _V(_ptr(host_idx)), _V(_ptr(device_idx)), n, arr,
@@ -455,8 +465,7 @@ class Loader:
     def submit_graph(self, graph, layer_events, start_event=None) -> Burst:
         """graph: a LoadBackGraph of this loader's pool (or a raw handle for custom ops);
         layer_events: the events it was captured with, in layer order."""
-        raw = [e.handle.value if isinstance(e, HipEvent) else int(e) for e in layer_events]
-        arr = (_V * len(raw))(*raw)
+        arr = self._event_array(layer_events)
         st = start_event.handle.value if isinstance(start_event, HipEvent) else start_event
         gh = graph.handle if isinstance(graph, LoadBackGraph) else _V(graph)
         out = _V()

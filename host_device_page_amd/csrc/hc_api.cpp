@@ -676,6 +676,7 @@ struct hc_lb_graph {
   bool held = false;  // counted in pool->users
   hipGraph_t graph = nullptr;
   hipGraphExec_t exec = nullptr;
+  std::vector<void*> events;  // the L layer events the replays record (NULL: none for that layer)
 };
 
 extern "C" {
@@ -708,6 +709,12 @@ int hc_load_back_graph_create(hc_pool* p, const int64_t* host_idx, const int64_t
   hc_lb_graph* g = new (std::nothrow) hc_lb_graph();
   if (!g) return set_err(HC_ERR_NOMEM, "graph handle allocation failed");
   g->pool = p;
+  try {
+    g->events.assign(layer_events, layer_events + p->lay.L);
+  } catch (...) {
+    delete g;
+    return set_err(HC_ERR_NOMEM, "graph handle allocation failed");
+  }
   hipError_t e = hipStreamBeginCapture(p->stream, hipStreamCaptureModeThreadLocal);
   if (e != hipSuccess) {
     delete g;
@@ -830,6 +837,19 @@ void pool_loader_ops(hc_pool* pool, hc_loader_ops* ops) {
 }
 
 int pool_layers(const hc_pool* pool) { return pool->lay.L; }
+
+int graph_matches(const hc_pool* pool, const void* graph, void* const* events, int32_t L) {
+  const hc_lb_graph* g = (const hc_lb_graph*)graph;
+  if (g->pool != pool) return set_error(HC_ERR_INVALID, "the graph was captured on another pool");
+  if ((int32_t)g->events.size() != L) return set_error(HC_ERR_INVALID, "the graph covers another layer count");
+  for (int32_t l = 0; l < L; l++)
+    if (g->events[(size_t)l] != events[l])
+      return set_error(HC_ERR_INVALID,
+                       "layer %d: the event differs from the one the graph was captured with (a replay records "
+                       "only its own events)",
+                       l);
+  return HC_OK;
+}
 
 void pool_hold(hc_pool* pool) { pool->users.fetch_add(1); }
 

@@ -67,6 +67,9 @@ int pool_layers(const hc_pool* pool);
 // Loaders and captured graphs that hold a pool: hc_pool_destroy refuses while any do.
 void pool_hold(hc_pool* pool);
 void pool_release(hc_pool* pool);
+// HC_OK when `graph` (an hc_lb_graph) was captured on `pool` and records exactly
+// `events` (L entries, in layer order); else HC_ERR_INVALID with a message.
+int graph_matches(const hc_pool* pool, const void* graph, void* const* events, int32_t L);
 
 // Optional timing of one kernel launch: two timing events that the launch itself
 // stamps with the kernel's start and end (hipExtLaunchKernel), so timing adds no

@@ -37,6 +37,7 @@ struct hc_burst {
 struct hc_loader {
   hc_loader_ops ops{};
   hc_pool* pool = nullptr;
+  bool pool_ops = false;  // ops are the pool's own: graphs are hc_lb_graph handles
   int32_t L = 0;
   bool async = false;
   std::mutex mu;
@@ -140,6 +141,7 @@ int hc_loader_create(hc_pool* pool, const hc_loader_ops* ops, int32_t num_layers
   if (!ld) return loader_err(HC_ERR_NOMEM, "loader allocation failed");
   ld->ops = use;
   ld->pool = pool;
+  ld->pool_ops = !ops;
   ld->L = num_layers;
   ld->async = async == 1;
   if (ld->async) {
@@ -176,6 +178,11 @@ int hc_loader_submit_graph(hc_loader* ld, void* graph, void* const* layer_events
   if (!ld || !out || !layer_events || !graph) return loader_err(HC_ERR_INVALID, "null argument");
   *out = nullptr;
   if (!ld->ops.launch_graph) return loader_err(HC_ERR_UNSUPPORTED, "the loader's ops cannot launch a graph");
+  if (ld->pool_ops) {
+    // a replay records only the events it was captured with; other ones would never be recorded
+    const int rc = hc::graph_matches(ld->pool, graph, layer_events, ld->L);
+    if (rc != HC_OK) return rc;
+  }
   return submit_burst(ld, nullptr, nullptr, 0, graph, layer_events, start_event, out);
 }
 

@@ -309,7 +309,10 @@ int hc_loader_submit(hc_loader* loader, const int64_t* host_idx, const int64_t* 
  * The worker makes the transfer stream wait for start_event (if any), launches the
  * graph and flags every layer at once; on failure it records every layer event, as
  * hc_loader_submit does.  Bursts of both kinds share one FIFO and one event-reuse
- * rule.  HC_ERR_UNSUPPORTED when the loader's ops have no launch_graph. */
+ * rule.  HC_ERR_UNSUPPORTED when the loader's ops have no launch_graph.  A loader
+ * created with the pool's own ops (ops NULL) checks at submit that the graph was
+ * captured on its pool with exactly these events (so a graph captured with a NULL
+ * layer event cannot be handed over) and refuses others with HC_ERR_INVALID. */
 int hc_loader_submit_graph(hc_loader* loader, void* graph, void* const* layer_events, void* start_event,
                            hc_burst** out);
 /* Block until layer `layer` of the burst is recorded, then make consumer_stream wait

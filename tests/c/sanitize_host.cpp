@@ -34,6 +34,7 @@ void pool_loader_ops(hc_pool*, hc_loader_ops*) { abort(); }  // every loader her
 int pool_layers(const hc_pool*) { return 0; }
 void pool_hold(hc_pool*) {}
 void pool_release(hc_pool*) {}
+int graph_matches(const hc_pool*, const void*, void* const*, int32_t) { abort(); }  // pool ops only
 }  // namespace hc
 
 #define CHECK(cond)                                                     \

@@ -170,3 +170,51 @@ def test_loader_replays_a_captured_burst(asynchronous):
         if graph is not None:
             graph.close()
         rig.close()
+
+
+@pytest.mark.gpu
+def test_loader_refuses_a_graph_it_could_not_flag():
+    """With the pool's own ops, a captured burst is handed over only with the exact events it
+    records and only to a loader of its own pool; anything else would leave a consumer
+    waiting on an event no replay records."""
+    say("[loader] mismatched captured bursts refused")
+    rig = Rig(SHAPE, seed=14)
+    other_rig = Rig(SHAPE, seed=15)
+    loader = None
+    graphs = []
+    try:
+        h = W.whole_page_tokens(W.host_pages(7, SHAPE.host_pages, 4), SHAPE.page_size)
+        d = W.permutation_slots(8, SHAPE.device_slots, h.size)
+        h_t, d_t = cuda_i64(h), cuda_i64(d)
+        events = [B.HipEvent() for _ in range(SHAPE.layers)]
+        g = rig.pool.capture_load_back(h_t, d_t, events)
+        graphs.append(g)
+        with_gap = list(events)
+        with_gap[2] = None
+        g_gap = rig.pool.capture_load_back(h_t, d_t, with_gap)
+        graphs.append(g_gap)
+        g_other = other_rig.pool.capture_load_back(h_t, d_t, events)
+        graphs.append(g_other)
+        loader = B.Loader(rig.pool, SHAPE.layers, asynchronous=True)
+        swapped = list(events)
+        swapped[3], swapped[4] = swapped[4], swapped[3]
+        cases = [(g, swapped, "layer 3"), (g, [B.HipEvent() for _ in events], "layer 0"),
+                 (g_gap, events, "layer 2"), (g_other, events, "another pool")]
+        for graph, evs, why in cases:
+            with pytest.raises(B.HcError) as ex:
+                loader.submit_graph(graph, evs)
+            assert ex.value.code == B.HC_ERR_INVALID and why in str(ex.value), str(ex.value)
+        with pytest.raises(ValueError):
+            loader.submit_graph(g, events[:-1])
+        # nothing was queued by the refusals; the matching hand-over still runs
+        burst = loader.submit_graph(g, events)
+        assert burst.wait() is None
+        burst.release()
+        assert loader.info() == (0, True)
+    finally:
+        if loader is not None:
+            loader.close()
+        for graph in graphs:
+            graph.close()
+        other_rig.close()
+        rig.close()

@@ -230,6 +230,13 @@ def test_argument_errors():
     with pytest.raises(B.HcError):
         ld.submit(0, 0, 1, [EV[0], 0, EV[2], EV[3]])
     assert B.lib.hc_burst_wait_layer(None, 0, None) == B.HC_ERR_INVALID
+    # the library reads exactly num_layers events: the binding refuses other counts
+    for evs in (EV[:-1], EV + EV[:1]):
+        with pytest.raises(ValueError):
+            ld.submit(0, 0, 1, evs)
+        with pytest.raises(ValueError):
+            ld.submit_graph(1, evs)
+    assert f.calls == []  # no refused submission reached the device ops
     ld.close()
 
 
