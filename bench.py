@@ -53,6 +53,12 @@ def parse():
                     help="threads of the second CPU oracle sample (0 = the usable cores, at most 16; 1 = skip it)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-staged-probe", action="store_true")
+    ap.add_argument("--no-duplex", action="store_true",
+                    help="skip the write-back + load-back at-once measurement")
+    ap.add_argument("--duplex-pairs", type=parse_pairs, default=DUPLEX_PAIRS,
+                    help="(write-back mode):(its workgroup cap):(load-back workgroup cap), comma-separated")
+    ap.add_argument("--duplex-only", action="store_true",
+                    help="instead: only the write-back + load-back at-once measurement and its copy-engine peak")
     ap.add_argument("--pipeline-ctas", type=lambda t: tuple(int(x) for x in t.split(",")), default=(0, 256),
                     help="zero-copy grid caps for the layer-pipeline measurement (0 = the pool's setting)")
     ap.add_argument("--sweep", action="store_true",
@@ -94,6 +100,155 @@ def memcpy_peak(hip, host_ptr: int, dev_ptr: int, nbytes: int, stream_ptr: int, 
     hip.hipEventDestroy(e0)
     hip.hipEventDestroy(e1)
     return nbytes / (best * 1e-3) / 1e9
+
+
+def memcpy_duplex_peak(hip, host_ptr: int, dev_ptr: int, nbytes: int, streams, reps: int = 5) -> dict:
+    """hipMemcpyAsync D2H and H2D of nbytes each at the same time on two streams (host
+    regions [0, nbytes) and [nbytes, 2 nbytes) of host_ptr, device likewise); best span of
+    `reps`.  The copy engines move both directions at once."""
+    V = ctypes.c_void_p
+    sw, sr = streams
+    ev = [V() for _ in range(3)]
+    for e in ev:
+        hip.hipEventCreate(ctypes.byref(e))
+    best = None
+    for _ in range(reps):
+        hip.hipEventRecord(ev[0], V(sw))
+        hip.hipStreamWaitEvent(V(sr), ev[0], 0)
+        assert hip.hipMemcpyAsync(V(host_ptr), V(dev_ptr), ctypes.c_size_t(nbytes), 2, V(sw)) == 0
+        assert hip.hipMemcpyAsync(V(dev_ptr + nbytes), V(host_ptr + nbytes), ctypes.c_size_t(nbytes), 1, V(sr)) == 0
+        hip.hipEventRecord(ev[1], V(sw))
+        hip.hipEventRecord(ev[2], V(sr))
+        hip.hipEventSynchronize(ev[1])
+        hip.hipEventSynchronize(ev[2])
+        ms = [ctypes.c_float(), ctypes.c_float()]
+        hip.hipEventElapsedTime(ctypes.byref(ms[0]), ev[0], ev[1])
+        hip.hipEventElapsedTime(ctypes.byref(ms[1]), ev[0], ev[2])
+        span = max(ms[0].value, ms[1].value)
+        if best is None or span < best[0]:
+            best = (span, ms[0].value, ms[1].value)
+    for e in ev:
+        hip.hipEventDestroy(e)
+    span, d2h, h2d = best
+    return {"aggregate_GBps": round(2 * nbytes / (span * 1e-3) / 1e9, 3),
+            "d2h_GBps": round(nbytes / (d2h * 1e-3) / 1e9, 3), "h2d_GBps": round(nbytes / (h2d * 1e-3) / 1e9, 3),
+            "bytes_each_way": nbytes}
+
+
+# (write-back mode, write-back workgroup cap, load-back workgroup cap) of the duplex measurement.
+# The caps decide how the two directions share the link: zero-copy host writes on 16 workgroups
+# starve zero-copy host reads; copy-engine writes beside reads on 8 workgroups leave both near 45 GB/s.
+DUPLEX_PAIRS = (("staged", 16, 8), ("staged", 16, 16), ("zerocopy", 16, 16), ("zerocopy", 2, 10))
+
+
+def parse_pairs(text: str):
+    """'staged:16:8,zerocopy:2:10' -> ((mode, write-back cap, load-back cap), ...)"""
+    out = []
+    for item in text.split(","):
+        mode, w, r = item.split(":")
+        if mode not in ("staged", "zerocopy"):
+            raise argparse.ArgumentTypeError(f"unknown write-back mode {mode!r}")
+        out.append((mode, int(w), int(r)))
+    return tuple(out)
+
+
+def relabel_host_pages(h, page_size: int, host_pages: int, seed: int = 7):
+    """The same rows of other host pages: each distinct page of the token list h is mapped to
+    a distinct page that h does not name (seeded), rows kept.  None when too few pages are left."""
+    import numpy as np
+    uniq, inv = np.unique(h // page_size, return_inverse=True)
+    rest = np.setdiff1d(np.arange(host_pages, dtype=np.int64), uniq)
+    if rest.size < uniq.size:
+        return None
+    other = np.random.default_rng(seed).choice(rest, uniq.size, replace=False)
+    return np.ascontiguousarray(other[inv.reshape(-1)] * page_size + h % page_size, dtype=np.int64)
+
+
+def duplex_timing(B, torch, np, make_pool, shape, burst, d_t, h_np, d2_t, link_bytes, pairs, reps=5):
+    """A write-back burst and a per-layer load-back burst of other rows at the same time:
+    two pools over the same buffers, each on its own stream.  The load-back names the same
+    rows of other host pages (a page-by-page relabelling of the burst's host tokens) into
+    the fresh slots d2, so the two bursts touch disjoint device and host rows."""
+    L = shape.layers
+    h_other = relabel_host_pages(h_np, shape.page_size, shape.host_pages)
+    if h_other is None:
+        return None
+    hl_t = torch.from_numpy(h_other).cuda()
+    sw, sr = torch.cuda.Stream(), torch.cuda.Stream()
+    e0, ew, er = B.HipEvent(timing=True), B.HipEvent(timing=True), B.HipEvent(timing=True)
+
+    def run(wp, rp, do_w, do_r):
+        torch.cuda.synchronize()
+        e0.record(sw)
+        e0.wait_on(sr)
+        if do_w:
+            wp.write_back_all_layers(d_t, h_np)
+        if do_r:
+            for l in range(L):
+                rp.load_back_layer(l, hl_t, d2_t)
+        ew.record(sw)
+        er.record(sr)
+        ew.synchronize()
+        er.synchronize()
+        return e0.elapsed_ms(ew), e0.elapsed_ms(er)
+
+    def gbs(ms):
+        return round(link_bytes / (ms * 1e-3) / 1e9, 3)
+
+    rows = []
+    for mode, wctas, rctas in pairs:
+        wmode = B.HC_MODE_STAGED if mode == "staged" else B.HC_MODE_ZEROCOPY
+        wp = make_pool(wmode, max_ctas=wctas, flags=0, stream_=sw)
+        rp = make_pool(B.HC_MODE_ZEROCOPY, max_ctas=rctas, flags=0, stream_=sr)
+        run(wp, rp, True, True)
+        w_alone = float(np.median([run(wp, rp, True, False)[0] for _ in range(reps)]))
+        r_alone = float(np.median([run(wp, rp, False, True)[1] for _ in range(reps)]))
+        both = [run(wp, rp, True, True) for _ in range(reps)]
+        wp.sync()
+        rp.sync()
+        wp.close()
+        rp.close()
+        span = float(np.median([max(b) for b in both]))
+        rows.append({"write_back": f"{mode}, {wctas} workgroups" if mode == "zerocopy" else "staged",
+                     "load_back_workgroups": rctas,
+                     "alone_GBps": {"write_back": gbs(w_alone), "load_back": gbs(r_alone)},
+                     "together_GBps": {"write_back": gbs(float(np.median([b[0] for b in both]))),
+                                       "load_back": gbs(float(np.median([b[1] for b in both])))},
+                     "together_span_ms": round(span, 3),
+                     "aggregate_GBps": round(2 * link_bytes / (span * 1e-3) / 1e9, 3),
+                     "one_after_the_other_GBps": round(2 * link_bytes / ((w_alone + r_alone) * 1e-3) / 1e9, 3)})
+        log(f"[bench] duplex {rows[-1]}")
+    return {"what": "write-back and per-layer load-back of disjoint rows at once, two pools on two streams",
+            "rows": rows, "streams": (sw, sr)}
+
+
+def hip_setup(B):
+    """The HIP runtime through ctypes, with the signatures the peak measurements use."""
+    hip = B._hip
+    for name, argt in {"hipMemcpyAsync": [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                                          ctypes.c_void_p], "hipEventCreate": [ctypes.POINTER(ctypes.c_void_p)],
+                       "hipStreamWaitEvent": [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint]}.items():
+        getattr(hip, name).argtypes = argt
+        getattr(hip, name).restype = ctypes.c_int
+    return hip
+
+
+def duplex_measurement(B, torch, np, hip, make_pool, shape, burst, d_t, h_np, d2_t, link_bytes, host, scratch,
+                       nbytes, pairs, have_staging):
+    """duplex_timing over `pairs`, plus the copy-engine duplex peak on the same two streams."""
+    duplex = duplex_timing(B, torch, np, make_pool, shape, burst, d_t, h_np, d2_t, link_bytes,
+                           [p for p in pairs if p[0] == "zerocopy" or have_staging])
+    if duplex is None:
+        return None
+    sw, sr = duplex.pop("streams")
+    duplex["roofline"] = dict(memcpy_duplex_peak(hip, host.ptr.value, scratch.data_ptr(), nbytes,
+                                                 (sw.cuda_stream, sr.cuda_stream)),
+                              source="hipMemcpyAsync D2H and H2D at once on two streams, best of 5")
+    if duplex["rows"]:
+        best = max(duplex["rows"], key=lambda r: r["aggregate_GBps"])
+        duplex["best_frac_of_duplex_peak"] = round(best["aggregate_GBps"] / duplex["roofline"]["aggregate_GBps"], 4)
+    log(f"[bench] duplex copy-engine peak {duplex['roofline']}")
+    return duplex
 
 
 def kernel_source_digest() -> str:
@@ -492,9 +647,10 @@ def main():
         staging = torch.empty(args.staging_pages * B.staging_page_bytes(probe), dtype=torch.uint8, device="cuda")
     layers = [[t[l] for l in range(L)] for t in dev]
 
-    def make_pool(mode, max_ctas=None, flags=B.HC_FLAG_PROFILE):
+    def make_pool(mode, max_ctas=None, flags=B.HC_FLAG_PROFILE, stream_=None):
         return B.Pool(layers=L, page_size=P, subs=list(shape.subs), device_slots=shape.device_slots,
-                      host_pages=shape.host_pages, device_layers=layers, host=host, stream=stream,
+                      host_pages=shape.host_pages, device_layers=layers, host=host,
+                      stream=stream if stream_ is None else stream_,
                       layout=shape.layout, shard_align=shape.align, staging=staging, write_back_mode=mode,
                       flags=flags, max_ctas=args.max_ctas if max_ctas is None else max_ctas)
 
@@ -539,6 +695,17 @@ def main():
         return
 
     link_bytes, _ = burst_bytes(shape, burst)
+    if args.duplex_only:
+        pool.close()
+        hip = hip_setup(B)
+        nb = min(1 << 30, host.nbytes // 2 // 4096 * 4096)
+        scratch = torch.empty(2 * nb, dtype=torch.uint8, device="cuda")
+        res = duplex_measurement(B, torch, np, hip, make_pool, shape, burst, d_t, h_np, d2_t, link_bytes, host,
+                                 scratch, nb, args.duplex_pairs, staging is not None)
+        del scratch
+        print(json.dumps({"duplex": res, "workload": shape.name, "burst_bytes_each_way": link_bytes}), flush=True)
+        host.free()
+        return
     ev_wb0, ev_wb1, ev_lb1 = B.HipEvent(timing=True), B.HipEvent(timing=True), B.HipEvent(timing=True)
     layer_events = [B.HipEvent() for _ in range(L)]
     enqueue_s = []
@@ -580,16 +747,17 @@ def main():
     lb_gbs = link_bytes / (float(np.median(lb_ms)) * 1e-3) / 1e9
 
     # host-link peaks measured here: 1 GiB hipMemcpyAsync pinned <-> device, best of 5
-    hip = B._hip
-    for name, argt in {"hipMemcpyAsync": [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
-                                          ctypes.c_void_p], "hipEventCreate": [ctypes.POINTER(ctypes.c_void_p)]}.items():
-        getattr(hip, name).argtypes = argt
-        getattr(hip, name).restype = ctypes.c_int
-    one_gib = 1 << 30
-    scratch = torch.empty(one_gib, dtype=torch.uint8, device="cuda")
+    hip = hip_setup(B)
+    # 1 GiB, or half the host pool when it is smaller (the copies land in the host pool)
+    one_gib = min(1 << 30, host.nbytes // 2 // 4096 * 4096)
+    scratch = torch.empty(2 * one_gib, dtype=torch.uint8, device="cuda")
     torch.cuda.synchronize()
     peak_h2d = memcpy_peak(hip, host.ptr.value, scratch.data_ptr(), one_gib, stream.cuda_stream, True)
     peak_d2h = memcpy_peak(hip, host.ptr.value, scratch.data_ptr(), one_gib, stream.cuda_stream, False)
+    duplex = None
+    if not args.no_duplex:
+        duplex = duplex_measurement(B, torch, np, hip, make_pool, shape, burst, d_t, h_np, d2_t, link_bytes,
+                                    host, scratch, one_gib, args.duplex_pairs, staging is not None)
     del scratch
     log(f"[bench] hipMemcpyAsync peak H2D {peak_h2d:.2f} GB/s, D2H {peak_d2h:.2f} GB/s")
 
@@ -726,6 +894,7 @@ def main():
         "load_back_graph": graph,
         "load_back_handover_ms": handover,
         "layer_pipeline": pipeline,
+        "duplex": duplex,
         "kernel_avg_ms": {"zc_read": round(ms_rd / max(1, n_rd), 4), "zc_write": round(ms_wr / max(1, n_wr), 4)},
         "roofline": roofline,
         "roofline_hbm": roofline_hbm,

@@ -120,7 +120,8 @@ struct hc_pool {
 
 namespace {
 
-int check_device_ptr(const void* p, const char* what) {
+// Device memory of the pool's device (the kernels run there and take these addresses).
+int check_device_ptr(const void* p, int device, const char* what) {
   hipPointerAttribute_t attr;
   hipError_t e = hipPointerGetAttributes(&attr, p);
   if (e != hipSuccess) {
@@ -129,6 +130,8 @@ int check_device_ptr(const void* p, const char* what) {
   }
   if (attr.type != hipMemoryTypeDevice)
     return set_err(HC_ERR_INVALID, "%s must be device memory", what);
+  if (attr.device != device)
+    return set_err(HC_ERR_INVALID, "%s is on device %d, the pool's (current) device is %d", what, attr.device, device);
   return HC_OK;
 }
 
@@ -408,6 +411,16 @@ int hc_pool_create(const hc_pool_desc* desc, hc_pool** out) {
   if (hipDeviceGetAttribute(&p->num_cus, hipDeviceAttributeMultiprocessorCount, p->device) != hipSuccess)
     return bail(set_err(HC_ERR_HIP, "could not query the compute-unit count"));
   p->stream = (hipStream_t)desc->copy_stream;
+  if (p->stream) {
+    hipDevice_t sd = -1;
+    if (hipStreamGetDevice(p->stream, &sd) != hipSuccess) {
+      (void)hipGetLastError();
+      return bail(set_err(HC_ERR_INVALID, "copy_stream is not a valid stream"));
+    }
+    if (sd != p->device)
+      return bail(set_err(HC_ERR_INVALID, "copy_stream belongs to device %d, the pool's (current) device is %d", sd,
+                          p->device));
+  }
   p->flags = desc->flags;
   p->max_ctas = desc->max_ctas > 0 ? desc->max_ctas : kDefaultMaxCtas;
   // memory kinds
@@ -421,7 +434,7 @@ int hc_pool_create(const hc_pool_desc* desc, hc_pool** out) {
   }
   for (int b = 0; b < L.nsub; b++)
     for (int l = 0; l < L.L; l++) {
-      rc = check_device_ptr(desc->sub[b].device_layers[l], "device layer");
+      rc = check_device_ptr(desc->sub[b].device_layers[l], p->device, "device layer");
       if (rc != HC_OK) return bail(rc);
     }
   // modes.  AUTO write-back is staged whenever the caller brings staging for it: a
@@ -432,7 +445,7 @@ int hc_pool_create(const hc_pool_desc* desc, hc_pool** out) {
   p->wb_mode = (desc->write_back_mode == HC_MODE_STAGED || auto_staged) ? HC_MODE_STAGED : HC_MODE_ZEROCOPY;
   p->lb_mode = HC_MODE_ZEROCOPY;
   if (p->wb_mode == HC_MODE_STAGED) {
-    rc = check_device_ptr(desc->staging, "staging");
+    rc = check_device_ptr(desc->staging, p->device, "staging");
     if (rc != HC_OK) return bail(rc);
     p->staging = (uint8_t*)desc->staging;
     p->staging_bytes = desc->staging_bytes;

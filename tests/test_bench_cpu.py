@@ -107,3 +107,31 @@ def test_cpu_baseline_reports_threads_and_bytes():
     two = bench.cpu_baseline(shape, burst, d2, 0.2, threads=2)
     assert one["cores"] == 1 and two["cores"] == 2
     assert one["kind"] == two["kind"] == "oracle" and one["value"] > 0 and two["value"] > 0
+
+
+def test_duplex_load_back_names_the_same_rows_of_other_pages():
+    for name in ("llama3_8b_mha_bf16", "dsa_mla_indexer_78l", "mha_kv_split_shard_bf16"):
+        shape = W.SHAPES[name]
+        P = shape.page_size
+        burst = W.burst_for(shape, seed=1)
+        h = burst.host_idx
+        o = bench.relabel_host_pages(h, P, shape.host_pages)
+        assert o.dtype == np.int64 and o.shape == h.shape
+        assert np.array_equal(o % P, h % P)  # rows kept, so the byte count is the same
+        assert np.intersect1d(o // P, h // P).size == 0  # disjoint host pages
+        assert o.min() >= 0 and o.max() < shape.host_pages * P
+        # one new page per old page, and distinct old pages get distinct new ones
+        pairs = np.unique(np.stack([h // P, o // P]), axis=1)
+        assert pairs.shape[1] == np.unique(h // P).size == np.unique(o // P).size
+        assert bench.burst_bytes(shape, W.Burst(burst.device_idx, o, W.distinct_pages(o, P)))[0] == \
+            bench.burst_bytes(shape, burst)[0]
+    # too few pages left
+    assert bench.relabel_host_pages(np.arange(48, dtype=np.int64), 16, 5) is None
+
+
+def test_duplex_pairs_parse():
+    assert bench.parse_pairs("staged:16:8,zerocopy:2:10") == (("staged", 16, 8), ("zerocopy", 2, 10))
+    import argparse
+    import pytest
+    with pytest.raises(argparse.ArgumentTypeError):
+        bench.parse_pairs("copy:1:1")
