@@ -791,6 +791,21 @@ def main():
     # on a pool without per-launch timing (a launch that stamps timing events costs more CPU time)
     handover = {}
     hpool = make_pool(wb_mode, flags=0)
+    # CPU time of the enqueue calls alone (validation, planning, plan upload, launches) on this pool
+    wb_enq, lb_enq = [], []
+    for _ in range(5):
+        torch.cuda.synchronize()
+        t_s = time.perf_counter()
+        hpool.write_back_all_layers(d_t, h_np)
+        wb_enq.append(time.perf_counter() - t_s)
+        t_s = time.perf_counter()
+        for l in range(L):
+            hpool.load_back_layer(l, h_t, d2_t, layer_events[l])
+        lb_enq.append(time.perf_counter() - t_s)
+    hpool.sync()
+    enqueue_unprofiled = {"write_back": round(1e3 * float(np.median(wb_enq)), 4),
+                          "load_back_all_layers": round(1e3 * float(np.median(lb_enq)), 4)}
+    log(f"[bench] CPU enqueue without timing events (ms): {enqueue_unprofiled}")
     for asynchronous in (False, True):
         ld = B.Loader(hpool, L, asynchronous=asynchronous)
         times = []
@@ -891,6 +906,7 @@ def main():
         "host_link_peak_GBps": {"h2d": round(peak_h2d, 3), "d2h": round(peak_d2h, 3)},
         "frac_of_link_peak": {"write_back": round(wb_gbs / peak_d2h, 4), "load_back": round(lb_gbs / peak_h2d, 4)},
         "cpu_enqueue_ms_per_step": round(1e3 * float(np.median(enqueue_s)), 3),
+        "cpu_enqueue_ms_unprofiled": enqueue_unprofiled,
         "load_back_graph": graph,
         "load_back_handover_ms": handover,
         "layer_pipeline": pipeline,
