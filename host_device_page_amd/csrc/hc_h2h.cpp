@@ -141,6 +141,9 @@ int hc_h2h_submit(hc_h2h* e, int32_t direction, int32_t tensors, const int64_t* 
     return hc::set_error(HC_ERR_INVALID, "tensor count must be in [1, HC_H2H_MAX_TENSORS]");
   if (n < 0) return hc::set_error(HC_ERR_INVALID, "n must be >= 0");
   if (n > 0 && (!tensor_pages || !shards)) return hc::set_error(HC_ERR_INVALID, "null address array");
+  if (n > e->depth)  // could never be admitted: split it
+    return hc::set_error(HC_ERR_INVALID, "%lld shards exceed the queue depth %lld", (long long)n,
+                         (long long)e->depth);
   int64_t sum = 0;
   for (int32_t t = 0; t < tensors; t++) {
     if (tensor_bytes[t] <= 0) return hc::set_error(HC_ERR_INVALID, "tensor %d: size must be > 0", t);

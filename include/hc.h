@@ -81,7 +81,8 @@ typedef enum hc_status {
   HC_ERR_UNSUPPORTED = -2, /* well-formed but not handled: elem_bytes % 16, misalignment, mode */
   HC_ERR_HIP = -3,         /* a HIP runtime call failed (the message names it) */
   HC_ERR_NOMEM = -4,       /* the library could not allocate its own scratch */
-  HC_ERR_DEVICE = -5,      /* device-side validation flagged an index list (HC_FLAG_VALIDATE) */
+  HC_ERR_DEVICE = -5,      /* a kernel flagged an index list: an out-of-range entry (always checked),
+                              or page-block rows that are not one whole device page (HC_FLAG_VALIDATE) */
   HC_ERR_BUSY = -6         /* host-to-host queue capacity exhausted; nothing was submitted */
 } hc_status;
 
@@ -348,7 +349,8 @@ int hc_loader_destroy(hc_loader* loader);
  * different shards run concurrently.  Dump and load keep separate counts of
  * outstanding shards (queued + running); a request reserves capacity for all its
  * shards or is refused with HC_ERR_BUSY, never submitted in part.  A request with a
- * null address or a tensor-size mismatch is refused whole with HC_ERR_INVALID.
+ * null address, a tensor-size mismatch or more shards than the queue depth (it could
+ * never be admitted) is refused whole with HC_ERR_INVALID.
  * Every submitted job counts toward its request's completion.  The workers form an
  * unordered executor, not a FIFO stream: jobs (and requests) may finish in any
  * order, and a caller that needs ordering waits on the earlier request first. */

@@ -94,6 +94,9 @@ def test_refused_requests():
         eng.submit(B.HC_H2H_DUMP, [200, 100], [[a, a]], [a + 512], 256)  # pages do not fit the shard
     with pytest.raises(B.HcError):
         eng.submit(7, [16], [[a]], [a + 512], 16)
+    with pytest.raises(B.HcError) as e:  # more shards than the queue holds: never admissible, not "busy"
+        eng.submit(B.HC_H2H_DUMP, [16], [[a] for _ in range(17)], [a + 512 + 16 * i for i in range(17)], 16)
+    assert e.value.code == B.HC_ERR_INVALID and "queue depth" in str(e.value)
     assert eng.outstanding() == (0, 0)
     out = ctypes.c_void_p()
     assert B.lib.hc_h2h_create(-1, 4, ctypes.byref(out)) == B.HC_ERR_INVALID
