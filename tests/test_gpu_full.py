@@ -119,6 +119,9 @@ def round_trip(rig, burst, d2):
     ("llama3_8b_mha_bf16_token_major", "zerocopy"),
     ("llama3_8b_mha_bf16_token_major", "staged"),
     ("dsv3_mla_bf16", "zerocopy"),
+    ("dsv3_mla_bf16", "staged"),
+    ("dsa_mla_indexer_78l", "zerocopy"),
+    ("dsa_mla_indexer_78l", "staged"),
     ("mha_kv_split_shard_bf16", "zerocopy"),
     ("mha_kv_split_shard_bf16", "staged"),
 ])
