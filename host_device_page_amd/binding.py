@@ -202,8 +202,8 @@ class LoadBackGraph:
     on the pool's copy stream.  Keeps the index tensors and events alive."""
 
     def __init__(self, pool, host_idx, device_idx, events):
-        n = int(device_idx.numel())
-        if int(host_idx.numel()) != n:
+        n = _index_list(device_idx, "device_idx", True)
+        if _index_list(host_idx, "host_idx", True) != n:
             raise ValueError("host_idx and device_idx differ in length")
         if len(events) != pool.layers:
             raise ValueError(f"{len(events)} layer events for a pool of {pool.layers} layers")
@@ -314,6 +314,30 @@ def _ptr(x) -> int:
     return x.data_ptr()
 
 
+def _index_list(x, what: str, on_device: bool):
+    """Check an index list argument and return its element count.  torch tensors and numpy
+    arrays must be int64 and contiguous; device lists must be CUDA tensors, the
+    write-back's host list must not be one (the library rechecks the memory itself)."""
+    if isinstance(x, np.ndarray):
+        if on_device:
+            raise TypeError(f"{what} must be an int64 CUDA tensor, not a numpy array")
+        if x.dtype != np.int64 or not x.flags.c_contiguous:
+            raise TypeError(f"{what} must be a C-contiguous int64 array")
+        return int(x.size)
+    if hasattr(x, "is_cuda"):
+        if x.dtype != _torch_int64() or not x.is_contiguous():
+            raise TypeError(f"{what} must be a contiguous int64 tensor")
+        if x.is_cuda != on_device:
+            raise TypeError(f"{what} must be a {'CUDA' if on_device else 'CPU'} tensor")
+        return int(x.numel())
+    raise TypeError(f"{what}: expected a torch tensor or numpy array")
+
+
+def _torch_int64():
+    import torch
+    return torch.int64
+
+
 class Pool:
     """Owns one hc_pool handle.  device_layers[b][l] are torch CUDA tensors (or raw
     addresses); host is a HostBuffer; staging a torch CUDA tensor or None; stream a
@@ -343,15 +367,17 @@ class Pool:
 
     def write_back_all_layers(self, device_idx, host_idx, event: HipEvent | None = None) -> None:
         """device_idx: int64 CUDA tensor; host_idx: int64 CPU tensor or numpy array."""
-        n = int(device_idx.numel())
-        assert int(host_idx.size if isinstance(host_idx, np.ndarray) else host_idx.numel()) == n
+        n = _index_list(device_idx, "device_idx", True)
+        if _index_list(host_idx, "host_idx", False) != n:
+            raise ValueError("host_idx and device_idx differ in length")
         check(lib.hc_write_back_all_layers(self.handle, _V(_ptr(device_idx)), _V(_ptr(host_idx)), n,
                                            event.handle if event else None), "hc_write_back_all_layers")
 
     def load_back_layer(self, layer: int, host_idx, device_idx, event: HipEvent | None = None) -> None:
         """host_idx, device_idx: int64 CUDA tensors."""
-        n = int(device_idx.numel())
-        assert int(host_idx.numel()) == n
+        n = _index_list(device_idx, "device_idx", True)
+        if _index_list(host_idx, "host_idx", True) != n:
+            raise ValueError("host_idx and device_idx differ in length")
         check(lib.hc_load_back_layer(self.handle, layer, _V(_ptr(host_idx)), _V(_ptr(device_idx)), n,
                                      event.handle if event else None), "hc_load_back_layer")
 
@@ -362,7 +388,9 @@ class Pool:
 
     def round_trip_check(self, idx_a, idx_b) -> int:
         out = ctypes.c_int64()
-        n = int(idx_a.numel())
+        n = _index_list(idx_a, "idx_a", True)
+        if _index_list(idx_b, "idx_b", True) != n:
+            raise ValueError("idx_a and idx_b differ in length")
         check(lib.hc_round_trip_check(self.handle, _V(_ptr(idx_a)), _V(_ptr(idx_b)), n, ctypes.byref(out)),
               "hc_round_trip_check")
         return out.value

@@ -98,6 +98,7 @@ struct hc_pool {
   int32_t lb_mode = HC_MODE_ZEROCOPY;
   int32_t flags = 0;
   int32_t max_ctas = kDefaultMaxCtas;
+  bool capturing = false;       // hc_load_back_graph_create is recording this pool's stream
   int32_t num_cus = 0;          // compute units of the pool's device
   uint8_t* host = nullptr;      // host pool (host address == device address on ROCm)
   uint8_t* staging = nullptr;
@@ -132,6 +133,54 @@ int check_device_ptr(const void* p, int device, const char* what) {
     return set_err(HC_ERR_INVALID, "%s must be device memory", what);
   if (attr.device != device)
     return set_err(HC_ERR_INVALID, "%s is on device %d, the pool's (current) device is %d", what, attr.device, device);
+  return HC_OK;
+}
+
+// An index list the kernels read: memory the pool's device can address (its device
+// memory, or pinned host memory mapped at the same address) that holds n int64 entries
+// inside one allocation.  Pageable host memory would fault the kernel, and a list
+// shorter than n would be read past its end, so both are refused before any launch.
+int check_device_list(const hc_pool* p, const int64_t* q, int64_t n, const char* what) {
+  hipPointerAttribute_t attr;
+  if (hipPointerGetAttributes(&attr, q) != hipSuccess) {
+    (void)hipGetLastError();
+    return set_err(HC_ERR_INVALID, "%s is not memory known to HIP", what);
+  }
+  if (attr.type == hipMemoryTypeDevice) {
+    if (attr.device != p->device)
+      return set_err(HC_ERR_INVALID, "%s is on device %d, the pool's device is %d", what, attr.device, p->device);
+  } else if (attr.type == hipMemoryTypeHost) {
+    if (attr.devicePointer != (const void*)q)
+      return set_err(HC_ERR_INVALID, "%s: pinned host memory not mapped at its host address", what);
+  } else {
+    return set_err(HC_ERR_INVALID,
+                   "%s must be device memory (or pinned host memory): the kernels read it, and pageable host "
+                   "memory would fault them",
+                   what);
+  }
+  hipDeviceptr_t base = nullptr;
+  size_t size = 0;
+  if (hipMemGetAddressRange(&base, &size, (hipDeviceptr_t)q) != hipSuccess || !base) {
+    (void)hipGetLastError();
+    return set_err(HC_ERR_INVALID, "%s: its allocation could not be found", what);
+  }
+  const uint64_t end = (uint64_t)(uintptr_t)base + (uint64_t)size;
+  const uint64_t need = (uint64_t)(uintptr_t)q + (uint64_t)n * sizeof(int64_t);
+  if (need > end)
+    return set_err(HC_ERR_INVALID, "%s holds fewer than n = %lld int64 entries (its allocation ends %llu bytes in)",
+                   what, (long long)n, (unsigned long long)(end - (uint64_t)(uintptr_t)q));
+  return HC_OK;
+}
+
+// The write-back's host list is read by the CPU: device memory would crash it.
+int check_host_list(const int64_t* q, const char* what) {
+  hipPointerAttribute_t attr;
+  if (hipPointerGetAttributes(&attr, q) != hipSuccess) {
+    (void)hipGetLastError();
+    return HC_OK;  // not known to HIP: ordinary host memory
+  }
+  if (attr.type == hipMemoryTypeDevice || attr.type == hipMemoryTypeArray)
+    return set_err(HC_ERR_INVALID, "%s must be in host memory: the CPU plans the write-back from it", what);
   return HC_OK;
 }
 
@@ -546,6 +595,9 @@ int hc_write_back_all_layers(hc_pool* p, const int64_t* device_idx, const int64_
   if (n == 0) return finish(HC_OK);
   if (!device_idx || !host_idx) return finish(set_err(HC_ERR_INVALID, "null index list"));
   if (n >= ((int64_t)1 << 31)) return finish(set_err(HC_ERR_INVALID, "n must be below 2^31"));
+  rc = check_device_list(p, device_idx, n, "device_idx");
+  if (rc == HC_OK) rc = check_host_list(host_idx, "host_idx");
+  if (rc != HC_OK) return finish(rc);
   {
     char msg[256];
     rc = p->planner.validate(host_idx, n, msg, sizeof(msg));
@@ -651,6 +703,11 @@ int hc_load_back_layer(hc_pool* p, int32_t layer, const int64_t* host_idx, const
   if (!host_idx || !device_idx) return finish(set_err(HC_ERR_INVALID, "null index list"));
   if (p->lay.has_blocks && n % p->lay.P != 0)
     return finish(set_err(HC_ERR_INVALID, "page-block sub-buffers need whole pages (n %% page_size != 0)"));
+  if (!p->capturing) {  // a capture checks its lists once, before it starts
+    rc = check_device_list(p, host_idx, n, "host_idx");
+    if (rc == HC_OK) rc = check_device_list(p, device_idx, n, "device_idx");
+    if (rc != HC_OK) return finish(rc);
+  }
   hipError_t e;
   {
     Timer t(p, 2);
@@ -669,6 +726,11 @@ int hc_round_trip_check(hc_pool* p, const int64_t* idx_a, const int64_t* idx_b, 
   if (rc != HC_OK) return rc;
   if (n < 0) return set_err(HC_ERR_INVALID, "n must be >= 0");
   if (n > 0 && (!idx_a || !idx_b)) return set_err(HC_ERR_INVALID, "null index list");
+  if (n > 0) {
+    rc = check_device_list(p, idx_a, n, "idx_a");
+    if (rc == HC_OK) rc = check_device_list(p, idx_b, n, "idx_b");
+    if (rc != HC_OK) return rc;
+  }
   HIP_TRY(hipMemsetAsync(p->d_counter, 0, sizeof(unsigned long long), p->stream));
   if (n > 0) {
     Timer t(p, 4);
@@ -719,6 +781,11 @@ int hc_load_back_graph_create(hc_pool* p, const int64_t* host_idx, const int64_t
   hipStreamCaptureStatus status = hipStreamCaptureStatusNone;
   HIP_TRY(hipStreamIsCapturing(p->stream, &status));
   if (status != hipStreamCaptureStatusNone) return set_err(HC_ERR_INVALID, "the pool's stream is already capturing");
+  if (n > 0) {
+    rc = check_device_list(p, host_idx, n, "host_idx");
+    if (rc == HC_OK) rc = check_device_list(p, device_idx, n, "device_idx");
+    if (rc != HC_OK) return rc;
+  }
   hc_lb_graph* g = new (std::nothrow) hc_lb_graph();
   if (!g) return set_err(HC_ERR_NOMEM, "graph handle allocation failed");
   g->pool = p;
@@ -733,8 +800,10 @@ int hc_load_back_graph_create(hc_pool* p, const int64_t* host_idx, const int64_t
     delete g;
     return set_err(HC_ERR_HIP, "hipStreamBeginCapture failed: %s", hipGetErrorString(e));
   }
+  p->capturing = true;
   for (int32_t l = 0; l < p->lay.L && rc == HC_OK; l++)
     rc = hc_load_back_layer(p, l, host_idx, device_idx, n, layer_events[l]);
+  p->capturing = false;
   const std::string layer_err = rc != HC_OK ? g_err : std::string();
   e = hipStreamEndCapture(p->stream, &g->graph);
   if (rc != HC_OK) {

@@ -52,7 +52,11 @@
  *     named whole, as P consecutive list entries in row order (rows 0..P-1)
  *     that map onto one whole device page the same way, so the row-0 tokens sit
  *     at list positions k * P.  A host list
- *     read on the CPU is checked before anything is enqueued.  Device-resident
+ *     read on the CPU is checked before anything is enqueued.  A list the kernels
+ *     read must be device memory of the pool's device or pinned host memory and
+ *     hold n entries inside its allocation; anything else (pageable host memory,
+ *     a short buffer) is refused with HC_ERR_INVALID before any launch, and the
+ *     write-back's host list must not be device memory.  Device-resident
  *     lists are read by the kernels, which range-check every index, skip an
  *     out-of-range row and report it as HC_ERR_DEVICE at the next
  *     hc_round_trip_check or hc_pool_sync; distinctness of device-resident lists

@@ -279,3 +279,88 @@ def test_block_pool_write_back_rejects_out_of_order_pages():
         write_back_and_check(rig, d, h)  # the same pages in order go through
     finally:
         rig.close()
+
+
+def _raw(x):
+    return B._V(x.ctypes.data if isinstance(x, np.ndarray) else x.data_ptr())
+
+
+@pytest.mark.gpu
+def test_index_lists_the_kernels_cannot_read_are_refused():
+    """Lists in pageable host memory, or shorter than n, are refused before any launch (a
+    kernel would fault on the first and read past the end of the second); the layer
+    event is still recorded.  Pinned host lists are readable and move the same rows."""
+    import ctypes
+    say("[events] unreadable index lists refused")
+    rig = Rig(SHAPE, seed=10)
+    hip = B._hip
+    short = ctypes.c_void_p()
+    try:
+        h, d, d2 = prepare(rig, 11)
+        n = h.size
+        h_t, d_t, d2_t = cuda_i64(h), cuda_i64(d), cuda_i64(d2)
+        h_np = np.ascontiguousarray(h, dtype=np.int64)
+        pool = rig.pool.handle
+
+        def refused(rc, words):
+            assert rc == B.HC_ERR_INVALID, rc
+            msg = B.lib.hc_last_error().decode()
+            assert all(w in msg for w in words), msg
+
+        for l, (hh, dd, what) in enumerate([(h_np, d2_t, "host_idx"), (h_t, h_np, "device_idx")]):
+            ev = B.HipEvent()
+            refused(B.lib.hc_load_back_layer(pool, l, _raw(hh), _raw(dd), n, ev.handle), [what, "pageable"])
+            ev.synchronize()  # recorded although nothing was launched
+        refused(B.lib.hc_round_trip_check(pool, _raw(h_np), _raw(d_t), n, ctypes.byref(ctypes.c_int64())),
+                ["idx_a", "pageable"])
+        refused(B.lib.hc_write_back_all_layers(pool, _raw(d_t), _raw(h_t), n, None), ["host_idx", "host memory"])
+        refused(B.lib.hc_write_back_all_layers(pool, _raw(h_np), _raw(h_np), n, None), ["device_idx", "pageable"])
+        evs = (B._V * SHAPE.layers)(*[None] * SHAPE.layers)
+        g = ctypes.c_void_p()
+        refused(B.lib.hc_load_back_graph_create(pool, _raw(h_np), _raw(d2_t), n, evs, ctypes.byref(g)),
+                ["host_idx", "pageable"])
+        assert not g.value
+
+        # a list shorter than n: an exact 4096-byte allocation holding 512 entries
+        hip.hipMalloc.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_size_t]
+        hip.hipMalloc.restype = ctypes.c_int
+        assert hip.hipMalloc(ctypes.byref(short), 4096) == 0
+        base, size = ctypes.c_void_p(), ctypes.c_size_t()
+        hip.hipMemGetAddressRange.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(ctypes.c_size_t),
+                                              ctypes.c_void_p]
+        assert hip.hipMemGetAddressRange(ctypes.byref(base), ctypes.byref(size), short) == 0
+        assert base.value == short.value
+        fits = size.value // 8
+        assert fits < n
+        refused(B.lib.hc_load_back_layer(pool, 0, short, _raw(d2_t), n, None), ["host_idx", "fewer than"])
+        refused(B.lib.hc_round_trip_check(pool, _raw(d_t), short, n, ctypes.byref(ctypes.c_int64())),
+                ["idx_b", "fewer than"])
+        rig.pool.sync()  # nothing was flagged: no kernel ran
+
+        # the binding refuses the wrong kinds before the library sees them
+        with pytest.raises(TypeError):
+            rig.pool.load_back_layer(0, torch.from_numpy(h_np), d2_t)
+        with pytest.raises(TypeError):
+            rig.pool.load_back_layer(0, h_t.to(torch.int32), d2_t)
+        with pytest.raises(TypeError):
+            rig.pool.write_back_all_layers(d_t, h_t)
+        with pytest.raises(TypeError):
+            rig.pool.round_trip_check(d_t[::2], d_t[1::2])
+
+        # pinned host lists are readable by the kernels: the same rows land
+        dev0 = rig.dev_np()
+        pin_h = torch.from_numpy(h_np).pin_memory()
+        pin_d = torch.from_numpy(np.ascontiguousarray(d2, dtype=np.int64)).pin_memory()
+        for l in range(SHAPE.layers):
+            assert B.lib.hc_load_back_layer(pool, l, _raw(pin_h), _raw(pin_d), n, None) == B.HC_OK
+        rig.pool.sync()
+        for l in range(SHAPE.layers):
+            O.load_back_layer(rig.geom, l, dev0, rig.host.np, h, d2)
+        for b in range(2):
+            for l in range(SHAPE.layers):
+                assert np.array_equal(rig.dev[b][l].cpu().numpy(), dev0[b][l])
+    finally:
+        if short.value:
+            hip.hipFree.argtypes = [ctypes.c_void_p]
+            hip.hipFree(short)
+        rig.close()
