@@ -172,6 +172,22 @@ int check_device_list(const hc_pool* p, const int64_t* q, int64_t n, const char*
   return HC_OK;
 }
 
+// [q, q + bytes) lies inside one allocation known to HIP.  `required`: an allocation
+// that cannot be looked up is an error (else the extent is left unchecked).
+int check_extent(const void* q, int64_t bytes, bool required, const char* what) {
+  hipDeviceptr_t base = nullptr;
+  size_t size = 0;
+  if (hipMemGetAddressRange(&base, &size, (hipDeviceptr_t)q) != hipSuccess || !base) {
+    (void)hipGetLastError();
+    return required ? set_err(HC_ERR_INVALID, "%s: its allocation could not be found", what) : HC_OK;
+  }
+  const uint64_t end = (uint64_t)(uintptr_t)base + (uint64_t)size;
+  if ((uint64_t)(uintptr_t)q + (uint64_t)bytes > end)
+    return set_err(HC_ERR_INVALID, "%s: %lld bytes are needed, its allocation ends %llu bytes after it", what,
+                   (long long)bytes, (unsigned long long)(end - (uint64_t)(uintptr_t)q));
+  return HC_OK;
+}
+
 // The write-back's host list is read by the CPU: device memory would crash it.
 int check_host_list(const int64_t* q, const char* what) {
   hipPointerAttribute_t attr;
@@ -481,11 +497,19 @@ int hc_pool_create(const hc_pool_desc* desc, hc_pool** out) {
     }
     p->host = (uint8_t*)dptr;
   }
-  for (int b = 0; b < L.nsub; b++)
+  // every buffer the kernels address must hold what the layout puts in it
+  rc = check_extent(desc->host_base, L.host_bytes, false, "host_base");
+  if (rc != HC_OK) return bail(rc);
+  for (int b = 0; b < L.nsub; b++) {
+    const int64_t units = L.gran[b] == HC_PAGE_BLOCKS ? L.S / L.P : L.S;
     for (int l = 0; l < L.L; l++) {
-      rc = check_device_ptr(desc->sub[b].device_layers[l], p->device, "device layer");
+      char what[64];
+      snprintf(what, sizeof(what), "sub-buffer %d layer %d", b, l);
+      rc = check_device_ptr(desc->sub[b].device_layers[l], p->device, what);
+      if (rc == HC_OK) rc = check_extent(desc->sub[b].device_layers[l], units * L.elem[b], true, what);
       if (rc != HC_OK) return bail(rc);
     }
+  }
   // modes.  AUTO write-back is staged whenever the caller brings staging for it: a
   // zero-copy write-back that saturates the host link slows compute on other streams
   // until it barely overlaps, staged write-back leaves that compute alone (measured).
@@ -501,6 +525,8 @@ int hc_pool_create(const hc_pool_desc* desc, hc_pool** out) {
     p->chunk_pages = std::min<int64_t>(desc->staging_bytes / L.stride, (int64_t)1 << 20);
     p->chunk_pages = std::min<int64_t>(p->chunk_pages, std::max<int64_t>(1, kStagingChunkTarget / L.stride));
     if (p->chunk_pages * L.P >= ((int64_t)1 << 31)) p->chunk_pages = (((int64_t)1 << 31) - 1) / L.P;
+    rc = check_extent(desc->staging, p->chunk_pages * L.stride, true, "staging");
+    if (rc != HC_OK) return bail(rc);
   }
   // device tables and scratch
   std::vector<uint64_t> tables((size_t)L.nsub * L.L);

@@ -180,7 +180,9 @@ int hc_host_free(void* ptr);
 /* Validates desc, copies the per-layer pointer tables to device memory, and
  * records the modes.  The pool belongs to the current HIP device: the layer
  * buffers, the staging buffer and copy_stream must be that device's
- * (HC_ERR_INVALID otherwise), and every later call makes it current. */
+ * (HC_ERR_INVALID otherwise), and every later call makes it current.  Each device
+ * layer, the used part of the staging buffer and (when HIP can look it up) the host
+ * pool must fit inside their allocations, else HC_ERR_INVALID. */
 int hc_pool_create(const hc_pool_desc* desc, hc_pool** out);
 
 /* Waits for the pool's copy stream, then frees the handle and its scratch.  NULL is a no-op.

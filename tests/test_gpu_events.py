@@ -364,3 +364,59 @@ def test_index_lists_the_kernels_cannot_read_are_refused():
             hip.hipFree.argtypes = [ctypes.c_void_p]
             hip.hipFree(short)
         rig.close()
+
+
+@pytest.mark.gpu
+def test_pool_buffers_smaller_than_the_layout_are_refused():
+    """hc_pool_create checks that every device layer, the host pool and the staging
+    chunk fit inside their allocations (a kernel would otherwise run past their ends)."""
+    import ctypes
+    say("[events] undersized pool buffers refused")
+    hip = B._hip
+    hip.hipMalloc.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_size_t]
+    hip.hipMalloc.restype = ctypes.c_int
+    hip.hipFree.argtypes = [ctypes.c_void_p]
+    L, P, E, S, H = 2, 16, 64, 1024, 8
+    layer_bytes = S * E
+    bufs = []
+
+    def dmalloc(n):
+        p = ctypes.c_void_p()
+        assert hip.hipMalloc(ctypes.byref(p), n) == 0
+        bufs.append(p)
+        return p.value
+
+    probe, _k = B.make_desc(layers=L, page_size=P, subs=[(T, E, [1] * L)], device_slots=S, host_pages=H)
+    host_need = B.host_pool_bytes(probe)
+    host = B.HostBuffer(host_need)
+    small_host = B.HostBuffer(host_need // 2)
+    stream = torch.cuda.Stream()
+    try:
+        good = [dmalloc(layer_bytes) for _ in range(L)]
+        img = B.staging_page_bytes(probe)
+
+        def create(layers, host_ptr, staging_ptr=0, staging_bytes=0, mode=B.HC_MODE_ZEROCOPY):
+            desc, keep = B.make_desc(layers=L, page_size=P, subs=[(T, E, layers)], device_slots=S, host_pages=H,
+                                     host_ptr=host_ptr, host_bytes=host_need, staging_ptr=staging_ptr,
+                                     staging_bytes=staging_bytes, stream_ptr=stream.cuda_stream,
+                                     write_back_mode=mode)
+            out = ctypes.c_void_p()
+            rc = B.lib.hc_pool_create(ctypes.byref(desc), ctypes.byref(out))
+            if rc == B.HC_OK:
+                B.lib.hc_pool_destroy(out)
+            return rc, B.lib.hc_last_error().decode()
+
+        assert create(good, host.ptr.value)[0] == B.HC_OK
+        rc, msg = create([good[0], dmalloc(layer_bytes - 4096)], host.ptr.value)
+        assert rc == B.HC_ERR_INVALID and "sub-buffer 0 layer 1" in msg and "needed" in msg, msg
+        rc, msg = create(good, small_host.ptr.value)
+        assert rc == B.HC_ERR_INVALID and "host_base" in msg, msg
+        staging = dmalloc(2 * img)
+        assert create(good, host.ptr.value, staging, 2 * img, B.HC_MODE_STAGED)[0] == B.HC_OK
+        rc, msg = create(good, host.ptr.value, staging, 4 * img, B.HC_MODE_STAGED)
+        assert rc == B.HC_ERR_INVALID and "staging" in msg, msg
+    finally:
+        for p in bufs:
+            hip.hipFree(p)
+        small_host.free()
+        host.free()
