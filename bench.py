@@ -67,6 +67,9 @@ def parse():
     ap.add_argument("--beside-compute", action="store_true",
                     help="instead: only the write-back burst next to independent matmuls, zero-copy and staged "
                          "(for a kernel and memory-copy trace)")
+    ap.add_argument("--gather-patterns", action="store_true",
+                    help="instead: the staged gather's rate on the workload's burst with sequential, free-list, "
+                         "page-aligned and random device slots")
     ap.add_argument("--h2h", action="store_true",
                     help="instead: time host-to-host shard dump/load of the shard workload with 1..16 CPU workers")
     ap.add_argument("--max-pinned-gib", type=float, default=64.0,
@@ -150,6 +153,36 @@ def parse_pairs(text: str):
             raise argparse.ArgumentTypeError(f"unknown write-back mode {mode!r}")
         out.append((mode, int(w), int(r)))
     return tuple(out)
+
+
+def gather_patterns(B, torch, np, W, make_pool, shape, burst, h_np, link_bytes, reps=5, rounds=2):
+    """k_gather_stage rate (read + write bytes over its launch time) on the burst's host tokens
+    with four device-slot patterns: one sequential run, the workload's free-list draw, whole
+    device pages, and a random permutation.  Rounds interleave the patterns."""
+    P, S, n = shape.page_size, shape.device_slots, burst.n
+    start = (S - n) // 2 // P * P
+    pats = {"sequential": np.arange(start, start + n, dtype=np.int64),
+            "free_list": burst.device_idx,
+            "page_aligned": W.page_aligned_slots(6, S, P, -(-n // P))[:n],
+            "random": W.permutation_slots(5, S, n)}
+    if any(g == B.HC_PAGE_BLOCKS for g, _ in shape.subs):
+        del pats["random"]  # page blocks move whole device pages only
+    spool = make_pool(B.HC_MODE_STAGED)
+    out = {k: [] for k in pats}
+    for _ in range(rounds):
+        for name, d in pats.items():
+            d_t = torch.from_numpy(np.ascontiguousarray(d, dtype=np.int64)).cuda()
+            spool.write_back_all_layers(d_t, h_np)
+            spool.sync()
+            spool.kernel_time(0, reset=True)
+            for _ in range(reps):
+                spool.write_back_all_layers(d_t, h_np)
+            spool.sync()
+            ng, ms = spool.kernel_time(B.KIND_GATHER)
+            out[name].append(round(2 * link_bytes * reps / (ms * 1e-3) / 1e12, 3))
+            log(f"[bench] gather {name}: {out[name][-1]} TB/s")
+    spool.close()
+    return {k: {"TBps": v} for k, v in out.items()}
 
 
 def relabel_host_pages(h, page_size: int, host_pages: int, seed: int = 7):
@@ -695,6 +728,13 @@ def main():
         return
 
     link_bytes, _ = burst_bytes(shape, burst)
+    if args.gather_patterns:
+        pool.close()
+        rows = gather_patterns(B, torch, np, W, make_pool, shape, burst, h_np, link_bytes)
+        print(json.dumps({"gather_patterns": rows, "workload": shape.name, "chunk_pages": args.staging_pages}),
+              flush=True)
+        host.free()
+        return
     if args.duplex_only:
         pool.close()
         hip = hip_setup(B)
