@@ -381,6 +381,16 @@ class Pool:
         check(lib.hc_load_back_layer(self.handle, layer, _V(_ptr(host_idx)), _V(_ptr(device_idx)), n,
                                      event.handle if event else None), "hc_load_back_layer")
 
+    # The host-pool method names the pages use (hybrid-pool write-back page, host-pool
+    # excerpt; loader-thread page, Motivation), in their argument order, host indices
+    # first.  The device pool is this pool's own device side, so it is no argument.
+    def backup_from_device_all_layer(self, host_indices, device_indices, event: HipEvent | None = None) -> None:
+        self.write_back_all_layers(device_indices, host_indices, event)
+
+    def load_to_device_per_layer(self, host_indices, device_indices, layer_id: int,
+                                 event: HipEvent | None = None) -> None:
+        self.load_back_layer(layer_id, host_indices, device_indices, event)
+
     def capture_load_back(self, host_idx, device_idx, events) -> "LoadBackGraph":
         """Capture the per-layer load-back of (host_idx, device_idx) with one event per
         layer (None entries: no record) into a replayable graph."""

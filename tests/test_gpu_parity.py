@@ -239,3 +239,37 @@ def test_staged_regions_stay_inside_their_chunk(shape):
             d = W.permutation_slots(4, shape.device_slots, h.size)
     finally:
         rig.close()
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("mode", ["zerocopy", "staged"])
+def test_page_method_names(mode):
+    """backup_from_device_all_layer / load_to_device_per_layer (the host-pool names of the
+    pages, host indices first) move what the oracle moves."""
+    from gpu_support import assert_bytes_equal, assert_dev_equal
+    from oracle import oracle as O
+    shape = W.SHAPES["tiny_mha_bf16"]
+    say(f"[parity] page method names, {mode}")
+    rig = Rig(shape, seed=41, staging_pages=3 if mode == "staged" else 0,
+              write_back_mode=B.HC_MODE_STAGED if mode == "staged" else B.HC_MODE_ZEROCOPY)
+    try:
+        d, h = burst(shape, 42, "perm", 7, 5)
+        dev0, host0 = rig.dev_np(), rig.host.np.copy()
+        torch.cuda.synchronize()
+        rig.pool.backup_from_device_all_layer(np.ascontiguousarray(h, dtype=np.int64), cuda_i64(d))
+        rig.pool.sync()
+        want_host = host0.copy()
+        O.write_back(rig.geom, dev0, want_host, d, h)
+        assert_bytes_equal(rig.host.np, want_host, "host pool after backup_from_device_all_layer")
+        d2 = fresh(shape, d, 43)
+        ev = B.HipEvent()
+        for l in range(shape.layers):
+            rig.pool.load_to_device_per_layer(cuda_i64(h), cuda_i64(d2), l, ev if l == shape.layers - 1 else None)
+        ev.synchronize()
+        rig.pool.sync()
+        want = [[a.copy() for a in row] for row in dev0]
+        for l in range(shape.layers):
+            O.load_back_layer(rig.geom, l, want, want_host, h, d2)
+        assert_dev_equal(rig.dev_np(), want, "device pool after load_to_device_per_layer")
+    finally:
+        rig.close()
