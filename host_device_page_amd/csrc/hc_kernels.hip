@@ -28,6 +28,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <vector>
+
 #include "hc_internal.h"
 
 namespace hc {
@@ -218,27 +220,26 @@ __host__ __device__ __forceinline__ int64_t sub_positions(const SubGeom& s, int6
   return s.gran == HC_PAGE_BLOCKS ? (n + blk_stride - 1) / blk_stride : n;
 }
 
-// Page blocks walked with the block stride take tile_n >> HC_BLOCK_TILE_SHIFT blocks per
-// unit (at least 1).  Measured on the 78-layer MLA + indexer load-back: a full tile of
-// 256 blocks (2.1 MiB per unit, 4 units per layer) 1.56 ms per layer, the token-strided
-// walk 1.50 ms, 64 blocks per unit 1.47 ms (99 % of the host link), 32 or 16 the same.
+// Page blocks walked with the block stride take blk_tile blocks per unit, chosen by the
+// launcher so that the blocks alone give about one unit per workgroup, at most
+// kTile >> HC_BLOCK_TILE_SHIFT.  Measured on the 78-layer MLA + indexer load-back: at the
+// full 1024-page burst a fixed 256 blocks per unit (2.1 MiB, 4 units per layer) gave
+// 1.56 ms per layer, the token-strided walk 1.50 ms, 64 blocks 1.47 ms (99 % of the host
+// link), 32 or 16 the same; but a fixed 64 left a 64-page burst's blocks in one unit that
+// one workgroup read alone (147 us per layer against 101 us token-strided).
 #ifndef HC_BLOCK_TILE_SHIFT
 #define HC_BLOCK_TILE_SHIFT 2
 #endif
 #ifndef HC_BLOCK_STRIDE_ON
 #define HC_BLOCK_STRIDE_ON 1
 #endif
-__host__ __device__ __forceinline__ int sub_tile(const SubGeom& s, int blk_stride, int tile_n) {
-  if (s.gran == HC_PAGE_BLOCKS && blk_stride > 1) {
-    const int t = tile_n >> HC_BLOCK_TILE_SHIFT;
-    return t > 0 ? t : 1;
-  }
-  return tile_n;
+__host__ __device__ __forceinline__ int sub_tile(const SubGeom& s, int blk_stride, int tile_n, int blk_tile) {
+  return (s.gran == HC_PAGE_BLOCKS && blk_stride > 1) ? blk_tile : tile_n;
 }
 
 __host__ __device__ __forceinline__ int64_t sub_units(const SubGeom& s, int64_t n, int blk_stride, int tile_n,
-                                                      int64_t mult) {
-  const int t = sub_tile(s, blk_stride, tile_n);
+                                                      int blk_tile, int64_t mult) {
+  const int t = sub_tile(s, blk_stride, tile_n, blk_tile);
   return (sub_positions(s, n, blk_stride) + t - 1) / t * mult;
 }
 
@@ -246,13 +247,13 @@ __host__ __device__ __forceinline__ int64_t sub_units(const SubGeom& s, int64_t 
 // sub-buffers come first: with the block stride their units are the largest (a tile of
 // whole-page blocks), and taken last they left a few workgroups running alone at the
 // end of a layer.
-__device__ __forceinline__ int unit_sub(const Geom& g, int64_t n, int blk_stride, int tile_n, int64_t mult,
-                                        int64_t unit, int64_t* rem) {
+__device__ __forceinline__ int unit_sub(const Geom& g, int64_t n, int blk_stride, int tile_n, int blk_tile,
+                                        int64_t mult, int64_t unit, int64_t* rem) {
   int64_t acc = 0;
   for (int pass = 0; pass < 2; pass++) {
     for (int b = 0; b < g.nsub; b++) {
       if ((g.sub[b].gran == HC_PAGE_BLOCKS) != (pass == 0)) continue;
-      const int64_t ub = sub_units(g.sub[b], n, blk_stride, tile_n, mult);
+      const int64_t ub = sub_units(g.sub[b], n, blk_stride, tile_n, blk_tile, mult);
       if (unit < acc + ub) {
         *rem = unit - acc;
         return b;
@@ -261,7 +262,7 @@ __device__ __forceinline__ int unit_sub(const Geom& g, int64_t n, int blk_stride
     }
   }
   // not reached for unit < units; a position past sub-buffer 0's last leaves every lane idle
-  *rem = sub_units(g.sub[0], n, blk_stride, tile_n, mult);
+  *rem = sub_units(g.sub[0], n, blk_stride, tile_n, blk_tile, mult);
   return 0;
 }
 
@@ -330,18 +331,19 @@ __global__ __launch_bounds__(kThreads) void k_zc_write(Geom g, const int64_t* __
                                                        const int64_t* __restrict__ host_idx,
                                                        const int32_t* __restrict__ tok_list, int64_t count,
                                                        uint8_t* __restrict__ host, int32_t* __restrict__ err,
-                                                       int64_t units, int tile_shift, int blk_stride) {
+                                                       int64_t units, int tile_shift, int blk_stride,
+                                                       int blk_tile) {
   __shared__ uint64_t s_src[kTile];
   __shared__ uint64_t s_dst[kTile];
   __shared__ int s_wave[kWaves];
   const int tile_n = kTile >> tile_shift;
   for (int64_t unit = blockIdx.x; unit < units; unit += gridDim.x) {
     int64_t rem;
-    const int b = unit_sub(g, count, blk_stride, tile_n, g.L, unit, &rem);
+    const int b = unit_sub(g, count, blk_stride, tile_n, blk_tile, g.L, unit, &rem);
     const int64_t tile = rem / g.L;
     const int l = (int)(rem - tile * g.L);
     const SubGeom& s = g.sub[b];
-    const int st = sub_tile(s, blk_stride, tile_n);
+    const int st = sub_tile(s, blk_stride, tile_n, blk_tile);
     const int64_t j = tile * st + threadIdx.x;
     const int stride = s.gran == HC_PAGE_BLOCKS ? blk_stride : 1;
     bool keep = false;
@@ -384,16 +386,17 @@ __global__ __launch_bounds__(kThreads) void k_zc_write(Geom g, const int64_t* __
 __global__ __launch_bounds__(kThreads) void k_zc_read(Geom g, int32_t layer, const int64_t* __restrict__ host_idx,
                                                       const int64_t* __restrict__ dev_idx, int64_t n,
                                                       const uint8_t* __restrict__ host, int32_t* __restrict__ err,
-                                                      int64_t units, int tile_shift, int blk_stride) {
+                                                      int64_t units, int tile_shift, int blk_stride,
+                                                      int blk_tile) {
   __shared__ uint64_t s_src[kTile];
   __shared__ uint64_t s_dst[kTile];
   __shared__ int s_wave[kWaves];
   const int tile_n = kTile >> tile_shift;
   for (int64_t unit = blockIdx.x; unit < units; unit += gridDim.x) {
     int64_t tile;
-    const int b = unit_sub(g, n, blk_stride, tile_n, 1, unit, &tile);
+    const int b = unit_sub(g, n, blk_stride, tile_n, blk_tile, 1, unit, &tile);
     const SubGeom& s = g.sub[b];
-    const int st = sub_tile(s, blk_stride, tile_n);
+    const int st = sub_tile(s, blk_stride, tile_n, blk_tile);
     const int64_t j = tile * st + threadIdx.x;
     const int64_t i = j * (s.gran == HC_PAGE_BLOCKS ? blk_stride : 1);
     bool keep = false;
@@ -535,20 +538,86 @@ hipError_t launch_gather_stage(const Geom& g, const int64_t* dev_idx, const int6
 }
 
 // Units of a zero-copy launch over list positions [0, count): summed over sub-buffers.
-static int64_t zc_units(const Geom& g, int64_t count, int blk_stride, int tile_n, int64_t mult) {
+static int64_t zc_units(const Geom& g, int64_t count, int blk_stride, int tile_n, int blk_tile, int64_t mult) {
   int64_t units = 0;
-  for (int b = 0; b < g.nsub; b++) units += sub_units(g.sub[b], count, blk_stride, tile_n, mult);
+  for (int b = 0; b < g.nsub; b++) units += sub_units(g.sub[b], count, blk_stride, tile_n, blk_tile, mult);
   return units;
 }
 
-// Tile shift: the smallest (at most kMaxTileShift, i.e. 4-position tiles) whose
-// kTile >> shift tiles give at least `max_ctas` units.
-constexpr int kMaxTileShift = 6;
+// Blocks per page-block unit under the block stride: enough units for the grid (blocks
+// x mult / max_ctas, rounded up), at most kTile >> HC_BLOCK_TILE_SHIFT.
+static int block_tile_for(int64_t count, int blk_stride, int64_t mult, int32_t max_ctas) {
+  constexpr int64_t kMaxBlockTile = kTile >> HC_BLOCK_TILE_SHIFT;
+  if (blk_stride <= 1) return (int)kMaxBlockTile;  // not used: blocks walk the token tiles
+  const int64_t blocks = (count + blk_stride - 1) / blk_stride;
+  const int64_t ctas = max_ctas > 0 ? max_ctas : 1;
+  const int64_t t = (blocks * mult + ctas - 1) / ctas;
+  return (int)(t < 1 ? 1 : (t > kMaxBlockTile ? kMaxBlockTile : t));
+}
+static_assert((kTile >> HC_BLOCK_TILE_SHIFT) >= 1 && (kTile >> HC_BLOCK_TILE_SHIFT) <= kTile,
+              "a block unit fits the unit's LDS lists");
 
-static int tile_shift_for(const Geom& g, int64_t count, int blk_stride, int64_t mult, int32_t max_ctas) {
-  int shift = 0;
-  while (shift < kMaxTileShift && zc_units(g, count, blk_stride, kTile >> shift, mult) < (int64_t)max_ctas) shift++;
-  return shift;
+// Tile shift for a small burst.  Units go to workgroups round-robin (unit u to
+// workgroup u % grid, in the kernels' order: page blocks first, then sub-buffer, tile,
+// layer), and one workgroup moves only ~7 GB/s over the host link, so a launch lasts
+// about as long as its busiest workgroup.  The shift (0 .. kMaxTileShift, tiles of
+// kTile >> shift list positions) is the one whose busiest workgroup carries the fewest
+// bytes, counting a fixed intake per unit.  Measured before this model, on the 78-layer
+// MLA + indexer load-back: "shrink until the units fill the grid" left 17 units on 16
+// workgroups for a 1-page burst (11.3 us per layer, 8.1 us when each workgroup takes one
+// unit), and counting page-block units toward the grid left a 16-page burst's latent rows
+// in 4 units of 256 tokens (44 us per layer against 32 us).
+constexpr int kMaxTileShift = 6;
+constexpr int64_t kUnitIntakeBytes = 8192;  // the intake's cost, in bytes of copying
+
+static int64_t busiest_workgroup_bytes(const Geom& g, int64_t count, int bs, int tile_n, int bt, int64_t mult,
+                                       int64_t grid) {
+  std::vector<int64_t> load((size_t)grid, 0);
+  int64_t u = 0;
+  for (int pass = 0; pass < 2; pass++) {
+    for (int b = 0; b < g.nsub; b++) {
+      const SubGeom& s = g.sub[b];
+      if ((s.gran == HC_PAGE_BLOCKS) != (pass == 0)) continue;
+      const int t = sub_tile(s, bs, tile_n, bt);
+      const int64_t pos = sub_positions(s, count, bs);
+      for (int64_t j0 = 0; j0 < pos; j0 += t) {
+        int64_t items = pos - j0 < t ? pos - j0 : t;
+        if (s.gran == HC_PAGE_BLOCKS && bs <= 1) items = (items + g.P - 1) / g.P;  // one block per page
+        const int64_t bytes = items * s.elem + kUnitIntakeBytes;
+        for (int64_t l = 0; l < mult; l++) load[(size_t)(u++ % grid)] += bytes;
+      }
+    }
+  }
+  int64_t most = 0;
+  for (int64_t x : load) most = x > most ? x : most;
+  return most;
+}
+
+static int tile_shift_for(const Geom& g, int64_t count, int blk_stride, int blk_tile, int64_t mult,
+                          int32_t max_ctas) {
+  // under the block stride, page blocks have their own units (block_tile_for spreads them)
+  auto row_units = [&](int tile_n) {
+    int64_t n = 0;
+    for (int b = 0; b < g.nsub; b++)
+      if (blk_stride <= 1 || g.sub[b].gran != HC_PAGE_BLOCKS)
+        n += sub_units(g.sub[b], count, blk_stride, tile_n, blk_tile, mult);
+    return n;
+  };
+  const int64_t ctas = max_ctas > 0 ? max_ctas : 1;
+  if (row_units(kTile) == 0 || row_units(kTile) >= 4 * ctas) return 0;  // no rows, or plenty of full tiles
+  int best = 0;
+  int64_t best_bytes = -1;
+  for (int shift = 0; shift <= kMaxTileShift; shift++) {
+    if (shift > 0 && row_units(kTile >> (shift - 1)) >= 4 * ctas) break;  // finer tiles only add intakes
+    const int64_t units = zc_units(g, count, blk_stride, kTile >> shift, blk_tile, mult);
+    const int64_t grid = units < ctas ? units : ctas;
+    const int64_t most = busiest_workgroup_bytes(g, count, blk_stride, kTile >> shift, blk_tile, mult, grid);
+    if (best_bytes < 0 || most < best_bytes) {
+      best = shift;
+      best_bytes = most;
+    }
+  }
+  return best;
 }
 
 // Page blocks take only the positions k * P when the list is known to hold whole pages
@@ -566,11 +635,12 @@ hipError_t launch_zc_write(const Geom& g, const int64_t* dev_idx, const int64_t*
                            hipStream_t stream) {
   if (count <= 0) return hipSuccess;
   const int bs = block_stride(g, tok_list == nullptr);
-  const int shift = tile_shift_for(g, count, bs, g.L, max_ctas);
-  const int64_t units = zc_units(g, count, bs, kTile >> shift, g.L);
+  const int bt = block_tile_for(count, bs, g.L, max_ctas);
+  const int shift = tile_shift_for(g, count, bs, bt, g.L, max_ctas);
+  const int64_t units = zc_units(g, count, bs, kTile >> shift, bt, g.L);
   const int64_t grid = units < max_ctas ? units : max_ctas;
   return launch(k_zc_write, dim3((unsigned)grid), t, stream, g, dev_idx, host_idx, tok_list, count, host, err, units,
-                shift, bs);
+                shift, bs, bt);
 }
 
 hipError_t launch_zc_read(const Geom& g, int32_t layer, const int64_t* host_idx, const int64_t* dev_idx, int64_t n,
@@ -578,11 +648,12 @@ hipError_t launch_zc_read(const Geom& g, int32_t layer, const int64_t* host_idx,
                           hipStream_t stream) {
   if (n <= 0) return hipSuccess;
   const int bs = block_stride(g, true);
-  const int shift = tile_shift_for(g, n, bs, 1, max_ctas);
-  const int64_t units = zc_units(g, n, bs, kTile >> shift, 1);
+  const int bt = block_tile_for(n, bs, 1, max_ctas);
+  const int shift = tile_shift_for(g, n, bs, bt, 1, max_ctas);
+  const int64_t units = zc_units(g, n, bs, kTile >> shift, bt, 1);
   const int64_t grid = units < max_ctas ? units : max_ctas;
   return launch(k_zc_read, dim3((unsigned)grid), t, stream, g, layer, host_idx, dev_idx, n, host, err, units, shift,
-                bs);
+                bs, bt);
 }
 
 hipError_t launch_zero_pads(uint8_t* base, const int64_t* pages, int64_t npages, int64_t stride, int64_t off,
