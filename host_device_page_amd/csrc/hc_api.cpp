@@ -378,7 +378,7 @@ int hc_desc_check(const hc_pool_desc* desc) {
                    "staged load-back is not provided: per-(page, layer) copy-engine transfers run far below "
                    "the host-link rate, the zero-copy kernel does not");
   if (desc->flags & ~(HC_FLAG_VALIDATE | HC_FLAG_PROFILE)) return set_err(HC_ERR_INVALID, "unknown flags");
-  if (desc->max_ctas < 0) return set_err(HC_ERR_INVALID, "max_ctas must be >= 0");
+  if (desc->max_ctas < 0 || desc->max_ctas > 65536) return set_err(HC_ERR_INVALID, "max_ctas must be in [0, 65536]");
   if (!desc->host_base) return set_err(HC_ERR_INVALID, "host_base is null");
   if (((uintptr_t)desc->host_base) % 16 != 0) return set_err(HC_ERR_UNSUPPORTED, "host_base must be 16-byte aligned");
   if (desc->host_bytes < L.host_bytes)

@@ -137,7 +137,7 @@ typedef struct hc_pool_desc {
   int32_t write_back_mode; /* HC_MODE_* */
   int32_t load_back_mode;  /* HC_MODE_* (load-back is always zero-copy in this version) */
   int32_t flags;           /* HC_FLAG_* */
-  int32_t max_ctas;        /* cap on workgroups of the zero-copy kernels; 0 = library default (16:
+  int32_t max_ctas;        /* cap on workgroups of the zero-copy kernels, 0..65536; 0 = library default (16:
                               the link saturates with 8, and idle CUs stay free for compute).  With a
                               write-back and a load-back running at once (two pools, two streams) the
                               caps decide how the link is shared: beside a staged write-back, a load-back
