@@ -218,3 +218,54 @@ def test_loader_refuses_a_graph_it_could_not_flag():
             graph.close()
         other_rig.close()
         rig.close()
+
+
+@pytest.mark.gpu
+def test_start_event_orders_the_producers_index_list_before_the_burst():
+    """The producer writes the slot list on its own stream after a bounded spin and records
+    the start event; the loader's transfer stream waits on it, so the kernels read the new
+    list, not the sentinel the buffer held before (loader-thread page, Modifications: the
+    index move runs after the start-event wait).  Negative control: without the start
+    event the same burst reads the sentinel, so the check has teeth."""
+    say("[loader] start event orders the index list")
+    rig = Rig(SHAPE, seed=16)
+    loader = None
+    try:
+        L, n_pages = SHAPE.layers, 24
+        h = W.whole_page_tokens(W.host_pages(21, SHAPE.host_pages, n_pages), SHAPE.page_size)
+        d = W.permutation_slots(22, SHAPE.device_slots, h.size)
+        rig.pool.write_back_all_layers(cuda_i64(d), h)
+        rig.pool.sync()
+        used = d
+        lists = []
+        for seed in (23, 24, 25, 26):  # real and sentinel lists of the two runs, all disjoint
+            lists.append(W.permutation_slots(seed, SHAPE.device_slots, h.size, exclude=used))
+            used = np.concatenate([used, lists[-1]])
+        h_t = cuda_i64(h)
+        producer = torch.cuda.Stream()
+        loader = B.Loader(rig.pool, L, asynchronous=True)
+        for k, use_start in enumerate((True, False)):
+            real, sentinel = lists[2 * k], lists[2 * k + 1]
+            real_t, d_buf = cuda_i64(real), cuda_i64(sentinel)  # the buffer holds the sentinel at hand-over
+            events = [B.HipEvent() for _ in range(L)]
+            start = B.HipEvent()
+            torch.cuda.synchronize()
+            producer.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(producer):
+                torch.cuda._sleep(50_000_000)  # bounded spin: the producer is still writing the list
+                d_buf.copy_(real_t)
+                start.record(producer)
+            burst = loader.submit(h_t, d_buf, h.size, events, start_event=start if use_start else None)
+            burst.wait()
+            burst.release()
+            torch.cuda.synchronize()
+            at_real = all([int(x) for x in dev_sums(rig, l, real_t)] == host_sums(rig, h, l) for l in range(L))
+            if use_start:
+                assert at_real, "the burst did not wait for the producer's start event"
+            else:
+                assert not at_real, "negative control: the burst without a start event read the new list anyway"
+        rig.pool.sync()
+    finally:
+        if loader is not None:
+            loader.close()
+        rig.close()
