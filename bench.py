@@ -46,7 +46,8 @@ def parse():
     ap.add_argument("--write-back-mode", choices=["auto", "zerocopy", "staged"], default="zerocopy",
                     help="mode of the timed write-back (zero-copy: the highest burst rate; the staged mode, "
                          "which leaves concurrent compute alone, is measured beside it)")
-    ap.add_argument("--staging-pages", type=int, default=32)
+    ap.add_argument("--staging-pages", type=int, default=0,
+                    help="staging buffer in page images (0 = as many as the library's 256 MB chunk cap uses)")
     ap.add_argument("--max-ctas", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle sample")
     ap.add_argument("--cpu-threads", type=int, default=0,
@@ -78,6 +79,10 @@ def parse():
                     help="run one plain device-to-device copy of this size first (a known-size "
                          "reference for the FETCH_SIZE / WRITE_SIZE counters)")
     return ap.parse_args()
+
+
+# The library caps a staging chunk at this many bytes of page images (MI355X's Infinity Cache).
+STAGING_CHUNK_BYTES = 256 << 20
 
 
 def memcpy_peak(hip, host_ptr: int, dev_ptr: int, nbytes: int, stream_ptr: int, h2d: bool, reps: int = 5) -> float:
@@ -677,7 +682,10 @@ def main():
     wb_mode = {"auto": B.HC_MODE_AUTO, "zerocopy": B.HC_MODE_ZEROCOPY, "staged": B.HC_MODE_STAGED}[args.write_back_mode]
     staging = None
     if wb_mode == B.HC_MODE_STAGED or not args.no_staged_probe:
-        staging = torch.empty(args.staging_pages * B.staging_page_bytes(probe), dtype=torch.uint8, device="cuda")
+        img = B.staging_page_bytes(probe)
+        if args.staging_pages <= 0:
+            args.staging_pages = max(1, STAGING_CHUNK_BYTES // img)
+        staging = torch.empty(args.staging_pages * img, dtype=torch.uint8, device="cuda")
     layers = [[t[l] for l in range(L)] for t in dev]
 
     def make_pool(mode, max_ctas=None, flags=B.HC_FLAG_PROFILE, stream_=None):
