@@ -543,11 +543,6 @@ int hc_pool_create(const hc_pool_desc* desc, hc_pool** out) {
                      p->stream) != hipSuccess ||
       hipMemsetAsync(p->d_err, 0, 64, p->stream) != hipSuccess)
     return bail(set_err(HC_ERR_HIP, "initial copies failed"));
-  if (p->staging && L.stride > L.payload) {
-    // staging page images carry the shard pad, which stays zero
-    if (hipMemsetAsync(p->staging, 0, (size_t)(p->chunk_pages * L.stride), p->stream) != hipSuccess)
-      return bail(set_err(HC_ERR_HIP, "staging clear failed"));
-  }
   if (hipStreamSynchronize(p->stream) != hipSuccess) return bail(set_err(HC_ERR_HIP, "stream sync failed"));
   p->planner.reset(L);
   fill_geom(p);
@@ -661,6 +656,15 @@ int hc_write_back_all_layers(hc_pool* p, const int64_t* device_idx, const int64_
   p->plan_cur ^= 1;
   hipError_t e = hipSuccess;
   if (staged) {
+    if (L.stride > L.payload && !p->planner.regions.empty()) {
+      // Staging page images carry the shard's zero pad, and a whole page leaves staging with
+      // it.  The gathers never write the pad, but another pool may have used this staging
+      // buffer since the last burst, so the pads of the images this burst fills are cleared.
+      // (untimed: a launch-stamped kernel ahead of the region copies turned them into blit kernels)
+      e = hc::launch_zero_pads(p->staging, nullptr, p->planner.max_chunk_slots(), L.stride, L.payload,
+                               L.stride - L.payload, hc::LaunchTimer{}, p->stream);
+      if (e != hipSuccess) return finish(set_err(HC_ERR_HIP, "staging pad launch failed: %s", hipGetErrorString(e)));
+    }
     for (const hc::Chunk& c : p->planner.chunks) {
       {
         // Recorded events, not launch-stamped ones: right after a launch-stamped kernel the

@@ -101,7 +101,9 @@ void Planner::plan_staged(const int64_t* h, int64_t n, int64_t chunk_pages, uint
   int64_t nslots = 0, t0 = 0;
   *nz = 0;
   *npads = 0;
+  max_slots_ = 0;
   auto close_chunk = [&](int64_t t1) {
+    if (nslots > max_slots_) max_slots_ = nslots;
     const size_t r0 = regions.size();
     chunk_first_region_ = r0;
     for (int64_t s = 0; s < nslots; s++) {

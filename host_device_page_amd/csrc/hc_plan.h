@@ -52,12 +52,15 @@ class Planner {
 
   std::vector<Region> regions;
   std::vector<Chunk> chunks;
+  // Staging slots the fullest chunk of the last staged plan uses.
+  int64_t max_chunk_slots() const { return max_slots_; }
 
  private:
   void emit_region(uint8_t* dst, const uint8_t* src, int64_t len);
 
   Layout lay_;
   size_t chunk_first_region_ = 0;    // regions before this index belong to closed chunks
+  int64_t max_slots_ = 0;
   std::vector<int32_t> page_slot_;   // [H] staging slot of a page in the open chunk, -1 otherwise
   std::vector<uint64_t> seen_;       // bitmap over host tokens (distinctness)
   std::vector<uint64_t> page_seen_;  // bitmap over host pages

@@ -130,7 +130,9 @@ typedef struct hc_pool_desc {
   void* staging;        /* device memory for staged write-back (HC_MODE_STAGED, or HC_MODE_AUTO when it
                            holds at least one page image); NULL when no staged mode is used.  The
                            pool writes it during every staged write-back: pools whose transfers can
-                           run at the same time (other streams) need their own staging buffers. */
+                           run at the same time (other streams) need their own staging buffers.
+                           Pools used one after the other may share one: each staged burst rewrites
+                           what it sends, shard pads included. */
   int64_t staging_bytes;/* size of staging; the chunk is staging_bytes / hc_staging_page_bytes pages,
                            capped so that one chunk fits the 256 MB Infinity Cache (at least 1 page) */
   void* copy_stream;    /* hipStream_t every transfer of this pool is enqueued on (NULL: null stream) */

@@ -273,3 +273,45 @@ def test_page_method_names(mode):
         assert_dev_equal(rig.dev_np(), want, "device pool after load_to_device_per_layer")
     finally:
         rig.close()
+
+
+@pytest.mark.gpu
+def test_shard_pads_stay_zero_when_staging_is_shared():
+    """A shard pool's staging images carry the zero pad of every whole shard they send.
+    Another pool using the same staging buffer between its bursts (or anything else
+    writing there) must not leak into the host shards' pads."""
+    from gpu_support import assert_bytes_equal
+    from oracle import oracle as O
+    shape = S("shared_staging_pad", 3, 16, [(T, 1024), (T, 128)], 4096, 40, SH)
+    other = S("shared_staging_rows", 2, 16, [(T, 4096)], 4096, 40)
+    say("[parity] shard pads with a shared staging buffer")
+    rig = Rig(shape, seed=51, staging_pages=3, write_back_mode=B.HC_MODE_STAGED)
+    orig = Rig(other, seed=52, fill_device=True)
+    opool = None
+    try:
+        # a page-first pool over other buffers, staged through the shard pool's staging buffer
+        opool = B.Pool(layers=other.layers, page_size=other.page_size, subs=list(other.subs),
+                       device_slots=other.device_slots, host_pages=other.host_pages,
+                       device_layers=[[orig.dev[b][l] for l in range(other.layers)] for b in range(1)],
+                       host=orig.host, stream=rig.stream, staging=rig.staging, write_back_mode=B.HC_MODE_STAGED)
+        for r, scribble in enumerate(["none", "fill", "other pool"]):
+            if scribble == "fill":
+                rig.staging.fill_(0xEE)
+            elif scribble == "other pool":
+                pg = W.host_pages(60, other.host_pages, 5)
+                oh = W.whole_page_tokens(pg, other.page_size)
+                opool.write_back_all_layers(cuda_i64(W.permutation_slots(61, other.device_slots, oh.size)), oh)
+                opool.sync()
+            d, h = burst(shape, 70 + r, "perm", 7)
+            dev0, host0 = rig.dev_np(), rig.host.np.copy()
+            torch.cuda.synchronize()
+            rig.pool.write_back_all_layers(cuda_i64(d), np.ascontiguousarray(h, dtype=np.int64))
+            rig.pool.sync()
+            want = host0.copy()
+            O.write_back(rig.geom, dev0, want, d, h)
+            assert_bytes_equal(rig.host.np, want, f"host shards after a write-back (staging scribbled: {scribble})")
+    finally:
+        if opool is not None:
+            opool.close()
+        orig.close()
+        rig.close()
