@@ -1,6 +1,6 @@
 """Randomized parity sweep: many small random pools (layers, page size, row and block
-sizes, layouts, modes, partial pages, slot patterns), each compared byte for byte
-with the oracle after a write-back and a per-layer load-back."""
+sizes, layouts, modes, partial pages, slot patterns, zero-copy grid caps), each
+compared byte for byte with the oracle after a write-back and a per-layer load-back."""
 import numpy as np
 import pytest
 
@@ -46,16 +46,18 @@ def random_case(seed):
         d2 = rng.choice(np.setdiff1d(np.arange(S), d), size=h.size, replace=False).astype(np.int64)
     mode = B.HC_MODE_STAGED if rng.random() < 0.5 else B.HC_MODE_ZEROCOPY
     staging_pages = int(rng.integers(1, 6))
-    return shape, d, h, d2, mode, staging_pages
+    # the zero-copy grid cap (0 = the library default) from a stream of its own, so the cases above stay as they were
+    max_ctas = int(np.random.default_rng(5000 + seed).choice([0, 0, 1, 2, 3, 5, 8, 16, 33, 64, 256]))
+    return shape, d, h, d2, mode, staging_pages, max_ctas
 
 
 @pytest.mark.gpu
 @pytest.mark.parametrize("seed", range(600))
 def test_random_pool(seed):
-    shape, d, h, d2, mode, staging_pages = random_case(seed)
+    shape, d, h, d2, mode, staging_pages, max_ctas = random_case(seed)
     say(f"[random {seed}] L={shape.layers} P={shape.page_size} subs={shape.subs} layout={shape.layout} "
-        f"align={shape.align} n={h.size} mode={mode}")
-    rig = Rig(shape, seed=seed, write_back_mode=mode, staging_pages=staging_pages)
+        f"align={shape.align} n={h.size} mode={mode} max_ctas={max_ctas}")
+    rig = Rig(shape, seed=seed, write_back_mode=mode, staging_pages=staging_pages, max_ctas=max_ctas)
     try:
         write_back_and_check(rig, d, h)
         load_back_and_check(rig, h, d2)
