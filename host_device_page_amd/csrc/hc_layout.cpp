@@ -74,6 +74,10 @@ int layout_from_desc(const hc_pool_desc* d, Layout* out, char* msg, size_t len) 
   }
   if (L.has_blocks && L.S % L.P != 0)
     return fail(msg, len, HC_ERR_INVALID, "device_slots must be a multiple of page_size with page-block sub-buffers");
+  for (int b = 0; b < L.nsub; b++) {
+    int64_t layer_bytes;  // one device layer: the extent hc_pool_create checks against its allocation
+    if (!mul_ok(L.S, L.elem[b], &layer_bytes)) return fail(msg, len, HC_ERR_INVALID, "device layer size overflows");
+  }
   int64_t tokens;
   if (!mul_ok(L.H, L.P, &tokens)) return fail(msg, len, HC_ERR_INVALID, "host_pages * page_size overflows");
   // one page of each sub-buffer over all layers

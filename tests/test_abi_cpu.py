@@ -67,6 +67,7 @@ def test_desc_check_accepts_valid():
     (dict(load_back_mode=B.HC_MODE_STAGED), B.HC_ERR_UNSUPPORTED, "staged load-back"),
     (dict(write_back_mode=9), B.HC_ERR_INVALID, "mode"),
     (dict(flags=64), B.HC_ERR_INVALID, "flags"),
+    (dict(device_slots=1 << 60), B.HC_ERR_INVALID, "device layer size overflows"),
     (dict(max_ctas=-1), B.HC_ERR_INVALID, "max_ctas"),
     (dict(max_ctas=65537), B.HC_ERR_INVALID, "max_ctas"),
 ])
