@@ -19,11 +19,12 @@
 // batches before their stores to keep enough bytes in flight (depth per kernel
 // below).
 //
-// The zero-copy kernels shrink the tile to kTile >> tile_shift tokens when a
-// burst is too small to give every workgroup of the grid a unit: a small burst
-// then still spreads over enough workgroups to keep the host link busy (one
-// workgroup alone reads only ~7 GB/s over it), and each unit still moves whole
-// rows, so a run of adjacent rows stays one contiguous stream on the link.
+// The zero-copy kernels shrink the tile to kTile >> tile_shift tokens for a
+// small burst, so that it still spreads over enough workgroups to keep the host
+// link busy (one workgroup alone reads only ~7 GB/s over it); the launcher picks
+// the shift whose busiest workgroup carries the fewest bytes.  Each unit still
+// moves whole rows, so a run of adjacent rows stays one contiguous stream on the
+// link.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
