@@ -539,9 +539,11 @@ int hc_pool_create(const hc_pool_desc* desc, hc_pool** out) {
   if (hipHostMalloc((void**)&p->h_counter, 64, hipHostMallocDefault) != hipSuccess)
     return bail(set_err(HC_ERR_HIP, "hipHostMalloc failed"));
   p->h_err = (int32_t*)((uint8_t*)p->h_counter + 32);
+  // d_err: [0, 4) error bits, [8, 16) smallest flagged list position (none: all ones), [32, 40) counter
   if (hipMemcpyAsync(p->d_tables, tables.data(), tables.size() * sizeof(uint64_t), hipMemcpyHostToDevice,
                      p->stream) != hipSuccess ||
-      hipMemsetAsync(p->d_err, 0, 64, p->stream) != hipSuccess)
+      hipMemsetAsync(p->d_err, 0, 64, p->stream) != hipSuccess ||
+      hipMemsetAsync((uint8_t*)p->d_err + 8, 0xFF, 8, p->stream) != hipSuccess)
     return bail(set_err(HC_ERR_HIP, "initial copies failed"));
   if (hipStreamSynchronize(p->stream) != hipSuccess) return bail(set_err(HC_ERR_HIP, "stream sync failed"));
   p->planner.reset(L);
@@ -589,15 +591,19 @@ int hc_pool_sync(hc_pool* p) {
   std::lock_guard<std::recursive_mutex> lock(p->mu);
   int rc = use_device(p);
   if (rc != HC_OK) return rc;
-  HIP_TRY(hipMemcpyAsync(p->h_err, p->d_err, sizeof(int32_t), hipMemcpyDeviceToHost, p->stream));
+  HIP_TRY(hipMemcpyAsync(p->h_err, p->d_err, 16, hipMemcpyDeviceToHost, p->stream));
   HIP_TRY(hipStreamSynchronize(p->stream));
   const int32_t e = *p->h_err;
   if (e) {
+    uint64_t pos = 0;
+    memcpy(&pos, (const uint8_t*)p->h_err + 8, sizeof(pos));
     HIP_TRY(hipMemsetAsync(p->d_err, 0, sizeof(int32_t), p->stream));
+    HIP_TRY(hipMemsetAsync((uint8_t*)p->d_err + 8, 0xFF, 8, p->stream));
     HIP_TRY(hipStreamSynchronize(p->stream));
-    return set_err(HC_ERR_DEVICE, "device-side check flagged an index list (code %d:%s%s)", e,
+    return set_err(HC_ERR_DEVICE,
+                   "device-side check flagged an index list (code %d:%s%s first flagged list position %llu)", e,
                    (e & 1) ? " index out of range;" : "",
-                   (e & 2) ? " page-block rows not one whole device page;" : "");
+                   (e & 2) ? " page-block rows not one whole device page;" : "", (unsigned long long)pos);
   }
   return HC_OK;
 }

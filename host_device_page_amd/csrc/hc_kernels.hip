@@ -201,6 +201,13 @@ __device__ __forceinline__ int64_t dev_off(const SubGeom& s, int64_t d, int P) {
   return (s.gran == HC_TOKEN_ROWS ? d : d / P) * s.elem;
 }
 
+// A bad index list: sets bit `bit` of the error word and keeps the smallest list position
+// flagged since the last report in the uint64 that follows the word at byte 8.
+__device__ __forceinline__ void flag_bad(int32_t* err, int bit, int64_t pos) {
+  atomicOr(err, bit);
+  atomicMin(reinterpret_cast<unsigned long long*>(err + 2), (unsigned long long)pos);
+}
+
 // HC_FLAG_VALIDATE for page-block sub-buffers: token i must either start a page on
 // both sides (h % P == 0 with d % P == 0) or continue the previous token's run on both
 // sides (d = d[i-1] + 1, h = h[i-1] + 1), so that every page moves as one whole device
@@ -208,7 +215,7 @@ __device__ __forceinline__ int64_t dev_off(const SubGeom& s, int64_t d, int P) {
 __device__ __forceinline__ void check_page_row(int64_t i, int64_t d, int64_t h, const int64_t* dev_idx,
                                                const int64_t* host_idx, int P, int32_t* err) {
   const bool ok = (h % P == 0) ? (d % P == 0) : (i > 0 && dev_idx[i - 1] + 1 == d && host_idx[i - 1] + 1 == h);
-  if (!ok) atomicOr(err, 2);
+  if (!ok) flag_bad(err, 2, i);
 }
 
 // Zero-copy units.  A sub-buffer's units walk list positions j * stride: stride 1 for
@@ -307,7 +314,7 @@ __global__ __launch_bounds__(kThreads) void k_gather_stage(Geom g, const int64_t
                                                  (int64_t)l * s.layer_stride + (int64_t)r * s.row_stride);
             keep = true;
           } else {
-            atomicOr(err, 1);
+            flag_bad(err, 1, i);
           }
         }
       }
@@ -362,7 +369,7 @@ __global__ __launch_bounds__(kThreads) void k_zc_write(Geom g, const int64_t* __
           dst = (uint64_t)host + (uint64_t)host_off(s, p, l, r);
           keep = true;
         } else {
-          atomicOr(err, 1);
+          flag_bad(err, 1, i);
         }
       }
     }
@@ -419,7 +426,7 @@ __global__ __launch_bounds__(kThreads) void k_zc_read(Geom g, int32_t layer, con
       if (live) {
         const bool first_row = (h % g.P) == 0;
         const bool ok = first_row ? (d % g.P == 0) : (i > 0 && dp + 1 == d && hp + 1 == h);
-        if (!ok) atomicOr(err, 2);
+        if (!ok) flag_bad(err, 2, i);
       }
     }
     if (live) {
@@ -431,7 +438,7 @@ __global__ __launch_bounds__(kThreads) void k_zc_read(Geom g, int32_t layer, con
           dst = layer_base(s, layer) + (uint64_t)dev_off(s, d, g.P);
           keep = true;
         } else {
-          atomicOr(err, 1);
+          flag_bad(err, 1, i);
         }
       }
     }
@@ -487,7 +494,7 @@ __global__ __launch_bounds__(kThreads) void k_compare(Geom g, const int64_t* __r
         keep = true;
       }
     } else {
-      atomicOr(err, 1);
+      flag_bad(err, 1, i);
     }
   }
   int total;

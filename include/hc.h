@@ -198,8 +198,9 @@ int hc_pool_mode(const hc_pool* pool, int32_t which, int32_t* out_mode);
 
 /* Blocks until the copy stream has drained; reports HC_ERR_DEVICE when a kernel
  * flagged an index list since the last report (an out-of-range index, or with
- * HC_FLAG_VALIDATE page-block rows that do not form whole device pages); the
- * report is cleared once returned. */
+ * HC_FLAG_VALIDATE page-block rows that do not form whole device pages).  The
+ * message names the smallest list position (index i of the call's lists) flagged
+ * by any call since then.  The report is cleared once returned. */
 int hc_pool_sync(hc_pool* pool);
 
 /* ---------------------------------------------------------------- transfers */

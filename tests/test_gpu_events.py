@@ -159,7 +159,7 @@ def test_bad_indices_rejected_or_reported():
         rig.pool.load_back_layer(0, cuda_i64(h), cuda_i64(bad_d), None)
         with pytest.raises(B.HcError) as e:
             rig.pool.sync()
-        assert e.value.code == B.HC_ERR_DEVICE
+        assert e.value.code == B.HC_ERR_DEVICE and "first flagged list position 3)" in str(e.value), str(e.value)
         rig.pool.sync()  # the report is cleared once read
         keep = np.arange(h.size) != 3
         O.load_back_layer(rig.geom, 0, dev0, rig.host.np, h[keep], bad_d[keep])
@@ -184,6 +184,7 @@ def test_validate_flag_reports_misaligned_page_blocks():
         with pytest.raises(B.HcError) as e:
             rig.pool.sync()
         assert e.value.code == B.HC_ERR_DEVICE and "page-block" in str(e.value)
+        assert f"first flagged list position {P})" in str(e.value), str(e.value)  # the shifted page's row 0
         rig.pool.load_back_layer(0, cuda_i64(h), cuda_i64(d), None)
         rig.pool.sync()
     finally:
@@ -253,6 +254,7 @@ def test_validate_flag_reports_misaligned_page_blocks_on_write_back(mode):
         with pytest.raises(B.HcError) as e:
             rig.pool.sync()
         assert e.value.code == B.HC_ERR_DEVICE and "page-block" in str(e.value)
+        assert f"first flagged list position {2 * P})" in str(e.value), str(e.value)
     finally:
         rig.close()
 

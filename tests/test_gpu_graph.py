@@ -200,6 +200,7 @@ def test_replay_with_an_out_of_range_slot_is_reported_not_faulted():
         with pytest.raises(B.HcError) as ex:
             rig.pool.sync()
         assert ex.value.code == B.HC_ERR_DEVICE and "out of range" in str(ex.value)
+        assert "first flagged list position 4)" in str(ex.value), str(ex.value)
         rig.pool.sync()  # the report is cleared once read
         keep = np.arange(h.size) != 4
         want = [[a.copy() for a in row] for row in dev0]
