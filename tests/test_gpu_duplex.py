@@ -62,11 +62,7 @@ def test_write_back_and_load_back_at_once(shape, staged):
         L = shape.layers
         rig.host.np[:] = np.random.default_rng(22).integers(0, 256, rig.host.np.size, dtype=np.uint8)
         load_stream = torch.cuda.Stream()
-        rpool = B.Pool(layers=L, page_size=shape.page_size, subs=list(shape.subs),
-                       device_slots=shape.device_slots, host_pages=shape.host_pages,
-                       device_layers=[[rig.dev[b][l] for l in range(L)] for b in range(len(shape.subs))],
-                       host=rig.host, stream=load_stream, layout=shape.layout, shard_align=shape.align,
-                       write_back_mode=B.HC_MODE_ZEROCOPY, max_ctas=8)
+        rpool = rig.pool.sibling(load_stream, max_ctas=8)
         for r in range(3):
             (dw, hw), (hl, dl) = bursts(shape, 30 + 10 * r, 9 + 2 * r)
             dw_t, hl_t, dl_t = cuda_i64(dw), cuda_i64(hl), cuda_i64(dl)
