@@ -220,6 +220,8 @@ class LoadBackGraph:
         if self.handle.value:
             check(lib.hc_load_back_graph_destroy(self.handle), "hc_load_back_graph_destroy")
             self.handle = _V()
+            # replays already enqueued still read the lists
+            _in_use_on(self._refs[0].stream, self._refs[1], self._refs[2])
 
     def __del__(self):
         try:
@@ -333,6 +335,17 @@ def _index_list(x, what: str, on_device: bool):
     raise TypeError(f"{what}: expected a torch tensor or numpy array")
 
 
+def _in_use_on(stream, *tensors):
+    """The library reads these device tensors on `stream` after the call returns: tell
+    torch's caching allocator, so a tensor freed meanwhile (a temporary argument) is not
+    handed to another allocation before that stream's work is done."""
+    if stream is None or not hasattr(stream, "cuda_stream"):
+        return
+    for t in tensors:
+        if getattr(t, "is_cuda", False):
+            t.record_stream(stream)
+
+
 def _torch_int64():
     import torch
     return torch.int64
@@ -385,6 +398,7 @@ class Pool:
             raise ValueError("host_idx and device_idx differ in length")
         check(lib.hc_write_back_all_layers(self.handle, _V(_ptr(device_idx)), _V(_ptr(host_idx)), n,
                                            event.handle if event else None), "hc_write_back_all_layers")
+        _in_use_on(self.stream, device_idx)
 
     def load_back_layer(self, layer: int, host_idx, device_idx, event: HipEvent | None = None) -> None:
         """host_idx, device_idx: int64 CUDA tensors."""
@@ -393,6 +407,7 @@ class Pool:
             raise ValueError("host_idx and device_idx differ in length")
         check(lib.hc_load_back_layer(self.handle, layer, _V(_ptr(host_idx)), _V(_ptr(device_idx)), n,
                                      event.handle if event else None), "hc_load_back_layer")
+        _in_use_on(self.stream, host_idx, device_idx)
 
     # The host-pool method names the pages use (hybrid-pool write-back page, host-pool
     # excerpt; loader-thread page, Motivation), in their argument order, host indices
@@ -509,6 +524,8 @@ class Loader:
         out = _V()
         check(lib.hc_loader_submit(self.handle, _V(_ptr(host_idx)), _V(_ptr(device_idx)), n, arr,
                                    _V(st) if st else None, ctypes.byref(out)), "hc_loader_submit")
+        if self._pool is not None:  # the worker enqueues on the pool's stream, maybe after the burst is released
+            _in_use_on(self._pool.stream, host_idx, device_idx)
         b = Burst(out, (host_idx, device_idx, arr, layer_events, start_event), self)
         self._bursts.add(b)
         return b
