@@ -1,0 +1,62 @@
+"""Back-to-back bursts on one pool with no synchronisation in between: write-backs of
+random sizes (the plan buffers alternate and grow while earlier bursts are still queued)
+and per-layer load-backs, some naming host pages an earlier burst of the run wrote.
+Temporaries are passed on purpose.  After one final sync the whole host pool and device
+pool must equal the oracle applied to the same calls in the same order."""
+import numpy as np
+import pytest
+import torch
+
+from host_device_page_amd import binding as B
+from host_device_page_amd import workloads as W
+from gpu_support import Rig, assert_bytes_equal, assert_dev_equal, cuda_i64, say
+from oracle import oracle as O
+
+T, BLK = W.TOKEN_ROWS, W.PAGE_BLOCKS
+PF, SH, TM = W.PAGE_FIRST, W.KV_SPLIT_SHARD, W.PAGE_FIRST_TOKEN_MAJOR
+SHAPES = [
+    W.PoolShape("stress_rows", 3, 16, ((T, 256), (T, 128)), 4096, 96, PF),
+    W.PoolShape("stress_shard", 2, 8, ((T, 512), (T, 96)), 2048, 80, SH, 1024),
+    W.PoolShape("stress_blocks", 2, 16, ((T, 64), (BLK, 512)), 2048, 64, TM),
+]
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("staged", [False, True], ids=["zerocopy", "staged"])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: s.name)
+def test_back_to_back_bursts_without_sync(shape, staged):
+    say(f"[stress] {shape.name} staged={staged}")
+    P, L, S, H = shape.page_size, shape.layers, shape.device_slots, shape.host_pages
+    blocks = any(g == BLK for g, _ in shape.subs)
+    rig = Rig(shape, seed=91, staging_pages=2 if staged else 0,
+              write_back_mode=B.HC_MODE_STAGED if staged else B.HC_MODE_ZEROCOPY)
+    try:
+        rng = np.random.default_rng(92)
+        rig.host.np[:] = rng.integers(0, 256, rig.host.np.size, dtype=np.uint8)
+        torch.cuda.synchronize()
+        dev = rig.dev_np()
+        host = rig.host.np.copy()
+        for k in range(60):
+            npages = int(rng.choice([1, 2, 3, 7, 20, 40]))
+            pages = rng.choice(H, size=npages, replace=False)
+            if blocks:
+                h = W.whole_page_tokens(pages, P)
+                dp = rng.choice(S // P, size=npages, replace=False)
+                d = (dp[:, None] * P + np.arange(P)[None, :]).reshape(-1).astype(np.int64)
+            else:
+                h = np.concatenate([p * P + np.sort(rng.choice(P, size=int(rng.integers(1, P + 1)), replace=False))
+                                    for p in pages]).astype(np.int64)
+                d = rng.choice(S, size=h.size, replace=False).astype(np.int64)
+            if k % 3 == 2:
+                # per-layer load-back of these host rows (some written earlier in the run)
+                for l in range(L):
+                    rig.pool.load_back_layer(l, cuda_i64(h), cuda_i64(d))
+                    O.load_back_layer(rig.geom, l, dev, host, h, d)
+            else:
+                rig.pool.write_back_all_layers(cuda_i64(d), h)
+                O.write_back(rig.geom, dev, host, d, h)
+        rig.pool.sync()
+        assert_bytes_equal(rig.host.np, host, "host pool after the run")
+        assert_dev_equal(rig.dev_np(), dev, "device pool after the run")
+    finally:
+        rig.close()
