@@ -60,3 +60,68 @@ def test_back_to_back_bursts_without_sync(shape, staged):
         assert_dev_equal(rig.dev_np(), dev, "device pool after the run")
     finally:
         rig.close()
+
+
+@pytest.mark.gpu
+def test_one_pool_called_from_several_threads():
+    """Four Python threads call one pool at the same time (the library serialises the calls
+    on its copy stream): two write back their own host pages, two load back their own
+    earlier-written pages into their own slots.  Rows are disjoint between threads, so the
+    final pools equal the oracle whatever the interleaving."""
+    import threading
+    shape = SHAPES[0]
+    P, L, S, H = shape.page_size, shape.layers, shape.device_slots, shape.host_pages
+    say("[stress] one pool, four threads")
+    rig = Rig(shape, seed=93)
+    try:
+        rng = np.random.default_rng(94)
+        rig.host.np[:] = rng.integers(0, 256, rig.host.np.size, dtype=np.uint8)
+        torch.cuda.synchronize()
+        dev, host = rig.dev_np(), rig.host.np.copy()
+        page_sets = np.array_split(rng.permutation(H), 4)
+        slot_sets = np.array_split(rng.permutation(S), 4)
+        plans = []
+        for t in range(4):
+            calls = []
+            for k in range(25):
+                pages = rng.choice(page_sets[t], size=3, replace=False)
+                h = W.whole_page_tokens(pages, P)
+                d = rng.choice(slot_sets[t], size=h.size, replace=False).astype(np.int64)
+                calls.append((h, d))
+            plans.append(calls)
+        errors = []
+
+        def writer(t):
+            try:
+                for h, d in plans[t]:
+                    rig.pool.write_back_all_layers(cuda_i64(d), h)
+            except Exception as e:  # reported below
+                errors.append(e)
+
+        def loader(t):
+            try:
+                for h, d in plans[t]:
+                    for l in range(L):
+                        rig.pool.load_back_layer(l, cuda_i64(h), cuda_i64(d))
+            except Exception as e:
+                errors.append(e)
+
+        threads = [threading.Thread(target=writer, args=(0,)), threading.Thread(target=writer, args=(1,)),
+                   threading.Thread(target=loader, args=(2,)), threading.Thread(target=loader, args=(3,))]
+        for th in threads:
+            th.start()
+        for th in threads:
+            th.join()
+        assert not errors, errors
+        rig.pool.sync()
+        for t in (0, 1):
+            for h, d in plans[t]:
+                O.write_back(rig.geom, dev, host, d, h)
+        for t in (2, 3):
+            for h, d in plans[t]:
+                for l in range(L):
+                    O.load_back_layer(rig.geom, l, dev, host, h, d)
+        assert_bytes_equal(rig.host.np, host, "host pool")
+        assert_dev_equal(rig.dev_np(), dev, "device pool")
+    finally:
+        rig.close()
