@@ -315,3 +315,42 @@ def test_shard_pads_stay_zero_when_staging_is_shared():
             opool.close()
         orig.close()
         rig.close()
+
+
+@pytest.mark.gpu
+def test_pool_on_the_null_stream():
+    """copy_stream NULL: the pool's work goes to the null stream; transfers still match the
+    oracle, and capturing a graph there is refused with an error, not a crash."""
+    from gpu_support import assert_bytes_equal, assert_dev_equal
+    from oracle import oracle as O
+    shape = W.SHAPES["tiny_mha_bf16"]
+    say("[parity] pool on the null stream")
+    rig = Rig(shape, seed=95)
+    pool = None
+    try:
+        L = shape.layers
+        pool = B.Pool(layers=L, page_size=shape.page_size, subs=list(shape.subs),
+                      device_slots=shape.device_slots, host_pages=shape.host_pages,
+                      device_layers=[[rig.dev[b][l] for l in range(L)] for b in range(len(shape.subs))],
+                      host=rig.host, stream=None, write_back_mode=B.HC_MODE_ZEROCOPY)
+        d, h = burst(shape, 96, "perm", 5, 3)
+        dev0, host0 = rig.dev_np(), rig.host.np.copy()
+        pool.write_back_all_layers(cuda_i64(d), h)
+        d2 = fresh(shape, d, 97)
+        for l in range(L):
+            pool.load_back_layer(l, cuda_i64(h), cuda_i64(d2))
+        pool.sync()
+        want_host = host0.copy()
+        O.write_back(rig.geom, dev0, want_host, d, h)
+        for l in range(L):
+            O.load_back_layer(rig.geom, l, dev0, want_host, h, d2)
+        assert_bytes_equal(rig.host.np, want_host, "host pool")
+        assert_dev_equal(rig.dev_np(), dev0, "device pool")
+        with pytest.raises(B.HcError):
+            pool.capture_load_back(cuda_i64(h), cuda_i64(d2), [B.HipEvent() for _ in range(L)])
+        pool.load_back_layer(0, cuda_i64(h), cuda_i64(d2))  # still usable after the refused capture
+        pool.sync()
+    finally:
+        if pool is not None:
+            pool.close()
+        rig.close()
