@@ -125,3 +125,33 @@ def test_one_pool_called_from_several_threads():
         assert_dev_equal(rig.dev_np(), dev, "device pool")
     finally:
         rig.close()
+
+
+@pytest.mark.gpu
+def test_profiling_pool_over_many_launches():
+    """A pool with per-launch timing folds its pending timing events into the totals every
+    4096 launches; 4500 layer launches must all be counted, with every row correct."""
+    shape = SHAPES[0]
+    P, L, S, H = shape.page_size, shape.layers, shape.device_slots, shape.host_pages
+    say("[stress] profiling pool, 4500 launches")
+    rig = Rig(shape, seed=97, flags=B.HC_FLAG_PROFILE)
+    try:
+        rng = np.random.default_rng(98)
+        rig.host.np[:] = rng.integers(0, 256, rig.host.np.size, dtype=np.uint8)
+        h = W.whole_page_tokens(rng.choice(H, size=2, replace=False), P)
+        d = rng.choice(S, size=h.size, replace=False).astype(np.int64)
+        h_t, d_t = cuda_i64(h), cuda_i64(d)
+        torch.cuda.synchronize()
+        dev = rig.dev_np()
+        rig.pool.kernel_time(B.KIND_ZC_READ, reset=True)
+        for k in range(1500):
+            for l in range(L):
+                rig.pool.load_back_layer(l, h_t, d_t)
+        rig.pool.sync()
+        n, ms = rig.pool.kernel_time(B.KIND_ZC_READ)
+        assert n == 1500 * L and ms > 0
+        for l in range(L):
+            O.load_back_layer(rig.geom, l, dev, rig.host.np, h, d)
+        assert_dev_equal(rig.dev_np(), dev, "device pool")
+    finally:
+        rig.close()
