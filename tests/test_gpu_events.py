@@ -422,3 +422,36 @@ def test_pool_buffers_smaller_than_the_layout_are_refused():
             hip.hipFree(p)
         small_host.free()
         host.free()
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("mode", [B.HC_MODE_ZEROCOPY, B.HC_MODE_STAGED], ids=["zerocopy", "staged"])
+def test_write_back_done_event(mode):
+    """The write-back's event completes only after every host byte of the burst has landed
+    (the host thread waits on the event alone, no pool sync), and it is recorded even when
+    the call is refused."""
+    say(f"[events] write-back done event, mode {mode}")
+    rig = Rig(SHAPE, seed=17, write_back_mode=mode, staging_pages=3)
+    try:
+        pages = W.host_pages(18, SHAPE.host_pages, 11)
+        h = W.whole_page_tokens(pages, SHAPE.page_size)
+        h = np.concatenate([h, np.setdiff1d(np.arange(SHAPE.host_pages), pages)[0] * SHAPE.page_size + np.arange(5)])
+        d = W.permutation_slots(19, SHAPE.device_slots, h.size)
+        dev0, host0 = rig.dev_np(), rig.host.np.copy()
+        torch.cuda.synchronize()
+        done = B.HipEvent()
+        rig.pool.write_back_all_layers(cuda_i64(d), h, done)
+        done.synchronize()
+        want = host0.copy()
+        O.write_back(rig.geom, dev0, want, d, h)
+        assert np.array_equal(rig.host.np, want), "host pool incomplete when the write-back event completed"
+        refused = B.HipEvent()
+        bad = h.copy()
+        bad[2] = bad[1]  # a repeated host token: refused on the CPU
+        with pytest.raises(B.HcError):
+            rig.pool.write_back_all_layers(cuda_i64(d), bad, refused)
+        refused.synchronize()
+        assert refused.query()
+        rig.pool.sync()
+    finally:
+        rig.close()
