@@ -354,3 +354,29 @@ def test_pool_on_the_null_stream():
         if pool is not None:
             pool.close()
         rig.close()
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("kind", ["torch_cpu", "torch_pinned"])
+def test_write_back_host_list_as_a_torch_tensor(kind):
+    """The write-back's host list may be a torch CPU tensor, pageable or pinned, as well as a
+    numpy array."""
+    from gpu_support import assert_bytes_equal
+    from oracle import oracle as O
+    shape = W.SHAPES["tiny_mha_bf16"]
+    say(f"[parity] host list as {kind}")
+    rig = Rig(shape, seed=98, staging_pages=2, write_back_mode=B.HC_MODE_STAGED)
+    try:
+        d, h = burst(shape, 99, "perm", 6, 4)
+        h_t = torch.from_numpy(np.ascontiguousarray(h, dtype=np.int64))
+        if kind == "torch_pinned":
+            h_t = h_t.pin_memory()
+        dev0, host0 = rig.dev_np(), rig.host.np.copy()
+        torch.cuda.synchronize()
+        rig.pool.write_back_all_layers(cuda_i64(d), h_t)
+        rig.pool.sync()
+        want = host0.copy()
+        O.write_back(rig.geom, dev0, want, d, h)
+        assert_bytes_equal(rig.host.np, want, "host pool")
+    finally:
+        rig.close()
