@@ -14,7 +14,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libhc.so")
 SOURCES = ["hc_api.cpp", "hc_layout.cpp", "hc_plan.cpp", "hc_loader.cpp", "hc_h2h.cpp", "hc_kernels.hip"]
-HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+HIPCC = os.environ.get("HIPCC", os.path.join(ROCM, "bin", "hipcc"))
 
 # Packed fp32 instructions are kept out of every code object (the copy kernels
 # have no float arithmetic; the flag makes sure none is generated).
@@ -23,11 +24,15 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
          "-Wall", "-Wno-unused-result", "-I", INCLUDE, "-I", CSRC]
 
 
+# roctx ranges around the entry points (rocprofiler-sdk's marker library)
+LIBS = ["-L" + os.path.join(ROCM, "lib"), "-lrocprofiler-sdk-roctx"]
+
+
 def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
     """Compile libhc.so; `defines` are extra -D tuning knobs (e.g. HC_UNROLL=16)."""
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
     tmp = out + ".tmp"
-    cmd = [HIPCC, *FLAGS, *[f"-D{d}" for d in defines], "-o", tmp, *srcs]
+    cmd = [HIPCC, *FLAGS, *[f"-D{d}" for d in defines], "-o", tmp, *srcs, *LIBS]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

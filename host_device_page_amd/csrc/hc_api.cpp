@@ -27,6 +27,8 @@
 #include <string>
 #include <vector>
 
+#include <rocprofiler-sdk-roctx/roctx.h>
+
 #include "hc_internal.h"
 #include "hc_plan.h"
 
@@ -199,6 +201,15 @@ int check_host_list(const int64_t* q, const char* what) {
     return set_err(HC_ERR_INVALID, "%s must be in host memory: the CPU plans the write-back from it", what);
   return HC_OK;
 }
+
+// A roctx range over one entry point's enqueue, so a trace shows each burst and layer
+// call next to the kernels and copies it launched (a no-op without a profiler).
+struct TraceRange {
+  explicit TraceRange(const char* name) { roctxRangePushA(name); }
+  ~TraceRange() { roctxRangePop(); }
+  TraceRange(const TraceRange&) = delete;
+  TraceRange& operator=(const TraceRange&) = delete;
+};
 
 int use_device(hc_pool* p) {
   int cur = -1;
@@ -611,6 +622,7 @@ int hc_pool_sync(hc_pool* p) {
 int hc_write_back_all_layers(hc_pool* p, const int64_t* device_idx, const int64_t* host_idx, int64_t n,
                              void* event) {
   if (!p) return set_err(HC_ERR_INVALID, "pool is null");
+  TraceRange range("hc_write_back_all_layers");
   std::lock_guard<std::recursive_mutex> lock(p->mu);
   int rc = use_device(p);
   if (rc != HC_OK) return rc;
@@ -725,6 +737,7 @@ int hc_load_back_layer(hc_pool* p, int32_t layer, const int64_t* host_idx, const
     if (event) (void)hipEventRecord((hipEvent_t)event, nullptr);
     return set_err(HC_ERR_INVALID, "pool is null");
   }
+  TraceRange range("hc_load_back_layer");
   std::lock_guard<std::recursive_mutex> lock(p->mu);
   int rc = use_device(p);
   auto finish = [&](int code) {
@@ -867,6 +880,7 @@ int hc_load_back_graph_create(hc_pool* p, const int64_t* host_idx, const int64_t
 
 int hc_load_back_graph_launch(hc_lb_graph* g) {
   if (!g) return set_err(HC_ERR_INVALID, "graph is null");
+  TraceRange range("hc_load_back_graph_launch");
   hc_pool* p = g->pool;
   std::lock_guard<std::recursive_mutex> lock(p->mu);
   int rc = use_device(p);

@@ -37,6 +37,9 @@
  *
  * Payload bytes are never interpreted: bf16, fp8 and fp32 all move bit-exactly.
  *
+ * Each write-back, load-back and graph launch call is a roctx range named after
+ * the function, visible to rocprofv3 --marker-trace.
+ *
  * Conventions for every call:
  *   - Return value: HC_OK (0) or a negative hc_status.  hc_last_error() returns
  *     a message for the calling thread's last failure.
