@@ -48,6 +48,7 @@ struct hc_loader {
   bool running = false;
   int64_t failed = 0;
   int64_t in_flight = 0;  // submitted, not yet done
+  int64_t live = 0;       // submitted, not yet released (each holds a pointer to the loader)
   std::thread worker;
 };
 
@@ -217,6 +218,7 @@ int submit_burst(hc_loader* ld, const int64_t* host_idx, const int64_t* device_i
     });
     for (void* e : b->events) ld->held[e] = b;
     ld->in_flight++;
+    ld->live++;
     if (ld->async) {
       ld->queue.push_back(b);
       ld->cv.notify_all();
@@ -279,6 +281,7 @@ int hc_burst_release(hc_burst* b) {
   {
     std::unique_lock<std::mutex> lk(ld->mu);
     ld->cv.wait(lk, [&] { return b->done; });
+    ld->live--;
   }
   delete b;
   return HC_OK;
@@ -303,6 +306,8 @@ int hc_loader_destroy(hc_loader* ld) {
   if (!ld) return HC_OK;
   {
     std::lock_guard<std::mutex> lk(ld->mu);
+    if (ld->live > 0)  // a later hc_burst_release would reach a freed loader
+      return hc::set_error(HC_ERR_INVALID, "%lld burst(s) not released; release them first", (long long)ld->live);
     ld->stop = true;
     ld->cv.notify_all();
   }

@@ -348,8 +348,9 @@ int hc_burst_release(hc_burst* burst);
 int hc_loader_drain(hc_loader* loader);
 /* Number of bursts whose enqueue failed so far, and whether a worker thread runs. */
 int hc_loader_info(hc_loader* loader, int64_t* failed_bursts, int32_t* worker_running);
-/* Drains, joins the worker, frees.  Every burst must be released before.  NULL is a no-op.
- * Destroy a pool's loaders before the pool. */
+/* Drains, joins the worker, frees.  NULL is a no-op.  Refused (HC_ERR_INVALID, nothing
+ * freed) while a burst of the loader is not released.  Destroy a pool's loaders before
+ * the pool. */
 int hc_loader_destroy(hc_loader* loader);
 
 /* ---------------------------------------------------------------- host-to-host shard copies

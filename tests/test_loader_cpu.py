@@ -287,3 +287,15 @@ def test_graph_submit_needs_a_launch_op():
     out = ctypes.c_void_p()
     assert B.lib.hc_loader_submit_graph(None, None, None, None, ctypes.byref(out)) == B.HC_ERR_INVALID
     ld.close()
+
+
+def test_destroy_refuses_while_a_burst_is_not_released():
+    f = Fake()
+    ld = B.Loader(None, L, asynchronous=True, ops=f.ops)
+    b = ld.submit(0x10, 0, 1, EV)
+    b.wait()
+    assert B.lib.hc_loader_destroy(ld.handle) == B.HC_ERR_INVALID
+    assert "not released" in B.lib.hc_last_error().decode()
+    b.release()
+    ld.close()  # now it goes
+    assert not ld.handle.value
