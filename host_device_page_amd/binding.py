@@ -572,6 +572,7 @@ class H2H:
 
     def __init__(self, workers: int = 4, queue_depth: int = 1024):
         self.handle = _V()
+        self._live = {}  # request handle -> the address arrays it was submitted with
         check(lib.hc_h2h_create(workers, queue_depth, ctypes.byref(self.handle)), "hc_h2h_create")
 
     def submit(self, direction: int, tensor_bytes, tensor_pages, shards, shard_bytes: int):
@@ -584,9 +585,12 @@ class H2H:
         out = _V()
         check(lib.hc_h2h_submit(self.handle, direction, T, sizes, pages, sh, shard_bytes, n, ctypes.byref(out)),
               "hc_h2h_submit")
+        self._live[out.value] = (sizes, pages, sh)
         return out
 
     def wait(self, req) -> None:
+        """Waits for the request's shards, then releases it."""
+        self._live.pop(req.value, None)
         check(lib.hc_h2h_release(req), "hc_h2h_release")
 
     def outstanding(self):
@@ -596,6 +600,8 @@ class H2H:
 
     def close(self) -> None:
         if self.handle.value:
+            for req in list(self._live):  # requests never waited for: finish and release them first
+                self.wait(_V(req))
             check(lib.hc_h2h_destroy(self.handle), "hc_h2h_destroy")
             self.handle = _V()
 

@@ -39,6 +39,7 @@ struct hc_h2h {
   bool stop = false;
   int64_t depth = 0;
   int64_t outstanding[2] = {0, 0};
+  int64_t live = 0;  // requests submitted and not yet released (each holds a pointer to the engine)
 };
 
 namespace {
@@ -176,6 +177,7 @@ int hc_h2h_submit(hc_h2h* e, int32_t direction, int32_t tensors, const int64_t* 
                            (long long)n, (long long)e->outstanding[direction], (long long)e->depth);
     }
     e->outstanding[direction] += n;
+    e->live++;
     r->remaining = n;
     for (int64_t i = 0; i < n; i++) e->queue.emplace_back(r, i);
     e->cv_work.notify_all();
@@ -196,6 +198,10 @@ int hc_h2h_wait(hc_h2h_request* r) {
 int hc_h2h_release(hc_h2h_request* r) {
   if (!r) return HC_OK;
   int rc = hc_h2h_wait(r);
+  {
+    std::lock_guard<std::mutex> lk(r->eng->mu);
+    r->eng->live--;
+  }
   delete r;
   return rc;
 }
@@ -210,6 +216,11 @@ int hc_h2h_outstanding(hc_h2h* e, int64_t* dump_shards, int64_t* load_shards) {
 
 int hc_h2h_destroy(hc_h2h* e) {
   if (!e) return HC_OK;
+  {
+    std::lock_guard<std::mutex> lk(e->mu);
+    if (e->live > 0)  // a later hc_h2h_wait or release would reach a freed engine
+      return hc::set_error(HC_ERR_INVALID, "%lld request(s) not released; release them first", (long long)e->live);
+  }
   if (e->workers.empty()) run_inline(e, nullptr);
   {
     std::lock_guard<std::mutex> lk(e->mu);

@@ -390,7 +390,8 @@ int hc_h2h_wait(hc_h2h_request* request);
 /* Waits like hc_h2h_wait, then frees the request. */
 int hc_h2h_release(hc_h2h_request* request);
 int hc_h2h_outstanding(hc_h2h* h2h, int64_t* dump_shards, int64_t* load_shards);
-/* Runs the remaining jobs, joins the workers, frees.  Release requests first.  NULL is a no-op. */
+/* Runs the remaining jobs, joins the workers, frees.  NULL is a no-op.  Refused
+ * (HC_ERR_INVALID, nothing freed) while a request is not released. */
 int hc_h2h_destroy(hc_h2h* h2h);
 
 /* Cache identity (CacheStore H2H page, page_first_kv_split support: model, host layout,

@@ -141,3 +141,16 @@ def test_cache_fingerprint():
     assert len(set(others + [fp])) == len(others) + 1, "a layout change kept the fingerprint"
     # host page count and device slots are capacity, not layout
     assert B.cache_fingerprint(desc(host_pages=100)[0], "deepseek-v3", 8) == fp
+
+
+def test_destroy_refuses_while_a_request_is_not_released():
+    eng = B.H2H(workers=2, queue_depth=16)
+    buf = np.zeros(4096, dtype=np.uint8)
+    a = buf.ctypes.data
+    req = eng.submit(B.HC_H2H_DUMP, [64], [[a + 64 * i] for i in range(4)], [a + 2048 + 64 * i for i in range(4)], 64)
+    assert B.lib.hc_h2h_destroy(eng.handle) == B.HC_ERR_INVALID
+    assert "not released" in B.lib.hc_last_error().decode()
+    eng.close()  # the binding waits for and releases the request first
+    assert not eng.handle.value
+    assert np.array_equal(buf[2048:2048 + 256], buf[0:256])
+    del req
