@@ -46,6 +46,9 @@
  *   - Ownership: the caller owns every buffer, stream and event passed in and
  *     keeps them alive until the copy stream has drained.  The library owns only
  *     the pool handle and its small scratch (index plans, counters).
+ *   - Threads: a pool's calls may come from several threads at once; the pool
+ *     takes them one at a time (one lock per pool), so its copy stream sees them
+ *     in the order they took the lock.  Handles must outlive every call on them.
  *   - Asynchrony: transfer calls enqueue on the pool's copy stream and return.
  *     Work on the copy stream runs in call order.  A caller whose index lists
  *     or device rows are produced on another stream must order that stream
