@@ -28,7 +28,7 @@ def geometries(draw):
     return L, P, subs, H, S, layout, align
 
 
-@settings(max_examples=300, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+@settings(max_examples=300, deadline=None, derandomize=True, suppress_health_check=[HealthCheck.too_slow])
 @given(geometries(), st.data())
 def test_host_offsets_match_the_oracle(geom, data):
     L, P, subs, H, S, layout, align = geom
@@ -46,7 +46,7 @@ def test_host_offsets_match_the_oracle(geom, data):
         assert B.host_offset(d, b, p, l, r) == O.host_offset(og, b, p, l, r), (b, p, l, r)
 
 
-@settings(max_examples=500, deadline=None)
+@settings(max_examples=500, deadline=None, derandomize=True)
 @given(layers=st.integers(-2, 1100), page_size=st.integers(-2, 1 << 21), nsub=st.integers(0, 5),
        elem=st.integers(-16, 1 << 17), gran=st.integers(-1, 2), slots=st.integers(-2, 1 << 62),
        pages=st.integers(-2, 1 << 62), layout=st.integers(-1, 3), align=st.integers(-1, 1 << 20),
