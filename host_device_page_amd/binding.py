@@ -66,6 +66,12 @@ class hc_pool_desc(ctypes.Structure):
                 ("flags", ctypes.c_int32), ("max_ctas", ctypes.c_int32)]
 
 
+class hc_pool_stats(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_int64) for name in (
+        "write_back_calls", "write_back_tokens", "write_back_bytes",
+        "load_back_calls", "load_back_tokens", "load_back_bytes", "device_errors")]
+
+
 _D = ctypes.POINTER(hc_pool_desc)
 _V = ctypes.c_void_p
 
@@ -102,6 +108,7 @@ _SIGS = {
     "hc_load_back_graph_destroy": (ctypes.c_int, [_V]),
     "hc_pool_kernel_time": (ctypes.c_int, [_V, ctypes.c_int32, ctypes.c_int32, _I64P,
                                            ctypes.POINTER(ctypes.c_double)]),
+    "hc_pool_get_stats": (ctypes.c_int, [_V, ctypes.POINTER(hc_pool_stats)]),
     "hc_loader_create": (ctypes.c_int, [_V, ctypes.POINTER(hc_loader_ops), ctypes.c_int32, ctypes.c_int32,
                                         ctypes.POINTER(_V)]),
     "hc_loader_submit": (ctypes.c_int, [_V, _V, _V, ctypes.c_int64, ctypes.POINTER(_V), _V, ctypes.POINTER(_V)]),
@@ -435,6 +442,12 @@ class Pool:
 
     def sync(self) -> None:
         check(lib.hc_pool_sync(self.handle), "hc_pool_sync")
+
+    def stats(self) -> dict:
+        """Running totals of the pool's enqueued transfer calls (hc_pool_get_stats)."""
+        out = hc_pool_stats()
+        check(lib.hc_pool_get_stats(self.handle, ctypes.byref(out)), "hc_pool_get_stats")
+        return {name: getattr(out, name) for name, _ in hc_pool_stats._fields_}
 
     def kernel_time(self, kind: int, reset: bool = False):
         n = ctypes.c_int64()

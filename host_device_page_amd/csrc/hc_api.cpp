@@ -119,6 +119,9 @@ struct hc_pool {
   std::vector<TimedLaunch> pending_timed;
   int64_t kind_launches[kKinds] = {};
   double kind_ms[kKinds] = {};
+  hc_pool_stats stats{};
+  int64_t row_bytes_per_layer = 0;    // sum of token-row sub-buffers' elem_bytes
+  int64_t block_bytes_per_layer = 0;  // sum of page-block sub-buffers' elem_bytes
 };
 
 namespace {
@@ -210,6 +213,10 @@ struct TraceRange {
   TraceRange(const TraceRange&) = delete;
   TraceRange& operator=(const TraceRange&) = delete;
 };
+
+// Host-link bytes of n named tokens in one layer: every token row, plus one block per
+// page for page-block sub-buffers (their lists name whole pages).
+int64_t layer_bytes(const hc_pool* p, int64_t n);
 
 int use_device(hc_pool* p) {
   int cur = -1;
@@ -559,6 +566,8 @@ int hc_pool_create(const hc_pool_desc* desc, hc_pool** out) {
   if (hipStreamSynchronize(p->stream) != hipSuccess) return bail(set_err(HC_ERR_HIP, "stream sync failed"));
   p->planner.reset(L);
   fill_geom(p);
+  for (int b = 0; b < L.nsub; b++)
+    (L.gran[b] == HC_PAGE_BLOCKS ? p->block_bytes_per_layer : p->row_bytes_per_layer) += L.elem[b];
   *out = p;
   return HC_OK;
 }
@@ -611,6 +620,7 @@ int hc_pool_sync(hc_pool* p) {
     HIP_TRY(hipMemsetAsync(p->d_err, 0, sizeof(int32_t), p->stream));
     HIP_TRY(hipMemsetAsync((uint8_t*)p->d_err + 8, 0xFF, 8, p->stream));
     HIP_TRY(hipStreamSynchronize(p->stream));
+    p->stats.device_errors++;
     return set_err(HC_ERR_DEVICE,
                    "device-side check flagged an index list (code %d:%s%s first flagged list position %llu)", e,
                    (e & 1) ? " index out of range;" : "",
@@ -727,6 +737,9 @@ int hc_write_back_all_layers(hc_pool* p, const int64_t* device_idx, const int64_
     t.done(e == hipSuccess);
     if (e != hipSuccess) return finish(set_err(HC_ERR_HIP, "pad launch failed: %s", hipGetErrorString(e)));
   }
+  p->stats.write_back_calls++;
+  p->stats.write_back_tokens += n;
+  p->stats.write_back_bytes += layer_bytes(p, n) * L.L;
   return finish(HC_OK);
 }
 
@@ -764,6 +777,11 @@ int hc_load_back_layer(hc_pool* p, int32_t layer, const int64_t* host_idx, const
     t.done(e == hipSuccess);
   }
   if (e != hipSuccess) return finish(set_err(HC_ERR_HIP, "load-back launch failed: %s", hipGetErrorString(e)));
+  if (!p->capturing) {  // a captured call is counted when its graph replays
+    p->stats.load_back_calls++;
+    p->stats.load_back_tokens += n;
+    p->stats.load_back_bytes += layer_bytes(p, n);
+  }
   return finish(HC_OK);
 }
 
@@ -801,6 +819,7 @@ struct hc_lb_graph {
   hipGraph_t graph = nullptr;
   hipGraphExec_t exec = nullptr;
   std::vector<void*> events;  // the L layer events the replays record (NULL: none for that layer)
+  int64_t n = 0;              // tokens per layer of every replay
 };
 
 extern "C" {
@@ -838,6 +857,7 @@ int hc_load_back_graph_create(hc_pool* p, const int64_t* host_idx, const int64_t
   hc_lb_graph* g = new (std::nothrow) hc_lb_graph();
   if (!g) return set_err(HC_ERR_NOMEM, "graph handle allocation failed");
   g->pool = p;
+  g->n = n;
   try {
     g->events.assign(layer_events, layer_events + p->lay.L);
   } catch (...) {
@@ -886,6 +906,18 @@ int hc_load_back_graph_launch(hc_lb_graph* g) {
   int rc = use_device(p);
   if (rc != HC_OK) return rc;
   HIP_TRY(hipGraphLaunch(g->exec, p->stream));
+  if (g->n > 0) {
+    p->stats.load_back_calls += p->lay.L;
+    p->stats.load_back_tokens += g->n * p->lay.L;
+    p->stats.load_back_bytes += layer_bytes(p, g->n) * p->lay.L;
+  }
+  return HC_OK;
+}
+
+int hc_pool_get_stats(hc_pool* p, hc_pool_stats* out) {
+  if (!p || !out) return set_err(HC_ERR_INVALID, "null argument");
+  std::lock_guard<std::recursive_mutex> lock(p->mu);
+  *out = p->stats;
   return HC_OK;
 }
 
@@ -988,3 +1020,11 @@ void pool_hold(hc_pool* pool) { pool->users.fetch_add(1); }
 void pool_release(hc_pool* pool) { pool->users.fetch_sub(1); }
 
 }  // namespace hc
+
+namespace {
+
+int64_t layer_bytes(const hc_pool* p, int64_t n) {
+  return n * p->row_bytes_per_layer + (p->lay.has_blocks ? n / p->lay.P : 0) * p->block_bytes_per_layer;
+}
+
+}  // namespace

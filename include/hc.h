@@ -407,6 +407,17 @@ int hc_cache_fingerprint(const hc_pool_desc* desc, const char* model, int32_t tp
 
 /* ---------------------------------------------------------------- measurement */
 
+/* Running totals of a pool's transfer calls that were enqueued (refused calls are not
+ * counted), for monitoring.  Bytes are the host-link bytes of the call: every named
+ * token row of every layer moved, plus page blocks once per page. */
+typedef struct hc_pool_stats {
+  int64_t write_back_calls, write_back_tokens, write_back_bytes;
+  int64_t load_back_calls, load_back_tokens, load_back_bytes;  /* one call = one layer */
+  int64_t device_errors;  /* HC_ERR_DEVICE reports returned by hc_pool_sync */
+} hc_pool_stats;
+/* Copies the totals to *out (host memory); touches no GPU. */
+int hc_pool_get_stats(hc_pool* pool, hc_pool_stats* out);
+
 /* Per-kernel timing with HIP events on the copy stream (pools with HC_FLAG_PROFILE).
  * kind: 0 gather to staging, 1 zero-copy write-back, 2 zero-copy load-back,
  *       3 pad fill, 4 round-trip compare, 5 staged copy-engine transfers.

@@ -93,6 +93,7 @@ def test_null_arguments_without_gpu():
     assert out.value is None
     assert B.lib.hc_load_back_graph_create(None, None, None, 0, evs, None) == B.HC_ERR_INVALID
     assert B.lib.hc_load_back_graph_launch(None) == B.HC_ERR_INVALID
+    assert B.lib.hc_pool_get_stats(None, ctypes.byref(B.hc_pool_stats())) == B.HC_ERR_INVALID
     assert B.lib.hc_load_back_graph_destroy(None) == B.HC_OK
 
 

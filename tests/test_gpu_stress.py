@@ -155,3 +155,51 @@ def test_profiling_pool_over_many_launches():
         assert_dev_equal(rig.dev_np(), dev, "device pool")
     finally:
         rig.close()
+
+
+@pytest.mark.gpu
+def test_pool_stats_count_enqueued_calls():
+    """hc_pool_get_stats: calls, tokens and host-link bytes of enqueued write-backs and
+    per-layer load-backs (captured replays included, refused calls not), and device
+    error reports."""
+    shape = SHAPES[2]  # token rows plus page blocks
+    P, L, S, H = shape.page_size, shape.layers, shape.device_slots, shape.host_pages
+    rows = sum(e for g, e in shape.subs if g == T)
+    blks = sum(e for g, e in shape.subs if g == BLK)
+    say("[stress] pool stats")
+    rig = Rig(shape, seed=99)
+    graph = None
+    try:
+        rng = np.random.default_rng(100)
+        pages = rng.choice(H, size=5, replace=False)
+        h = W.whole_page_tokens(pages, P)
+        dp = rng.choice(S // P, size=5, replace=False)
+        d = (dp[:, None] * P + np.arange(P)[None, :]).reshape(-1).astype(np.int64)
+        n = h.size
+        assert rig.pool.stats() == {f: 0 for f, _ in B.hc_pool_stats._fields_}
+        rig.pool.write_back_all_layers(cuda_i64(d), h)
+        with pytest.raises(B.HcError):
+            rig.pool.write_back_all_layers(cuda_i64(d), h[::-1].copy())  # rows out of order: refused
+        h_t, d_t = cuda_i64(h), cuda_i64(d)
+        for l in range(L):
+            rig.pool.load_back_layer(l, h_t, d_t)
+        graph = rig.pool.capture_load_back(h_t, d_t, [B.HipEvent() for _ in range(L)])
+        graph.launch()
+        graph.launch()
+        bad = d.copy()
+        bad[0] = S * 4  # out of range: skipped and reported
+        rig.pool.load_back_layer(0, h_t, cuda_i64(bad))
+        with pytest.raises(B.HcError):
+            rig.pool.sync()
+        per_layer = n * rows + (n // P) * blks
+        st = rig.pool.stats()
+        assert st["write_back_calls"] == 1 and st["write_back_tokens"] == n
+        assert st["write_back_bytes"] == per_layer * L
+        assert st["load_back_calls"] == L + 2 * L + 1
+        assert st["load_back_tokens"] == n * (3 * L + 1)
+        assert st["load_back_bytes"] == per_layer * (3 * L + 1)
+        assert st["device_errors"] == 1
+    finally:
+        if graph is not None:
+            graph.close()
+        rig.close()
