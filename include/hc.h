@@ -222,6 +222,7 @@ int hc_pool_sync(hc_pool* pool);
  *               when the call returns.
  *   done_event: hipEvent_t recorded on the copy stream after the last byte is
  *               enqueued, or NULL.
+ * n must be below 2^31 (the plan numbers tokens in int32), else HC_ERR_INVALID.
  * Errors are reported before anything is enqueued; done_event is still
  * recorded on error when the pool is valid. */
 int hc_write_back_all_layers(hc_pool* pool, const int64_t* device_idx, const int64_t* host_idx,
