@@ -19,7 +19,11 @@
  *   [P3] "[HiCache] Opt-in rank-sharded host tier for DSA under TP"
  *        (sglang PR 41984): Modifications (page_first_direct host pools for
  *        the MLA latent and the DSA indexer-K), Accuracy Tests (pages are
- *        restored bit-exactly).
+ *        restored bit-exactly), Modifications again for the per-layer
+ *        exchange of a layer-owner sharded host tier: the owner of a layer
+ *        gathers the rows it loaded into a staging buffer, broadcasts it, and
+ *        every other rank scatters it into the same device slots (device slot
+ *        allocation is replicated across the ranks).
  *   [P4] prhub summary of sglang PR 28434 (staged write-back JIT kernel for
  *        hybrid pools), key source excerpts: the CPU mock of the staged copy
  *        writes, for every layer, host[dst_index, layer] = device_layer[src_index]
@@ -47,6 +51,11 @@
  *   - Indices are token-granular int64; host index h names page h / P,
  *     row h % P; device and host indices are each distinct and in range.
  *     Rows not named in the index list are left untouched.
+ *   - Exchange staging bytes ([P3] leaves them open): sub-buffer after
+ *     sub-buffer; inside sub-buffer b the rows of the listed device slots in
+ *     list order, or for page blocks one block per page (the block of the
+ *     slot at list positions 0, P, 2P, ...) in list order.  The list names
+ *     whole device pages in row order when a sub-buffer holds page blocks.
  *
  * Payload bytes are opaque: nothing is interpreted as a number.
  */
@@ -317,6 +326,85 @@ int orc_h2h_load(const orc_geom* pf, const orc_geom* sh, uint8_t* host, const ui
         for (int32_t r = 0; r < rows; r++)
           memcpy(host + orc_host_offset(pf, b, dst_pages[i], l, r), store + orc_host_offset(sh, b, src_shards[i], l, r),
                  (size_t)pf->bytes[b]);
+    }
+  }
+  return ORC_OK;
+}
+
+/* ---------------------------------------------------------------- layer exchange
+ * [P3] Modifications (load-back of a rank-sharded tier): the owner of a layer
+ * gathers the rows it loaded into a staging buffer; the other ranks scatter that
+ * buffer into the same device slots.  The staging byte order is the reading
+ * stated at the top of this file.  The list d holds n distinct device slots in
+ * [0, S); with page blocks n is a multiple of P and positions kP..kP+P-1 hold
+ * the slots d0..d0+P-1 of one whole device page (d0 % P == 0). */
+static int check_exchange_list(const orc_geom* g, const int64_t* d, int64_t n) {
+  if (orc_check_geom(g) != ORC_OK || n < 0 || (n > 0 && !d)) return ORC_ERR_INVALID;
+  const int64_t P = g->page_size;
+  unsigned char* seen = (unsigned char*)calloc((size_t)g->device_slots, 1);
+  if (!seen) return ORC_ERR_INVALID;
+  int rc = ORC_OK;
+  for (int64_t i = 0; i < n; i++) {
+    if (d[i] < 0 || d[i] >= g->device_slots || seen[d[i]]) { rc = ORC_ERR_INVALID; break; }
+    seen[d[i]] = 1;
+  }
+  free(seen);
+  if (rc == ORC_OK && has_page_blocks(g)) {
+    if (n % P != 0) return ORC_ERR_INVALID;
+    for (int64_t k = 0; k < n; k += P) {
+      if (d[k] % P != 0) return ORC_ERR_INVALID;
+      for (int64_t r = 1; r < P; r++)
+        if (d[k + r] != d[k] + r) return ORC_ERR_INVALID;
+    }
+  }
+  return rc;
+}
+
+/* Bytes of one layer's staging for n list entries, or -1 on bad arguments:
+ * every token row once, every page block once per page. */
+int64_t orc_layer_packed_bytes(const orc_geom* g, int64_t n) {
+  if (orc_check_geom(g) != ORC_OK || n < 0) return -1;
+  int64_t total = 0;
+  for (int b = 0; b < g->nsub; b++) {
+    if (g->gran[b] == ORC_PAGE_BLOCKS) {
+      if (n % g->page_size != 0) return -1;
+      total += (n / g->page_size) * g->bytes[b];
+    } else {
+      total += n * g->bytes[b];
+    }
+  }
+  return total;
+}
+
+/* Owner side: out <- the rows of layer `layer` at the listed slots, in staging order. */
+int orc_layer_pack(const orc_geom* g, int32_t layer, uint8_t* const* dev, const int64_t* d, int64_t n, uint8_t* out) {
+  if (check_exchange_list(g, d, n) != ORC_OK || !dev || (n > 0 && !out)) return ORC_ERR_INVALID;
+  if (layer < 0 || layer >= g->layers) return ORC_ERR_INVALID;
+  const int L = g->layers;
+  uint8_t* at = out;
+  for (int b = 0; b < g->nsub; b++) {
+    const int64_t step = g->gran[b] == ORC_PAGE_BLOCKS ? g->page_size : 1;
+    for (int64_t i = 0; i < n; i += step) {
+      memcpy(at, dev[b * L + layer] + orc_device_offset(g, b, d[i]), (size_t)g->bytes[b]);
+      at += g->bytes[b];
+    }
+  }
+  return ORC_OK;
+}
+
+/* Receiving side: the rows of layer `layer` at the listed slots <- in, read in
+ * staging order.  Nothing else changes. */
+int orc_layer_unpack(const orc_geom* g, int32_t layer, uint8_t* const* dev, const int64_t* d, int64_t n,
+                     const uint8_t* in) {
+  if (check_exchange_list(g, d, n) != ORC_OK || !dev || (n > 0 && !in)) return ORC_ERR_INVALID;
+  if (layer < 0 || layer >= g->layers) return ORC_ERR_INVALID;
+  const int L = g->layers;
+  const uint8_t* at = in;
+  for (int b = 0; b < g->nsub; b++) {
+    const int64_t step = g->gran[b] == ORC_PAGE_BLOCKS ? g->page_size : 1;
+    for (int64_t i = 0; i < n; i += step) {
+      memcpy(dev[b * L + layer] + orc_device_offset(g, b, d[i]), at, (size_t)g->bytes[b]);
+      at += g->bytes[b];
     }
   }
   return ORC_OK;

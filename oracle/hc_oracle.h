@@ -39,5 +39,9 @@ int orc_h2h_dump(const orc_geom* pf, const orc_geom* sh, const uint8_t* host, ui
                  const int64_t* src_pages, const int64_t* dst_shards, int64_t n);
 int orc_h2h_load(const orc_geom* pf, const orc_geom* sh, uint8_t* host, const uint8_t* store,
                  const int64_t* src_shards, const int64_t* dst_pages, int64_t n);
+int64_t orc_layer_packed_bytes(const orc_geom* g, int64_t n);
+int orc_layer_pack(const orc_geom* g, int32_t layer, uint8_t* const* dev, const int64_t* d, int64_t n, uint8_t* out);
+int orc_layer_unpack(const orc_geom* g, int32_t layer, uint8_t* const* dev, const int64_t* d, int64_t n,
+                     const uint8_t* in);
 
 #endif

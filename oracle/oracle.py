@@ -10,7 +10,9 @@ What it computes, and the passages it follows, is documented at the top of
 the hybrid-pool write-back page, key source excerpts), per-layer load-back
 (the loader-thread page, Motivation), the page_first_kv_split shard layout
 with zero padding to the alignment (the CacheStore H2H page, section
-"page_first_kv_split support"), and a round-trip row comparison.
+"page_first_kv_split support"), a round-trip row comparison, and the per-layer
+exchange of a rank-sharded host tier (the rank-sharded tier page, Modifications:
+the owner packs a loaded layer's rows into staging, the other ranks unpack them).
 """
 from __future__ import annotations
 
@@ -79,6 +81,9 @@ def load(path: str = _LIB) -> ctypes.CDLL:
         "orc_host_offsets": (ctypes.c_int, [G, ctypes.c_int, ctypes.c_int32, _P64, ctypes.c_int64, _P64]),
         "orc_h2h_dump": (ctypes.c_int, [G, G, _PU8, _PU8, _P64, _P64, ctypes.c_int64]),
         "orc_h2h_load": (ctypes.c_int, [G, G, _PU8, _PU8, _P64, _P64, ctypes.c_int64]),
+        "orc_layer_packed_bytes": (ctypes.c_int64, [G, ctypes.c_int64]),
+        "orc_layer_pack": (ctypes.c_int, [G, ctypes.c_int32, ctypes.POINTER(_PU8), _P64, ctypes.c_int64, _PU8]),
+        "orc_layer_unpack": (ctypes.c_int, [G, ctypes.c_int32, ctypes.POINTER(_PU8), _P64, ctypes.c_int64, _PU8]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -256,3 +261,34 @@ def h2h_load(pf: Geometry, sh: Geometry, host: np.ndarray, store: np.ndarray, sr
                             store.ctypes.data_as(_PU8), _pi64(a), _pi64(b), a.size)
     if rc != 0:
         raise ValueError("oracle h2h_load rejected its arguments")
+
+
+def layer_packed_bytes(g: Geometry, n: int) -> int:
+    """Bytes of one layer's exchange staging for n list entries."""
+    r = lib().orc_layer_packed_bytes(ctypes.byref(g.c()), n)
+    if r < 0:
+        raise ValueError("oracle layer_packed_bytes rejected its arguments")
+    return int(r)
+
+
+def layer_pack(g: Geometry, layer: int, dev, d) -> np.ndarray:
+    """Owner side of the layer exchange: the staging bytes of layer `layer` at slots d."""
+    d = _i64(d)
+    size = lib().orc_layer_packed_bytes(ctypes.byref(g.c()), d.size)  # -1: the call below rejects the list
+    out = np.zeros(max(int(size), 1), dtype=np.uint8)
+    rc = lib().orc_layer_pack(ctypes.byref(g.c()), layer, _layer_table(g, dev), _pi64(d), d.size,
+                              out.ctypes.data_as(_PU8))
+    if rc != 0:
+        raise ValueError("oracle layer_pack rejected its arguments")
+    return out[:size]
+
+
+def layer_unpack(g: Geometry, layer: int, dev, d, packed: np.ndarray) -> None:
+    """Receiving side of the layer exchange: rows of layer `layer` at slots d <- packed.  In place on ``dev``."""
+    d = _i64(d)
+    assert packed.dtype == np.uint8 and packed.flags.c_contiguous
+    assert packed.nbytes >= lib().orc_layer_packed_bytes(ctypes.byref(g.c()), d.size)
+    rc = lib().orc_layer_unpack(ctypes.byref(g.c()), layer, _layer_table(g, dev), _pi64(d), d.size,
+                                packed.ctypes.data_as(_PU8))
+    if rc != 0:
+        raise ValueError("oracle layer_unpack rejected its arguments")

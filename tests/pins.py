@@ -10,7 +10,10 @@ Each ``pin_*`` function raises AssertionError when the oracle disagrees with
   * invariants: a write-back followed by a load-back into fresh slots restores
     every row bit-exactly, untouched rows and pages keep their bytes, shard pad
     bytes become zero (CacheStore H2H page, "page_first_kv_split support"),
-  * closed forms worked out by hand in ``golden/layout_closed_forms.txt``.
+  * closed forms worked out by hand in ``golden/layout_closed_forms.txt``,
+  * for the per-layer exchange of a rank-sharded tier (rank-sharded tier page,
+    Modifications and Accuracy Tests): numpy gathers of the loaded rows, and two
+    replicas of a pool that agree again after every layer's exchange.
 
 ``run_all()`` runs every pin; the mutation test runs it in a subprocess
 against deliberately broken builds of the oracle and expects a failure.
@@ -488,10 +491,96 @@ def pin_burst_algebra():
         assert_dev_equal(x, y, f"{name}: load-back order")
 
 
+# ---------------------------------------------------------------- layer exchange of a rank-sharded tier
+def pin_layer_exchange_gather_formula():
+    """Exchange staging (rank-sharded tier page, Modifications: the owner gathers a
+    loaded layer's rows into a staging buffer) against numpy fancy indexing on
+    [units, E] views of the device layer: sub-buffer after sub-buffer, token rows
+    view[d], page blocks view[d[0::P] // P]; its size is the concatenation's."""
+    for seed, (name, g) in enumerate(GEOMS.items()):
+        rng = np.random.default_rng(900 + seed)
+        dev = random_device(g, rng)
+        dev0 = copy_device(dev)
+        d, _ = make_burst(g, rng)  # ragged n for token-row pools
+        for layer in range(g.layers):
+            parts = []
+            for b, (gran, e) in enumerate(g.subs):
+                view = dev[b][layer].reshape(-1, e)
+                parts.append(view[d[0::g.page_size] // g.page_size] if gran == B else view[d])
+            want = np.concatenate([x.reshape(-1) for x in parts])
+            got = O.layer_pack(g, layer, dev, d)
+            assert got.size == want.size == O.layer_packed_bytes(g, d.size), (name, layer)
+            assert np.array_equal(got, want), f"{name} layer {layer}: staging differs from the gather"
+        assert_dev_equal(dev, dev0, f"{name}: pack changed the device pool")
+        assert O.layer_pack(g, 0, dev, np.zeros(0, np.int64)).size == 0
+
+
+def pin_layer_exchange_restores_owner_rows():
+    """Two replicas of one device pool (every TP rank holds the same slots).  Layer by
+    layer the owner loads from its host pool, packs, and the other rank unpacks: the
+    other rank's pool then equals the structural load-back of the same rows, bit for
+    bit, with every other layer and slot untouched (the page's accuracy claim).  A
+    skipped exchange, the page's negative control, leaves the replicas different."""
+    for seed, (name, g) in enumerate(GEOMS.items()):
+        rng = np.random.default_rng(950 + seed)
+        owner = random_device(g, rng)
+        other = copy_device(owner)
+        host = rng.integers(0, 256, O.host_pool_bytes(g), dtype=np.uint8)
+        d, h = make_burst(g, rng)
+        want = copy_device(other)
+        for layer in range(g.layers):
+            want = expected_device_after_load_back(g, layer, want, host, h, d)
+            O.load_back_layer(g, layer, owner, host, h, d)
+            assert any(not np.array_equal(owner[b][layer], other[b][layer]) for b in range(len(g.subs))), \
+                f"{name} layer {layer}: negative control not caught"
+            O.layer_unpack(g, layer, other, d, O.layer_pack(g, layer, owner, d))
+            assert_dev_equal(other, want, f"{name} after the exchange of layer {layer}")
+        assert_dev_equal(other, owner, f"{name}: replicas differ after every exchange")
+
+
+def pin_layer_exchange_preconditions():
+    """Lists the exchange refuses: out-of-range or repeated slots, and with page blocks
+    a count that is not whole pages, a page not starting at a multiple of P, rows of a
+    page out of order.  Token-row pools take ragged and empty lists."""
+    g = GEOMS["pf_latent_indexer"]
+    P = g.page_size
+    dev = random_device(g, np.random.default_rng(990))
+    d = np.concatenate([p * P + np.arange(P) for p in (5, 0, 9)]).astype(np.int64)
+    O.layer_pack(g, 1, dev, d)
+    swapped = d.copy()
+    swapped[[1, 2]] = swapped[[2, 1]]
+    repeated = np.concatenate([d, d[:P]])
+    bad = {"not whole pages": d[:-1], "misaligned page": d + 1, "out of range": d + g.device_slots,
+           "rows out of order": swapped, "repeated page": repeated, "negative": d - P * 20}
+    for what, lst in bad.items():
+        try:
+            O.layer_pack(g, 0, dev, lst)
+        except ValueError:
+            pass
+        else:
+            raise AssertionError(f"exchange accepted a bad list: {what}")
+        try:
+            O.layer_unpack(g, 0, dev, lst, np.zeros(max(O.layer_packed_bytes(g, P * 4), 1), np.uint8))
+        except ValueError:
+            pass
+        else:
+            raise AssertionError(f"unpack accepted a bad list: {what}")
+    tok = GEOMS["pf_kv"]
+    dev = random_device(tok, np.random.default_rng(991))
+    assert O.layer_pack(tok, 0, dev, np.array([7, 3, 60, 11, 0])).size == 5 * (32 + 32)
+    try:
+        O.layer_pack(tok, 0, dev, np.array([7, 3, 7]))
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("exchange accepted a repeated slot")
+
+
 PINS = [pin_sizes_match_structure, pin_offsets_match_structure, pin_write_back_brute_force,
         pin_write_back_mock_formula, pin_load_back_brute_force, pin_round_trip_restores,
         pin_untouched_and_byte_accounting, pin_round_trip_check_counts, pin_index_preconditions,
-        pin_golden_closed_forms, pin_h2h_shard_dump_and_load, pin_burst_algebra]
+        pin_golden_closed_forms, pin_h2h_shard_dump_and_load, pin_burst_algebra,
+        pin_layer_exchange_gather_formula, pin_layer_exchange_restores_owner_rows, pin_layer_exchange_preconditions]
 
 
 def run_all() -> list:

@@ -71,6 +71,24 @@ MUTANTS = [
     ("device and host index swapped in write-back",
      "const uint8_t* src = dev[b * L + l] + orc_device_offset(g, b, d[i]);",
      "const uint8_t* src = dev[b * L + l] + orc_device_offset(g, b, h[i] % g->device_slots);"),
+    ("exchange pack reads layer 0",
+     "memcpy(at, dev[b * L + layer] + orc_device_offset(g, b, d[i]), (size_t)g->bytes[b]);",
+     "memcpy(at, dev[b * L + 0] + orc_device_offset(g, b, d[i]), (size_t)g->bytes[b]);"),
+    ("exchange unpack writes layer 0",
+     "memcpy(dev[b * L + layer] + orc_device_offset(g, b, d[i]), at, (size_t)g->bytes[b]);",
+     "memcpy(dev[b * L + 0] + orc_device_offset(g, b, d[i]), at, (size_t)g->bytes[b]);"),
+    ("exchange pack takes a page block at every token",
+     "  uint8_t* at = out;\n  for (int b = 0; b < g->nsub; b++) {\n    const int64_t step = g->gran[b] == ORC_PAGE_BLOCKS ? g->page_size : 1;",
+     "  uint8_t* at = out;\n  for (int b = 0; b < g->nsub; b++) {\n    const int64_t step = 1;"),
+    ("exchange unpack reads staging one row late",
+     "const uint8_t* at = in;", "const uint8_t* at = in + g->bytes[0];"),
+    ("exchange accepts a page that does not start at a multiple of P",
+     "if (d[k] % P != 0) return ORC_ERR_INVALID;", ";"),
+    ("exchange accepts repeated slots",
+     "if (d[i] < 0 || d[i] >= g->device_slots || seen[d[i]]) { rc = ORC_ERR_INVALID; break; }",
+     "if (d[i] < 0 || d[i] >= g->device_slots) { rc = ORC_ERR_INVALID; break; }"),
+    ("exchange staging size counts page blocks per token",
+     "total += (n / g->page_size) * g->bytes[b];", "total += n * g->bytes[b];"),
 ]
 
 
