@@ -45,7 +45,7 @@ HC_FLAG_PROFILE = 2
 HC_MAX_SUBBUFS = 4
 
 # hc_pool_kernel_time kinds
-KIND_GATHER, KIND_ZC_WRITE, KIND_ZC_READ, KIND_PADS, KIND_COMPARE, KIND_COPY_ENGINE = range(6)
+KIND_GATHER, KIND_ZC_WRITE, KIND_ZC_READ, KIND_PADS, KIND_COMPARE, KIND_COPY_ENGINE, KIND_PACK, KIND_UNPACK = range(8)
 
 
 class hc_subbuf_desc(ctypes.Structure):
@@ -102,6 +102,9 @@ _SIGS = {
     "hc_write_back_all_layers": (ctypes.c_int, [_V, _V, _V, ctypes.c_int64, _V]),
     "hc_load_back_layer": (ctypes.c_int, [_V, ctypes.c_int32, _V, _V, ctypes.c_int64, _V]),
     "hc_round_trip_check": (ctypes.c_int, [_V, _V, _V, ctypes.c_int64, _I64P]),
+    "hc_layer_pack_bytes": (ctypes.c_int, [_V, ctypes.c_int64, _I64P]),
+    "hc_layer_pack": (ctypes.c_int, [_V, ctypes.c_int32, _V, ctypes.c_int64, _V, ctypes.c_int64, _V]),
+    "hc_layer_unpack": (ctypes.c_int, [_V, ctypes.c_int32, _V, ctypes.c_int64, _V, ctypes.c_int64, _V]),
     "hc_load_back_graph_create": (ctypes.c_int, [_V, _V, _V, ctypes.c_int64, ctypes.POINTER(_V),
                                                  ctypes.POINTER(_V)]),
     "hc_load_back_graph_launch": (ctypes.c_int, [_V]),
@@ -310,6 +313,13 @@ def host_offset(desc, sub: int, page: int, layer: int, row: int) -> int:
     return out.value
 
 
+def _staging_bytes(x, what: str) -> int:
+    """Size in bytes of an exchange staging buffer: a contiguous CUDA tensor."""
+    if not getattr(x, "is_cuda", False) or not x.is_contiguous():
+        raise TypeError(f"{what} must be a contiguous CUDA tensor")
+    return x.numel() * x.element_size()
+
+
 def _ptr(x) -> int:
     """Address of a torch tensor, a numpy array, a HostBuffer or an int."""
     if x is None:
@@ -360,8 +370,9 @@ def _torch_int64():
 
 class Pool:
     """Owns one hc_pool handle.  device_layers[b][l] are torch CUDA tensors (or raw
-    addresses); host is a HostBuffer; staging a torch CUDA tensor or None; stream a
-    torch.cuda.Stream (the copy stream)."""
+    addresses); host is a HostBuffer (None with host_pages=0: a device-only pool for the
+    layer exchange); staging a torch CUDA tensor or None; stream a torch.cuda.Stream
+    (the copy stream)."""
 
     def __init__(self, *, layers, page_size, subs, device_slots, host_pages, device_layers, host,
                  stream, layout=HC_LAYOUT_PAGE_FIRST, shard_align=4096, staging=None,
@@ -372,7 +383,7 @@ class Pool:
         self.desc, self._keep = make_desc(
             layers=layers, page_size=page_size, subs=sub_specs, device_slots=device_slots,
             host_pages=host_pages, layout=layout, shard_align=shard_align, host_ptr=_ptr(host),
-            host_bytes=host.nbytes, staging_ptr=_ptr(staging),
+            host_bytes=host.nbytes if host is not None else 0, staging_ptr=_ptr(staging),
             staging_bytes=(staging.numel() * staging.element_size()) if staging is not None else 0,
             stream_ptr=stream.cuda_stream if stream is not None else 0,
             write_back_mode=write_back_mode, load_back_mode=load_back_mode, flags=flags, max_ctas=max_ctas)
@@ -439,6 +450,27 @@ class Pool:
         check(lib.hc_round_trip_check(self.handle, _V(_ptr(idx_a)), _V(_ptr(idx_b)), n, ctypes.byref(out)),
               "hc_round_trip_check")
         return out.value
+
+    # Layer exchange of a rank-sharded host tier (rank-sharded tier page, Modifications):
+    # the owner packs a loaded layer's rows, the other ranks unpack the broadcast bytes.
+    def layer_pack_bytes(self, n: int) -> int:
+        out = ctypes.c_int64()
+        check(lib.hc_layer_pack_bytes(self.handle, n, ctypes.byref(out)), "hc_layer_pack_bytes")
+        return out.value
+
+    def layer_pack(self, layer: int, device_idx, dst, event: HipEvent | None = None) -> None:
+        """dst <- rows of `layer` at device_idx, sub-buffer after sub-buffer (dst: CUDA tensor)."""
+        n = _index_list(device_idx, "device_idx", True)
+        check(lib.hc_layer_pack(self.handle, layer, _V(_ptr(device_idx)), n, _V(_ptr(dst)), _staging_bytes(dst, "dst"),
+                                event.handle if event else None), "hc_layer_pack")
+        _in_use_on(self.stream, device_idx, dst)
+
+    def layer_unpack(self, layer: int, src, device_idx, event: HipEvent | None = None) -> None:
+        """Rows of `layer` at device_idx <- src, in the order layer_pack writes."""
+        n = _index_list(device_idx, "device_idx", True)
+        check(lib.hc_layer_unpack(self.handle, layer, _V(_ptr(src)), _staging_bytes(src, "src"), _V(_ptr(device_idx)), n,
+                                  event.handle if event else None), "hc_layer_unpack")
+        _in_use_on(self.stream, device_idx, src)
 
     def sync(self) -> None:
         check(lib.hc_pool_sync(self.handle), "hc_pool_sync")

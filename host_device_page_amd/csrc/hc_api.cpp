@@ -60,7 +60,7 @@ int set_err(int code, const char* fmt, ...) {
     if (e_ != hipSuccess) return set_err(HC_ERR_HIP, "%s failed: %s", #call, hipGetErrorString(e_)); \
   } while (0)
 
-constexpr int kKinds = 6;  // gather, zc write, zc read, pads, compare, copy engine
+constexpr int kKinds = 8;  // gather, zc write, zc read, pads, compare, copy engine, pack, unpack
 // Zero-copy kernels wait on the host link, not on the CU: 8-16 workgroups already
 // saturate it (measured 55 GB/s from 8 up to 1024), and every extra workgroup holds
 // a slot on a CU that the forward pass could use.  With 16, a bf16 GEMM consumer on
@@ -368,6 +368,12 @@ int plan_upload(hc_pool* p, int64_t bytes) {
 
 inline int64_t align16(int64_t x) { return (x + 15) / 16 * 16; }
 
+int no_host_pool() {
+  return set_err(HC_ERR_INVALID,
+                 "the pool has no host pages (a device-only pool): only the layer exchange and the round-trip "
+                 "check run on it");
+}
+
 int record_event(void* ev, hipStream_t s) {
   if (!ev) return HC_OK;
   hipError_t e = hipEventRecord((hipEvent_t)ev, s);
@@ -397,11 +403,19 @@ int hc_desc_check(const hc_pool_desc* desc) {
                    "the host-link rate, the zero-copy kernel does not");
   if (desc->flags & ~(HC_FLAG_VALIDATE | HC_FLAG_PROFILE)) return set_err(HC_ERR_INVALID, "unknown flags");
   if (desc->max_ctas < 0 || desc->max_ctas > 65536) return set_err(HC_ERR_INVALID, "max_ctas must be in [0, 65536]");
-  if (!desc->host_base) return set_err(HC_ERR_INVALID, "host_base is null");
-  if (((uintptr_t)desc->host_base) % 16 != 0) return set_err(HC_ERR_UNSUPPORTED, "host_base must be 16-byte aligned");
-  if (desc->host_bytes < L.host_bytes)
-    return set_err(HC_ERR_INVALID, "host_bytes %lld below the layout's %lld", (long long)desc->host_bytes,
-                   (long long)L.host_bytes);
+  if (L.H == 0) {
+    // a device-only pool: the layer exchange and the round-trip check, no host transfers
+    if (desc->host_base) return set_err(HC_ERR_INVALID, "a pool without host pages takes no host_base");
+    if (desc->write_back_mode == HC_MODE_STAGED || desc->staging)
+      return set_err(HC_ERR_INVALID, "a pool without host pages has no write-back: no staging, no HC_MODE_STAGED");
+  } else {
+    if (!desc->host_base) return set_err(HC_ERR_INVALID, "host_base is null");
+    if (((uintptr_t)desc->host_base) % 16 != 0)
+      return set_err(HC_ERR_UNSUPPORTED, "host_base must be 16-byte aligned");
+    if (desc->host_bytes < L.host_bytes)
+      return set_err(HC_ERR_INVALID, "host_bytes %lld below the layout's %lld", (long long)desc->host_bytes,
+                     (long long)L.host_bytes);
+  }
   for (int b = 0; b < L.nsub; b++) {
     if (!desc->sub[b].device_layers) return set_err(HC_ERR_INVALID, "sub-buffer %d: device_layers is null", b);
     for (int l = 0; l < L.L; l++) {
@@ -507,17 +521,17 @@ int hc_pool_create(const hc_pool_desc* desc, hc_pool** out) {
   p->flags = desc->flags;
   p->max_ctas = desc->max_ctas > 0 ? desc->max_ctas : kDefaultMaxCtas;
   // memory kinds
-  {
+  if (L.H > 0) {
     void* dptr = nullptr;
     if (hipHostGetDevicePointer(&dptr, desc->host_base, 0) != hipSuccess || !dptr) {
       (void)hipGetLastError();
       return bail(set_err(HC_ERR_INVALID, "host_base is not pinned (page-locked) host memory"));
     }
     p->host = (uint8_t*)dptr;
+    // every buffer the kernels address must hold what the layout puts in it
+    rc = check_extent(desc->host_base, L.host_bytes, false, "host_base");
+    if (rc != HC_OK) return bail(rc);
   }
-  // every buffer the kernels address must hold what the layout puts in it
-  rc = check_extent(desc->host_base, L.host_bytes, false, "host_base");
-  if (rc != HC_OK) return bail(rc);
   for (int b = 0; b < L.nsub; b++) {
     const int64_t units = L.gran[b] == HC_PAGE_BLOCKS ? L.S / L.P : L.S;
     for (int l = 0; l < L.L; l++) {
@@ -640,6 +654,7 @@ int hc_write_back_all_layers(hc_pool* p, const int64_t* device_idx, const int64_
     int r2 = record_event(event, p->stream);
     return code != HC_OK ? code : r2;
   };
+  if (p->lay.H == 0) return finish(no_host_pool());
   if (n < 0) return finish(set_err(HC_ERR_INVALID, "n must be >= 0"));
   if (n == 0) return finish(HC_OK);
   if (!device_idx || !host_idx) return finish(set_err(HC_ERR_INVALID, "null index list"));
@@ -758,6 +773,7 @@ int hc_load_back_layer(hc_pool* p, int32_t layer, const int64_t* host_idx, const
     return code != HC_OK ? code : r2;
   };
   if (rc != HC_OK) return finish(rc);
+  if (p->lay.H == 0) return finish(no_host_pool());
   if (layer < 0 || layer >= p->lay.L)
     return finish(set_err(HC_ERR_INVALID, "layer %d out of range [0, %d)", layer, p->lay.L));
   if (n < 0) return finish(set_err(HC_ERR_INVALID, "n must be >= 0"));
@@ -811,6 +827,76 @@ int hc_round_trip_check(hc_pool* p, const int64_t* idx_a, const int64_t* idx_b, 
   return rc;
 }
 
+int hc_layer_pack_bytes(const hc_pool* p, int64_t n, int64_t* out_bytes) {
+  if (!p || !out_bytes) return set_err(HC_ERR_INVALID, "null argument");
+  if (n < 0) return set_err(HC_ERR_INVALID, "n must be >= 0");
+  if (p->lay.has_blocks && n % p->lay.P != 0)
+    return set_err(HC_ERR_INVALID, "page-block sub-buffers need whole pages (n %% page_size != 0)");
+  *out_bytes = layer_bytes(p, n);
+  return HC_OK;
+}
+
+namespace {
+
+// One side of the layer exchange; `staging` is dst (pack) or src (unpack).
+int layer_exchange(hc_pool* p, bool pack, int32_t layer, const int64_t* device_idx, int64_t n, const void* staging,
+                   int64_t staging_bytes, void* event) {
+  std::lock_guard<std::recursive_mutex> lock(p->mu);
+  int rc = use_device(p);
+  auto finish = [&](int code) {
+    int r2 = record_event(event, p->stream);
+    return code != HC_OK ? code : r2;
+  };
+  if (rc != HC_OK) return finish(rc);
+  if (layer < 0 || layer >= p->lay.L)
+    return finish(set_err(HC_ERR_INVALID, "layer %d out of range [0, %d)", layer, p->lay.L));
+  if (n < 0) return finish(set_err(HC_ERR_INVALID, "n must be >= 0"));
+  if (n == 0) return finish(HC_OK);
+  if (!device_idx || !staging) return finish(set_err(HC_ERR_INVALID, "null index list or staging buffer"));
+  if (p->lay.has_blocks && n % p->lay.P != 0)
+    return finish(set_err(HC_ERR_INVALID, "page-block sub-buffers need whole pages (n %% page_size != 0)"));
+  const int64_t need = layer_bytes(p, n);
+  if (staging_bytes < need)
+    return finish(set_err(HC_ERR_INVALID, "staging_bytes %lld below the %lld bytes of %lld entries",
+                          (long long)staging_bytes, (long long)need, (long long)n));
+  if (((uintptr_t)staging) % 16 != 0) return finish(set_err(HC_ERR_UNSUPPORTED, "staging must be 16-byte aligned"));
+  rc = check_device_list(p, device_idx, n, "device_idx");
+  if (rc == HC_OK) rc = check_device_ptr(staging, p->device, "staging");
+  if (rc == HC_OK) rc = check_extent(staging, need, true, "staging");
+  if (rc != HC_OK) return finish(rc);
+  hipError_t e;
+  {
+    Timer t(p, pack ? 6 : 7);
+    e = hc::launch_layer_exchange(p->geom, pack, layer, device_idx, n, (uint8_t*)staging, p->d_err, p->num_cus,
+                                  t.ev, p->stream);
+    t.done(e == hipSuccess);
+  }
+  if (e != hipSuccess) return finish(set_err(HC_ERR_HIP, "exchange launch failed: %s", hipGetErrorString(e)));
+  return finish(HC_OK);
+}
+
+}  // namespace
+
+int hc_layer_pack(hc_pool* p, int32_t layer, const int64_t* device_idx, int64_t n, void* dst, int64_t dst_bytes,
+                  void* event) {
+  if (!p) {
+    if (event) (void)hipEventRecord((hipEvent_t)event, nullptr);
+    return set_err(HC_ERR_INVALID, "pool is null");
+  }
+  TraceRange range("hc_layer_pack");
+  return layer_exchange(p, true, layer, device_idx, n, dst, dst_bytes, event);
+}
+
+int hc_layer_unpack(hc_pool* p, int32_t layer, const void* src, int64_t src_bytes, const int64_t* device_idx,
+                    int64_t n, void* event) {
+  if (!p) {
+    if (event) (void)hipEventRecord((hipEvent_t)event, nullptr);
+    return set_err(HC_ERR_INVALID, "pool is null");
+  }
+  TraceRange range("hc_layer_unpack");
+  return layer_exchange(p, false, layer, device_idx, n, src, src_bytes, event);
+}
+
 }  // extern "C"
 
 struct hc_lb_graph {
@@ -842,6 +928,7 @@ int hc_load_back_graph_create(hc_pool* p, const int64_t* host_idx, const int64_t
   if (n < 0) return set_err(HC_ERR_INVALID, "n must be >= 0");
   if (n > 0 && (!host_idx || !device_idx)) return set_err(HC_ERR_INVALID, "null index list");
   std::lock_guard<std::recursive_mutex> lock(p->mu);
+  if (p->lay.H == 0) return no_host_pool();
   if (p->flags & HC_FLAG_PROFILE)
     return set_err(HC_ERR_UNSUPPORTED, "a pool created with HC_FLAG_PROFILE cannot be captured");
   int rc = use_device(p);
@@ -1001,6 +1088,8 @@ void pool_loader_ops(hc_pool* pool, hc_loader_ops* ops) {
 }
 
 int pool_layers(const hc_pool* pool) { return pool->lay.L; }
+
+bool pool_has_host(const hc_pool* pool) { return pool->lay.H > 0; }
 
 int graph_matches(const hc_pool* pool, const void* graph, void* const* events, int32_t L) {
   const hc_lb_graph* g = (const hc_lb_graph*)graph;

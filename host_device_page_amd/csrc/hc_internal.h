@@ -64,6 +64,7 @@ int set_error(int code, const char* fmt, ...);
 // The pool's own device operations for an hc_loader, and its layer count.
 void pool_loader_ops(hc_pool* pool, hc_loader_ops* ops);
 int pool_layers(const hc_pool* pool);
+bool pool_has_host(const hc_pool* pool);  // false for a device-only pool (no host pages)
 // Loaders and captured graphs that hold a pool: hc_pool_destroy refuses while any do.
 void pool_hold(hc_pool* pool);
 void pool_release(hc_pool* pool);
@@ -91,6 +92,21 @@ hipError_t launch_zc_read(const Geom& g, int32_t layer, const int64_t* host_idx,
                           const LaunchTimer& t, hipStream_t stream);
 hipError_t launch_zero_pads(uint8_t* base, const int64_t* pages, int64_t npages, int64_t stride,
                             int64_t off, int64_t bytes, const LaunchTimer& t, hipStream_t stream);
+// Layer exchange of a layer-owner sharded tier (hc_exchange.hip): per sub-buffer the
+// positions it moves (n token rows, or n / P page blocks), its offset in the staging
+// buffer, its positions per unit and the running unit count.
+struct XPlan {
+  int64_t positions[HC_MAX_SUBBUFS];
+  int64_t seg[HC_MAX_SUBBUFS];
+  int64_t units_end[HC_MAX_SUBBUFS];
+  int32_t tile[HC_MAX_SUBBUFS];
+};
+// Fills *x for n list entries; returns the staging bytes of one layer.
+int64_t exchange_plan(const Geom& g, int64_t n, int32_t num_cus, XPlan* x);
+// pack: staging <- rows of `layer` at dev_idx; else the rows <- staging.
+hipError_t launch_layer_exchange(const Geom& g, bool pack, int32_t layer, const int64_t* dev_idx, int64_t n,
+                                 uint8_t* staging, int32_t* err, int32_t num_cus, const LaunchTimer& t,
+                                 hipStream_t stream);
 hipError_t launch_compare(const Geom& g, const int64_t* a, const int64_t* c, int64_t n,
                           unsigned long long* counter, int32_t* err, const LaunchTimer& t,
                           hipStream_t stream);

@@ -49,8 +49,8 @@ int layout_from_desc(const hc_pool_desc* d, Layout* out, char* msg, size_t len) 
   if (d->layout != HC_LAYOUT_PAGE_FIRST && d->layout != HC_LAYOUT_KV_SPLIT_SHARD &&
       d->layout != HC_LAYOUT_PAGE_FIRST_TOKEN_MAJOR)
     return fail(msg, len, HC_ERR_INVALID, "unknown layout");
-  if (d->device_slots < 1 || d->host_pages < 1)
-    return fail(msg, len, HC_ERR_INVALID, "device_slots and host_pages must be >= 1");
+  if (d->device_slots < 1) return fail(msg, len, HC_ERR_INVALID, "device_slots must be >= 1");
+  if (d->host_pages < 0) return fail(msg, len, HC_ERR_INVALID, "host_pages must be >= 0 (0: a device-only pool)");
   Layout L;
   L.L = d->num_layers;
   L.P = d->page_size;

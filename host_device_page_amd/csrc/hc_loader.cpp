@@ -132,6 +132,7 @@ int hc_loader_create(hc_pool* pool, const hc_loader_ops* ops, int32_t num_layers
     use = *ops;
   } else {
     if (!pool) return loader_err(HC_ERR_INVALID, "a loader without ops needs a pool");
+    if (!hc::pool_has_host(pool)) return loader_err(HC_ERR_INVALID, "the pool has no host pages to load from");
     hc::pool_loader_ops(pool, &use);
   }
   if (!use.load_layer || !use.wait_event || !use.record_event || !use.sync_event || !use.stream_wait)

@@ -129,7 +129,11 @@ typedef struct hc_pool_desc {
   int32_t layout;       /* HC_LAYOUT_* */
   hc_subbuf_desc sub[HC_MAX_SUBBUFS];
   int64_t device_slots; /* S token slots per layer (a multiple of P when a sub-buffer holds page blocks) */
-  int64_t host_pages;   /* H pages (shards) in the host pool */
+  int64_t host_pages;   /* H pages (shards) in the host pool.  0 makes a device-only pool: host_base
+                           and staging are NULL, write-back and load-back are refused, and only the
+                           layer exchange and the round-trip check run on it (a TP rank's view of
+                           every layer of its replicated device pool, next to the pool of the host
+                           layers it owns) */
   int64_t shard_align;  /* shard layout: power of two >= 16 (4096 for Direct I/O); ignored otherwise */
   void* host_base;      /* pinned host memory (hc_host_alloc or hipHostMalloc), >= hc_host_pool_bytes */
   int64_t host_bytes;   /* size of host_base */
@@ -249,6 +253,43 @@ int hc_load_back_layer(hc_pool* pool, int32_t layer, const int64_t* host_idx,
  * *mismatched_units (host memory). */
 int hc_round_trip_check(hc_pool* pool, const int64_t* idx_a, const int64_t* idx_b, int64_t n,
                         int64_t* mismatched_units);
+
+/* ---------------------------------------------------------------- layer exchange of a rank-sharded tier
+ * A layer-owner sharded host tier (rank-sharded tier page, sglang PR 41984,
+ * Modifications) gives each host layer one owner rank, round-robin over the TP
+ * ranks; device pools and slot allocation stay replicated.  Write-back and
+ * load-back of a rank then cover only its own layers: a pool over the device
+ * buffers of the owned layers (the descriptor takes one pointer per layer) with a
+ * host pool of those layers.  On load-back, once the owner has loaded layer l into
+ * its device slots, it packs those rows into a staging buffer, the buffer is
+ * broadcast to the other TP ranks (the caller's collective on its own
+ * communicator; not part of this library), and each of them unpacks it into the
+ * same slots.  Each rank's layer-done event follows its own exchange.  Pack and
+ * unpack run on any pool, including a device-only one (host_pages = 0) over all
+ * layers, which is how a rank addresses the layers it does not own.
+ *
+ * Staging bytes: sub-buffer after sub-buffer; inside sub-buffer b the token rows
+ * of device_idx[0..n) in list order (n * elem_bytes), or for page blocks the block
+ * of each page, taken at list positions 0, P, 2P, ... ((n / P) * elem_bytes).
+ *   device_idx: n int64 slots in device memory (or pinned host memory), read on the
+ *               GPU, distinct, the same list on every rank; with page blocks n is a
+ *               multiple of P and every page is named whole in row order.
+ *   dst / src:  device memory of the pool's device, 16-byte aligned, holding at
+ *               least hc_layer_pack_bytes(n) bytes inside its allocation (dst_bytes /
+ *               src_bytes give the caller's size; smaller is HC_ERR_INVALID).
+ *   event:      hipEvent_t recorded on the copy stream after the kernel, or NULL;
+ *               recorded on failure too (on the null stream when pool is NULL).
+ * Out-of-range slots are skipped and reported as HC_ERR_DEVICE by the next
+ * hc_pool_sync (a skipped slot leaves its staging row, or its device row, as it
+ * was); with HC_FLAG_VALIDATE page-block slots are also checked to form whole
+ * device pages.  Only layer `layer` of the device pool (unpack) or the staging
+ * buffer (pack) changes.  Neither call touches the host link; hc_pool_stats does
+ * not count them. */
+int hc_layer_pack_bytes(const hc_pool* pool, int64_t n, int64_t* out_bytes);
+int hc_layer_pack(hc_pool* pool, int32_t layer, const int64_t* device_idx, int64_t n, void* dst,
+                  int64_t dst_bytes, void* event);
+int hc_layer_unpack(hc_pool* pool, int32_t layer, const void* src, int64_t src_bytes,
+                    const int64_t* device_idx, int64_t n, void* event);
 
 /* ---------------------------------------------------------------- captured load-back bursts
  * The per-layer load-back chain of one burst, captured once into a HIP graph on
@@ -421,7 +462,8 @@ int hc_pool_get_stats(hc_pool* pool, hc_pool_stats* out);
 
 /* Per-kernel timing with HIP events on the copy stream (pools with HC_FLAG_PROFILE).
  * kind: 0 gather to staging, 1 zero-copy write-back, 2 zero-copy load-back,
- *       3 pad fill, 4 round-trip compare, 5 staged copy-engine transfers.
+ *       3 pad fill, 4 round-trip compare, 5 staged copy-engine transfers,
+ *       6 layer pack, 7 layer unpack.
  * Returns the number of timed launches and their summed milliseconds since the
  * last reset (synchronizes the copy stream).  reset != 0 clears the counters. */
 int hc_pool_kernel_time(hc_pool* pool, int32_t kind, int32_t reset, int64_t* launches,

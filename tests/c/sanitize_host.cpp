@@ -32,6 +32,7 @@ int set_error(int code, const char* fmt, ...) {
 }
 void pool_loader_ops(hc_pool*, hc_loader_ops*) { abort(); }  // every loader here brings its own ops
 int pool_layers(const hc_pool*) { return 0; }
+bool pool_has_host(const hc_pool*) { return true; }
 void pool_hold(hc_pool*) {}
 void pool_release(hc_pool*) {}
 int graph_matches(const hc_pool*, const void*, void* const*, int32_t) { abort(); }  // pool ops only

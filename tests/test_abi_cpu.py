@@ -70,11 +70,25 @@ def test_desc_check_accepts_valid():
     (dict(device_slots=1 << 60), B.HC_ERR_INVALID, "device layer size overflows"),
     (dict(max_ctas=-1), B.HC_ERR_INVALID, "max_ctas"),
     (dict(max_ctas=65537), B.HC_ERR_INVALID, "max_ctas"),
+    (dict(host_pages=-1), B.HC_ERR_INVALID, "host_pages"),
+    # a device-only pool (host_pages = 0) takes no host memory and no write-back staging
+    (dict(host_pages=0), B.HC_ERR_INVALID, "takes no host_base"),
+    (dict(host_pages=0, host_ptr=0, write_back_mode=B.HC_MODE_STAGED), B.HC_ERR_INVALID, "no write-back"),
+    (dict(host_pages=0, host_ptr=0, staging_ptr=0x20000, staging_bytes=1 << 30), B.HC_ERR_INVALID, "no staging"),
 ])
 def test_desc_check_rejects(kw, code, text):
     d, _k = desc(**kw)
     assert status(d) == code
     assert text in B.lib.hc_last_error().decode()
+
+
+def test_device_only_descriptor():
+    """host_pages = 0: no host pool at all (host_base NULL, 0 host bytes, no page offsets)."""
+    d, _k = desc(host_pages=0, host_ptr=0, host_bytes=0)
+    assert status(d) == B.HC_OK, B.lib.hc_last_error()
+    out = ctypes.c_int64(-1)
+    assert B.lib.hc_host_pool_bytes(ctypes.byref(d), ctypes.byref(out)) == B.HC_OK and out.value == 0
+    assert B.lib.hc_host_offset(ctypes.byref(d), 0, 0, 0, 0, ctypes.byref(out)) == B.HC_ERR_INVALID
 
 
 def test_null_arguments_without_gpu():
@@ -95,6 +109,10 @@ def test_null_arguments_without_gpu():
     assert B.lib.hc_load_back_graph_launch(None) == B.HC_ERR_INVALID
     assert B.lib.hc_pool_get_stats(None, ctypes.byref(B.hc_pool_stats())) == B.HC_ERR_INVALID
     assert B.lib.hc_load_back_graph_destroy(None) == B.HC_OK
+    n = ctypes.c_int64()
+    assert B.lib.hc_layer_pack_bytes(None, 64, ctypes.byref(n)) == B.HC_ERR_INVALID
+    assert B.lib.hc_layer_pack(None, 0, None, 0, None, 0, None) == B.HC_ERR_INVALID
+    assert B.lib.hc_layer_unpack(None, 0, None, 0, None, 0, None) == B.HC_ERR_INVALID
 
 
 GEOMS = [
