@@ -12,8 +12,9 @@ slots come from a free list with half the segments contiguous runs of 1-64.
 Prints one JSON line: whole-step host-link throughput (GB/s, both directions'
 bytes over the step time), per-direction rates, the host-link roofline of the
 dominant kernel (HIP-event timing on the copy stream against the hipMemcpyAsync
-peak measured here), the HBM roofline of the staged relayout kernel, and the
-CPU oracle timed on a bounded sample.
+peak measured here), the HBM roofline of the staged relayout kernel and of the
+layer exchange kernels of a rank-sharded tier, and the CPU oracle timed on a
+bounded sample.
 """
 from __future__ import annotations
 
@@ -75,6 +76,8 @@ def parse():
                     help="instead: time host-to-host shard dump/load of the shard workload with 1..16 CPU workers")
     ap.add_argument("--max-pinned-gib", type=float, default=64.0,
                     help="cap on the pinned host pool; a larger pool keeps the burst and shrinks the page count")
+    ap.add_argument("--exchange-only", action="store_true",
+                    help="only time the layer exchange kernels (pack / unpack) on the workload's device pool")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="run one plain device-to-device copy of this size first (a known-size "
                          "reference for the FETCH_SIZE / WRITE_SIZE counters)")
@@ -289,27 +292,31 @@ def duplex_measurement(B, torch, np, hip, make_pool, shape, burst, d_t, h_np, d2
     return duplex
 
 
-def kernel_source_digest() -> str:
-    """sha256 of the kernel source with comments and whitespace removed: the counters
-    stay attached to the kernels they measured, not to their comments."""
+def kernel_source_digest(source: str = "kernels") -> str:
+    """sha256 of a kernel source (hc_kernels.hip, or hc_exchange.hip for "exchange") with
+    comments and whitespace removed: the counters stay attached to the kernels they
+    measured, not to their comments."""
     import hashlib
     import re
-    src = open(os.path.join(ROOT, "host_device_page_amd", "csrc", "hc_kernels.hip")).read()
+    fname = "hc_kernels.hip" if source == "kernels" else "hc_exchange.hip"
+    src = open(os.path.join(ROOT, "host_device_page_amd", "csrc", fname)).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     src = re.sub(r"//[^\n]*", "", src)
     src = "".join(src.split())
     return hashlib.sha256(src.encode()).hexdigest()
 
 
-def counter_traffic(workload: str, kernel: str):
+def counter_traffic(workload: str, kernel: str, source: str = "kernels"):
     """Bytes per launch that the FETCH_SIZE / WRITE_SIZE counter passes measured for
     `kernel` (scaled by the known-size copy), from the committed profile summary, or
-    None when the kernel source changed since the counters were taken."""
-    path = os.path.join(ROOT, "profiles", f"{workload}_counters.json")
+    None when the kernel source changed since the counters were taken.  source:
+    "kernels" (the transfer kernels) or "exchange" (the layer exchange kernels)."""
+    suffix = "_counters.json" if source == "kernels" else "_exchange_counters.json"
+    path = os.path.join(ROOT, "profiles", f"{workload}{suffix}")
     if not os.path.exists(path):
         return None
     prof = json.load(open(path))
-    if prof.get("kernel_code_digest") != kernel_source_digest():
+    if prof.get("kernel_code_digest") != kernel_source_digest(source):
         return None
     k = prof["kernels"].get(kernel)
     if not k:
@@ -550,6 +557,78 @@ def h2h_main(args):
     print(json.dumps(out), flush=True)
 
 
+def calibration_copy(torch, mib: int) -> None:
+    """A plain device-to-device copy of known size, for scaling the HBM byte counters."""
+    if not mib:
+        return
+    nb = mib << 20
+    src = torch.ones(nb, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"[bench] calibration copy of {nb} bytes done")
+    del src, dst
+
+
+def layer_exchange_timing(B, np, shape, dev, d_t, n, stream, counter_workload=None, rounds=2):
+    """The per-layer exchange of a rank-sharded host tier (the owner packs a loaded layer's
+    rows into staging, the other ranks unpack them), on a device-only pool over the
+    workload's device buffers: every layer packed into its own staging buffer, then every
+    layer unpacked from it, `rounds` times, with per-launch HIP-event timing.  Each launch
+    finds its rows and its staging cold (the layers cycle through more than the 256 MB
+    Infinity Cache), as a receiving rank's unpack after the broadcast would.  Unpack puts
+    back the bytes pack took, so the pool is unchanged.  Algorithmic bytes per launch: the
+    layer's packed bytes read plus the same written.  For scale, a plain device-to-device
+    copy of the same bytes is timed too."""
+    import torch
+    L = shape.layers
+    xpool = B.Pool(layers=L, page_size=shape.page_size, subs=list(shape.subs), device_slots=shape.device_slots,
+                   host_pages=0, device_layers=[[t[l] for l in range(L)] for t in dev], host=None, stream=stream,
+                   flags=B.HC_FLAG_PROFILE)
+    packed = xpool.layer_pack_bytes(n)
+    staging = torch.empty((L, packed), dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    xpool.layer_pack(0, d_t, staging[0])
+    xpool.layer_unpack(0, staging[0], d_t)
+    xpool.sync()
+    xpool.kernel_time(B.KIND_PACK, reset=True)
+    for _ in range(rounds):
+        for l in range(L):
+            xpool.layer_pack(l, d_t, staging[l])
+        for l in range(L):
+            xpool.layer_unpack(l, staging[l], d_t)
+    n_p, ms_p = xpool.kernel_time(B.KIND_PACK)
+    n_u, ms_u = xpool.kernel_time(B.KIND_UNPACK)
+    xpool.sync()
+    xpool.close()
+    # the same bytes through a plain copy, source and destination as cold as the kernels'
+    # (rows half the layer count apart, so neither was touched recently)
+    e0, e1 = B.HipEvent(timing=True), B.HipEvent(timing=True)
+    half = max(1, L // 2)
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for _ in range(rounds):
+            for l in range(L):
+                staging[(l + half) % L].copy_(staging[l])
+        e1.record(stream)
+    e1.synchronize()
+    copies = rounds * L if L > 1 else 0
+    copy_gbs = 2 * packed * copies / (e0.elapsed_ms(e1) * 1e-3) / 1e9 if copies else None
+    del staging
+    out = {"layer_packed_bytes": packed, "tokens": n, "launches": {"pack": n_p, "unpack": n_u},
+           "plain_copy_same_bytes_GBps": round(copy_gbs, 1) if copy_gbs else None}
+    for name, cnt, ms, kname in (("pack", n_p, ms_p, "k_layer_exchange<true>"),
+                                 ("unpack", n_u, ms_u, "k_layer_exchange<false>")):
+        avg = ms / max(1, cnt)
+        gbs = 2 * packed / (avg * 1e-3) / 1e9
+        traffic = counter_traffic(counter_workload, kname, "exchange") if counter_workload else None
+        out[name] = {"bound": "hbm", "kernel": kname, "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "avg_launch_ms": round(avg, 5),
+                     "bytes_per_launch": 2 * packed, "traffic": traffic["bytes"] if traffic else None}
+    return out
+
+
 def load_back_graph_timing(B, np, pool, stream, L, h, d, link_bytes, reps=7):
     """The per-layer load-back of (h, d) as one captured graph against the same L calls
     made eagerly, on an unprofiled pool: GPU time per layer (HIP events on the copy
@@ -674,6 +753,19 @@ def main():
     for g, e in shape.subs:
         units = shape.device_slots // P if g == 1 else shape.device_slots
         dev.append(torch.empty((L, units * e), dtype=torch.uint8, device="cuda").random_(0, 256, generator=gen))
+    if args.exchange_only:
+        # no host pool: the exchange runs on device memory only
+        calibration_copy(torch, args.calibration_copy_mib)
+        stream = torch.cuda.Stream()
+        burst = W.burst_for(shape, seed=1)
+        d2 = W.fresh_slots_like(shape, burst, seed=2)
+        d2_t = torch.from_numpy(d2).cuda()
+        torch.cuda.synchronize()
+        log(f"[bench] setup {time.perf_counter() - t_setup:.1f} s; exchange of {burst.n} tokens per layer")
+        res = layer_exchange_timing(B, np, shape, dev, d2_t, burst.n, stream, counter_workload=shape.name)
+        log(f"[bench] layer exchange {res}")
+        print(json.dumps({"layer_exchange": res, "workload": shape.name}), flush=True)
+        return
     probe, _k = B.make_desc(layers=L, page_size=P, subs=[(g, e, [1] * L) for g, e in shape.subs],
                             device_slots=shape.device_slots, host_pages=shape.host_pages, layout=shape.layout,
                             shard_align=shape.align)
@@ -695,15 +787,7 @@ def main():
                       layout=shape.layout, shard_align=shape.align, staging=staging, write_back_mode=mode,
                       flags=flags, max_ctas=args.max_ctas if max_ctas is None else max_ctas)
 
-    if args.calibration_copy_mib:
-        nb = args.calibration_copy_mib << 20
-        src = torch.ones(nb, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        log(f"[bench] calibration copy of {nb} bytes done")
-        del src, dst
+    calibration_copy(torch, args.calibration_copy_mib)
     pool = make_pool(wb_mode)
     burst = W.burst_for(shape, seed=1)
     d2 = W.fresh_slots_like(shape, burst, seed=2)
@@ -884,6 +968,8 @@ def main():
     hpool.close()
     log(f"[bench] load-back hand-over per burst (ms): {handover}")
     pool.close()
+    exchange = layer_exchange_timing(B, np, shape, dev, d2_t, burst.n, stream, counter_workload=shape.name)
+    log(f"[bench] layer exchange {exchange}")
 
     # staged relayout kernel (HBM-bound): same burst through the staged write-back
     roofline_hbm = None
@@ -963,6 +1049,7 @@ def main():
         "roofline": roofline,
         "roofline_hbm": roofline_hbm,
         "staged_write_back": staged,
+        "layer_exchange": exchange,
         "cpu_baseline": cpu,
         "cpu_baseline_threads": cpu_mt,
     }
