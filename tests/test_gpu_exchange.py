@@ -296,3 +296,42 @@ def test_refusals_and_device_reports():
         pool.close()
         host.free()
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("seed", range(200))
+def test_random_exchange(seed):
+    """Random pools of the randomized parity sweep (layers, page size, row and block sizes,
+    partial pages, slot patterns): one random layer packed and unpacked against the oracle."""
+    from test_gpu_random import random_case
+    shape, d, _h, _d2, _mode, _staging, _ctas = random_case(seed)
+    rng = np.random.default_rng(7000 + seed)
+    L = shape.layers
+    layer = int(rng.integers(0, L))
+    flags = B.HC_FLAG_VALIDATE if rng.random() < 0.3 else 0
+    say(f"[exchange random {seed}] L={L} P={shape.page_size} subs={shape.subs} n={d.size} layer={layer} flags={flags}")
+    g = oracle_geom(shape, L)
+    stream = torch.cuda.Stream()
+    owner, other = device_pool(shape, L, 7100 + seed), device_pool(shape, L, 7200 + seed)
+    torch.cuda.synchronize()
+    owner0, other0 = to_np(owner), to_np(other)
+    po = device_only_pool(shape, L, owner, stream, flags=flags)
+    pr = device_only_pool(shape, L, other, stream, flags=flags)
+    try:
+        need = po.layer_pack_bytes(d.size)
+        staging = torch.full((need + 16,), 0xC3, dtype=torch.uint8, device="cuda")
+        d_t = cuda_i64(d)
+        po.layer_pack(layer, d_t, staging)
+        pr.layer_unpack(layer, staging, d_t)
+        po.sync()
+        pr.sync()
+        got = staging.cpu().numpy()
+        packed = O.layer_pack(g, layer, owner0, d)
+        assert_bytes_equal(got[:need], packed, "staging after pack")
+        assert np.all(got[need:] == 0xC3), "pack wrote past its bytes"
+        want = [[a.copy() for a in row] for row in other0]
+        O.layer_unpack(g, layer, want, d, packed)
+        assert_dev_equal(to_np(other), want, "receiving pool after unpack")
+        assert_dev_equal(to_np(owner), owner0, "pack changed the owner's pool")
+    finally:
+        po.close()
+        pr.close()
