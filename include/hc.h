@@ -13,7 +13,11 @@
  *   load-back (host -> device), one layer per call, each call recording a
  *     layer-done event so a forward pass can start layer l while later layers
  *     are still in flight (loader-thread page, sglang PR 38472: Motivation and
- *     Modifications; rank-sharded host tier page, sglang PR 41984).
+ *     Modifications; rank-sharded host tier page, sglang PR 41984);
+ *   the per-layer exchange of a rank-sharded host tier (rank-sharded host tier
+ *     page, Modifications): the owner of a layer packs the rows it loaded into a
+ *     staging buffer, the other TP ranks unpack the broadcast bytes into the
+ *     same slots (device memory only; the broadcast is the caller's).
  *
  * Host layouts:
  *   HC_LAYOUT_PAGE_FIRST      per sub-buffer [page][layer][row][elem_bytes]
