@@ -412,6 +412,32 @@ def cpu_baseline(shape, burst, d2, seconds: float, threads: int = 1):
                       f"{el:.1f} s, {how}, host-RAM replicas of the device pool and the host pool"}
 
 
+def cpu_exchange_baseline(shape, burst, d2, seconds: float):
+    """The oracle's layer exchange, as written, on a host-memory replica of layer 0: pack
+    the burst's slots, unpack them into a second replica, repeated until `seconds` pass,
+    on one thread.  Counted like the GPU kernels: each of the two calls reads and writes
+    the layer's packed bytes."""
+    import numpy as np
+
+    from oracle import oracle as O
+    g1 = O.Geometry(1, shape.page_size, list(shape.subs), 1, shape.device_slots, shape.layout, shape.align)
+    owner = [[np.ones(g1.device_units(b) * e, dtype=np.uint8)] for b, (_, e) in enumerate(shape.subs)]
+    other = [[np.full(g1.device_units(b) * e, 2, dtype=np.uint8)] for b, (_, e) in enumerate(shape.subs)]
+    packed_bytes = O.layer_packed_bytes(g1, d2.size)
+    O.layer_unpack(g1, 0, other, d2, O.layer_pack(g1, 0, owner, d2))  # untimed: first touch of the pages
+    passes = 0
+    t0 = time.perf_counter()
+    while True:
+        O.layer_unpack(g1, 0, other, d2, O.layer_pack(g1, 0, owner, d2))
+        passes += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    el = time.perf_counter() - t0
+    return {"value": round(4 * packed_bytes * passes / el / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"C oracle pack + unpack of layer 0 at the burst's {d2.size} load-back slots "
+                      f"({packed_bytes} packed bytes), {passes} passes in {el:.1f} s, single thread, host-RAM replicas"}
+
+
 def layer_pipeline(B, torch, pool, shape, h_t, d2_t, n, stream, layer_events, make_pool, args):
     """Overlap of the per-layer load-back with a consumer on a second stream.  The
     consumer's work per layer is a bf16 matmul sized to about one layer's transfer
@@ -1022,6 +1048,8 @@ def main():
         if t > 1:
             cpu_mt = cpu_baseline(shape, burst, d2, args.cpu_seconds / 2, threads=t)
             log(f"[bench] CPU oracle, {cpu_mt['cores']} threads: {cpu_mt['value']} GB/s")
+        exchange["cpu_baseline"] = cpu_exchange_baseline(shape, burst, d2, args.cpu_seconds / 4)
+        log(f"[bench] CPU oracle, layer exchange: {exchange['cpu_baseline']['value']} GB/s")
 
     pages = burst.pages.size
     out = {
