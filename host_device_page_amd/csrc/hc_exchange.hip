@@ -59,8 +59,30 @@ typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(1))) const v4u* gload_t;
 typedef __attribute__((address_space(1))) v4u* gstore_t;
 
-__device__ __forceinline__ v4u xld16(uint64_t a) { return *reinterpret_cast<gload_t>(a); }
-__device__ __forceinline__ void xst16(uint64_t a, v4u v) { *reinterpret_cast<gstore_t>(a) = v; }
+// Both sides of an exchange are streamed once, so loads and stores carry the
+// non-temporal hint (bit 0: loads, bit 1: stores).  Measured with the launch shape above,
+// cold, two rounds: pack / unpack of a DeepSeek-V3 layer 4.39-4.43 / 4.15-4.25 TB/s with
+// both hints against 3.77 / 3.81 without, MLA + indexer 4.91-5.06 / 4.73-4.89 against
+// 4.33-4.60 / 4.45-4.71, Llama-3-8B 4.71-4.94 / 4.65-4.84 against 4.09-4.12 / 4.22-4.26
+// (94-97 % of the same-size copy); stores alone or loads alone gain less.  Eight waves
+// per SIMD (HC_XCHG_MIN_WAVES, which needs 4 loads in flight per lane to fit 64
+// registers) was slower with or without the hints.
+#ifndef HC_XCHG_NT
+#define HC_XCHG_NT 3
+#endif
+#ifndef HC_XCHG_MIN_WAVES
+#define HC_XCHG_MIN_WAVES 1  // launch-bounds floor on waves per SIMD (caps registers)
+#endif
+__device__ __forceinline__ v4u xld16(uint64_t a) {
+  if (HC_XCHG_NT & 1) return __builtin_nontemporal_load(reinterpret_cast<gload_t>(a));
+  return *reinterpret_cast<gload_t>(a);
+}
+__device__ __forceinline__ void xst16(uint64_t a, v4u v) {
+  if (HC_XCHG_NT & 2)
+    __builtin_nontemporal_store(v, reinterpret_cast<gstore_t>(a));
+  else
+    *reinterpret_cast<gstore_t>(a) = v;
+}
 
 // The error word of the pool: bit `bit`, and the smallest flagged list position in the
 // uint64 at byte 8 (the same report the transfer kernels make).
@@ -70,7 +92,7 @@ __device__ __forceinline__ void flag_position(int32_t* err, int bit, int64_t pos
 }
 
 template <bool PACK>
-__global__ __launch_bounds__(kXThreads) void k_layer_exchange(Geom g, XPlan x, int32_t layer,
+__global__ __launch_bounds__(kXThreads, HC_XCHG_MIN_WAVES) void k_layer_exchange(Geom g, XPlan x, int32_t layer,
                                                               const int64_t* __restrict__ dev_idx,
                                                               uint8_t* __restrict__ staging,
                                                               int32_t* __restrict__ err) {
