@@ -107,7 +107,7 @@ enum { HC_LAYOUT_PAGE_FIRST = 0, HC_LAYOUT_KV_SPLIT_SHARD = 1, HC_LAYOUT_PAGE_FI
  * kernels read or write the pinned host pool directly.  AUTO: write-back is staged
  * when the descriptor brings a staging buffer of at least one page image, else
  * zero-copy; load-back is zero-copy (hc_pool_mode reports the choice).
- * Measured on MI355X: zero-copy write-back reaches ~98 % of the host-link peak, but
+ * Measured on MI355X: zero-copy write-back reaches ~99 % of the host-link peak, but
  * while its kernel saturates the link, compute kernels on other streams slow down
  * until they barely overlap it; staged write-back runs ~12 % slower alone and leaves
  * concurrent compute almost untouched, because the copy engines carry its host
