@@ -64,7 +64,7 @@ typedef __attribute__((address_space(1))) v4u* gstore_t;
 // cold, two rounds: pack / unpack of a DeepSeek-V3 layer 4.39-4.43 / 4.15-4.25 TB/s with
 // both hints against 3.77 / 3.81 without, MLA + indexer 4.91-5.06 / 4.73-4.89 against
 // 4.33-4.60 / 4.45-4.71, Llama-3-8B 4.71-4.94 / 4.65-4.84 against 4.09-4.12 / 4.22-4.26
-// (94-97 % of the same-size copy); stores alone or loads alone gain less.  Eight waves
+// (89-97 % of the same-size copy); stores alone or loads alone gain less.  Eight waves
 // per SIMD (HC_XCHG_MIN_WAVES, which needs 4 loads in flight per lane to fit 64
 // registers) was slower with or without the hints.
 #ifndef HC_XCHG_NT
