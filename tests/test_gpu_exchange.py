@@ -335,3 +335,47 @@ def test_random_exchange(seed):
     finally:
         po.close()
         pr.close()
+
+
+def test_exchange_in_a_captured_graph():
+    """Pack and unpack captured into a HIP graph on the pools' stream (a caller that replays
+    its per-layer exchange instead of enqueueing it), replayed three times with eager
+    writes to the owner's layer in between; every replay is checked against the oracle."""
+    shape = W.SHAPES["dsa_mla_indexer_78l"]
+    shape = W.shape_scaled(shape, "graph", layers=3, device_slots=65536, host_pages=8)
+    L = shape.layers
+    d = W.page_aligned_slots(120, shape.device_slots, shape.page_size, 40)
+    g = oracle_geom(shape, L)
+    stream = torch.cuda.Stream()
+    owner, other = device_pool(shape, L, 121), device_pool(shape, L, 122)
+    po, pr = device_only_pool(shape, L, owner, stream), device_only_pool(shape, L, other, stream)
+    try:
+        d_t = cuda_i64(d)
+        staging = torch.zeros(po.layer_pack_bytes(d.size), dtype=torch.uint8, device="cuda")
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream, capture_error_mode="thread_local"):
+            po.layer_pack(1, d_t, staging)
+            pr.layer_unpack(1, staging, d_t)
+        torch.cuda.synchronize()
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(123)
+        for replay in range(3):
+            for t in owner:  # new rows to exchange, written eagerly between replays
+                t[1].random_(0, 256, generator=gen)
+            torch.cuda.synchronize()
+            owner0, other0 = to_np(owner), to_np(other)
+            graph.replay()
+            torch.cuda.synchronize()
+            po.sync()
+            pr.sync()
+            packed = O.layer_pack(g, 1, owner0, d)
+            assert_bytes_equal(staging.cpu().numpy(), packed, f"staging after replay {replay}")
+            want = [[a.copy() for a in row] for row in other0]
+            O.layer_unpack(g, 1, want, d, packed)
+            assert_dev_equal(to_np(other), want, f"receiving pool after replay {replay}")
+        del graph
+    finally:
+        po.close()
+        pr.close()
+        torch.cuda.synchronize()
