@@ -243,8 +243,10 @@ struct Timer {
   hc_pool* p;
   int kind;
   hc::LaunchTimer ev;
-  Timer(hc_pool* pool, int k) : p(pool), kind(k) {
-    if (p->flags & HC_FLAG_PROFILE) {
+  // enabled = false: no timing for this launch (a launch recorded into a graph, whose
+  // launch-stamped events and harvesting synchronizations would break the capture)
+  Timer(hc_pool* pool, int k, bool enabled = true) : p(pool), kind(k) {
+    if (enabled && (p->flags & HC_FLAG_PROFILE)) {
       ev.start = take_event(p);
       ev.stop = ev.start ? take_event(p) : nullptr;
       if (!ev.stop) {
@@ -367,6 +369,22 @@ int plan_upload(hc_pool* p, int64_t bytes) {
 }
 
 inline int64_t align16(int64_t x) { return (x + 15) / 16 * 16; }
+
+// Whether the pool's stream is recording a graph: the library's own capture of a load-back
+// burst, or a caller's capture around library calls.
+bool stream_capturing(const hc_pool* p) {
+  if (p->capturing) return true;
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(p->stream, &st) != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  return st != hipStreamCaptureStatusNone;
+}
+
+int refuse_capture(const char* what, const char* why) {
+  return set_err(HC_ERR_UNSUPPORTED, "%s cannot run while the pool's stream is capturing a graph: %s", what, why);
+}
 
 int no_host_pool() {
   return set_err(HC_ERR_INVALID,
@@ -625,6 +643,7 @@ int hc_pool_sync(hc_pool* p) {
   std::lock_guard<std::recursive_mutex> lock(p->mu);
   int rc = use_device(p);
   if (rc != HC_OK) return rc;
+  if (stream_capturing(p)) return refuse_capture("hc_pool_sync", "it waits for the stream");
   HIP_TRY(hipMemcpyAsync(p->h_err, p->d_err, 16, hipMemcpyDeviceToHost, p->stream));
   HIP_TRY(hipStreamSynchronize(p->stream));
   const int32_t e = *p->h_err;
@@ -655,6 +674,10 @@ int hc_write_back_all_layers(hc_pool* p, const int64_t* device_idx, const int64_
     return code != HC_OK ? code : r2;
   };
   if (p->lay.H == 0) return finish(no_host_pool());
+  if (stream_capturing(p))
+    return finish(refuse_capture("hc_write_back_all_layers",
+                                 "its plan is built on the CPU for each call, so a replay would reuse a stale "
+                                 "plan"));
   if (n < 0) return finish(set_err(HC_ERR_INVALID, "n must be >= 0"));
   if (n == 0) return finish(HC_OK);
   if (!device_idx || !host_idx) return finish(set_err(HC_ERR_INVALID, "null index list"));
@@ -788,7 +811,7 @@ int hc_load_back_layer(hc_pool* p, int32_t layer, const int64_t* host_idx, const
   }
   hipError_t e;
   {
-    Timer t(p, 2);
+    Timer t(p, 2, !stream_capturing(p));
     e = hc::launch_zc_read(p->geom, layer, host_idx, device_idx, n, p->host, p->d_err, p->max_ctas, t.ev, p->stream);
     t.done(e == hipSuccess);
   }
@@ -807,6 +830,7 @@ int hc_round_trip_check(hc_pool* p, const int64_t* idx_a, const int64_t* idx_b, 
   std::lock_guard<std::recursive_mutex> lock(p->mu);
   int rc = use_device(p);
   if (rc != HC_OK) return rc;
+  if (stream_capturing(p)) return refuse_capture("hc_round_trip_check", "it waits for the stream");
   if (n < 0) return set_err(HC_ERR_INVALID, "n must be >= 0");
   if (n > 0 && (!idx_a || !idx_b)) return set_err(HC_ERR_INVALID, "null index list");
   if (n > 0) {
@@ -866,7 +890,7 @@ int layer_exchange(hc_pool* p, bool pack, int32_t layer, const int64_t* device_i
   if (rc != HC_OK) return finish(rc);
   hipError_t e;
   {
-    Timer t(p, pack ? 6 : 7);
+    Timer t(p, pack ? 6 : 7, !stream_capturing(p));
     e = hc::launch_layer_exchange(p->geom, pack, layer, device_idx, n, (uint8_t*)staging, p->d_err, p->num_cus,
                                   t.ev, p->stream);
     t.done(e == hipSuccess);

@@ -75,6 +75,14 @@
  *   - Sizes: elem_bytes is a multiple of 16 (16-byte vectors, the element-size
  *     rule of the hybrid-pool write-back page) and at most 65536; every device
  *     layer pointer, the host pool and the staging buffer are 16-byte aligned.
+ *   - Graph capture: hc_load_back_layer, hc_layer_pack and hc_layer_unpack may be
+ *     recorded into a caller's HIP graph on the pool's stream; a replay reads the
+ *     index lists and buffers as they are when it runs, and a pool created with
+ *     HC_FLAG_PROFILE does not time the launches it records.  While the pool's
+ *     stream is capturing, hc_write_back_all_layers (its plan is built on the CPU
+ *     for each call, so a replay would reuse a stale plan), hc_pool_sync and
+ *     hc_round_trip_check (both wait for the stream) return HC_ERR_UNSUPPORTED
+ *     and enqueue nothing.
  */
 #ifndef HC_H
 #define HC_H
@@ -194,7 +202,13 @@ int hc_host_free(void* ptr);
 /* ---------------------------------------------------------------- pool lifetime */
 
 /* Validates desc, copies the per-layer pointer tables to device memory, and
- * records the modes.  The pool belongs to the current HIP device: the layer
+ * records the modes.  The descriptor follows the host-pool excerpt of the
+ * hybrid-pool write-back page (prhub summary of sglang PR 28434, key source
+ * excerpts): the host pool is page-first, the device staging buffer for the
+ * staged write-back is allocated once, up front, and sized in pages (its chunk),
+ * per-layer device pointers are kept in a table (as the pools' k_data_ptrs), and
+ * the element size per token must be a multiple of 16 bytes.  The pool belongs to
+ * the current HIP device: the layer
  * buffers, the staging buffer and copy_stream must be that device's
  * (HC_ERR_INVALID otherwise), and every later call makes it current.  Each device
  * layer, the used part of the staging buffer and (when HIP can look it up) the host
@@ -250,7 +264,11 @@ int hc_write_back_all_layers(hc_pool* pool, const int64_t* device_idx, const int
 int hc_load_back_layer(hc_pool* pool, int32_t layer, const int64_t* host_idx,
                        const int64_t* device_idx, int64_t n, void* event);
 
-/* Round-trip check: counts the (token, sub-buffer, layer) units whose device
+/* Round-trip check.  The pages print no such call: its name and meaning are this
+ * library's own, the check that a write-back followed by a load-back into other
+ * slots restored every row (the accuracy claim of the rank-sharded tier page,
+ * Accuracy Tests: pages come back bit-exactly).  It counts the (token,
+ * sub-buffer, layer) units whose device
  * rows at slots idx_a[i] and idx_b[i] differ, over all layers and sub-buffers
  * (page blocks once per page, at tokens with idx_a[i] % P == 0).  Indices are
  * device-resident.  Synchronizes the copy stream and writes the count to

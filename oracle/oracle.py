@@ -204,6 +204,12 @@ def host_offsets(g: Geometry, b: int, layer: int, h) -> np.ndarray:
     return out
 
 
+def check_geom(g: Geometry) -> bool:
+    """Whether the oracle accepts the geometry (positive sizes, known layout and granularity, at
+    most MAX_SUB sub-buffers, a positive shard alignment, whole device pages with page blocks)."""
+    return lib().orc_check_geom(ctypes.byref(g.c())) == 0
+
+
 def check_indices(g: Geometry, d, h) -> bool:
     d, h = _i64(d), _i64(h)
     if d.shape != h.shape:

@@ -20,6 +20,7 @@ against deliberately broken builds of the oracle and expects a failure.
 """
 from __future__ import annotations
 
+import ctypes
 import os
 import sys
 
@@ -576,11 +577,126 @@ def pin_layer_exchange_preconditions():
         raise AssertionError("exchange accepted a repeated slot")
 
 
+# ---------------------------------------------------------------- helpers the GPU tests rely on
+def _refused(fn) -> bool:
+    try:
+        fn()
+    except ValueError:
+        return True
+    return False
+
+
+def pin_host_offsets_walk():
+    """orc_host_offsets, the batched lookup with which the full-size GPU tests find the
+    host bytes of every named row, against the structural walk's running sums: every host
+    token of every geometry, in order and shuffled, for every sub-buffer and layer (a page
+    block at every row of its page).  A token past the pool, a negative token, a bad
+    sub-buffer or a bad layer is refused; an empty list gives no offsets."""
+    for k, (name, g) in enumerate(GEOMS.items()):
+        pos, _ = positions(g)
+        P = g.page_size
+        tokens = np.arange(g.host_pages * P, dtype=np.int64)
+        shuffled = np.random.default_rng(1000 + k).permutation(tokens)
+        for b, (gran, _) in enumerate(g.subs):
+            for l in range(g.layers):
+                for order in (tokens, shuffled):
+                    if gran == B:
+                        want = [pos[("blk", b, int(t) // P, l)][0] for t in order]
+                    else:
+                        want = [pos[("row", b, int(t) // P, l, int(t) % P)][0] for t in order]
+                    got = O.host_offsets(g, b, l, order)
+                    assert np.array_equal(got, np.array(want, dtype=np.int64)), (name, b, l)
+        past = g.host_pages * P
+        for bad in ([past], [-1], [0, 1, past]):
+            assert _refused(lambda: O.host_offsets(g, 0, 0, bad)), (name, "token outside the pool accepted", bad)
+        assert _refused(lambda: O.host_offsets(g, len(g.subs), 0, [0])), (name, "sub-buffer past the last accepted")
+        assert _refused(lambda: O.host_offsets(g, -1, 0, [0])), (name, "negative sub-buffer accepted")
+        assert _refused(lambda: O.host_offsets(g, 0, g.layers, [0])), (name, "layer past the last accepted")
+        assert _refused(lambda: O.host_offsets(g, 0, -1, [0])), (name, "negative layer accepted")
+        assert O.host_offsets(g, 0, 0, np.zeros(0, np.int64)).size == 0
+
+
+def pin_host_offsets_golden():
+    """The batched lookup at the workloads' full sizes (offsets far past 2^32) against the
+    hand-derived closed forms: every host_offset line of the golden file, asked as the host
+    token page * P + row."""
+    with open(GOLDEN) as f:
+        lines = [ln.strip() for ln in f if ln.strip() and not ln.startswith("#")]
+    seen = 0
+    for ln in lines:
+        name, geo, q = [x.strip() for x in ln.split("|")]
+        lhs, rhs = [x.strip() for x in q.split("=")]
+        what, *args = lhs.split()
+        if what != "host_offset":
+            continue
+        layout, L, P, H, S, align, subs = geo.split()
+        sub = [((T if s[0] == "T" else B), int(s[1:])) for s in subs.split(",")]
+        lay = {"shard": O.KV_SPLIT_SHARD, "page_first": O.PAGE_FIRST, "token_major": O.PAGE_FIRST_TOKEN_MAJOR}[layout]
+        g = O.Geometry(int(L), int(P), sub, int(H), int(S), lay, int(align))
+        b, page, layer, row = [int(a) for a in args]
+        got = O.host_offsets(g, b, layer, [page * int(P) + row])
+        assert int(got[0]) == int(rhs), f"{name}: batched {lhs} = {int(got[0])}, closed form {rhs}"
+        seen += 1
+    assert seen >= 10
+
+
+def _raw_geom(g: O.Geometry, nsub: int, tail: bytes = b"") -> ctypes.Array:
+    """The C struct of g with its sub-buffer count overwritten, followed by `tail`: a way to
+    hand the oracle a count its arrays cannot hold, with readable memory behind them."""
+    c = g.c()
+    c.nsub = nsub
+    raw = bytes(c) + tail
+    return (ctypes.c_uint8 * len(raw)).from_buffer_copy(raw)
+
+
+def pin_geometry_refusals():
+    """orc_check_geom, which every oracle entry point runs first: every geometry of these
+    pins is accepted, and each rule refuses its own violation while a neighbour that keeps
+    the rule is accepted.  Refused: zero layers, page size or sizes; no sub-buffer or more
+    than four; an unknown layout or granularity; a shard layout with alignment 0 or
+    negative; page blocks over a slot count that is not whole pages (token rows alone take
+    any slot count)."""
+    for name, g in GEOMS.items():
+        assert O.check_geom(g), (name, "a pinned geometry refused")
+    base = GEOMS["pf_kv"]
+    def with_(**kw):
+        d = dict(layers=base.layers, page_size=base.page_size, subs=list(base.subs), host_pages=base.host_pages,
+                 device_slots=base.device_slots, layout=base.layout, align=base.align)
+        d.update(kw)
+        return O.Geometry(**d)
+    for what, g in {"zero layers": with_(layers=0), "zero page size": with_(page_size=0),
+                    "zero host pages": with_(host_pages=0), "zero device slots": with_(device_slots=0),
+                    "no sub-buffer": with_(subs=[]), "unknown layout": with_(layout=3),
+                    "zero row bytes": with_(subs=[(T, 32), (T, 0)]),
+                    "unknown granularity": with_(subs=[(T, 32), (2, 32)]),
+                    "shard alignment 0": with_(layout=O.KV_SPLIT_SHARD, align=0),
+                    "negative shard alignment": with_(layout=O.KV_SPLIT_SHARD, align=-4096),
+                    "page blocks over a partial device page": with_(subs=[(T, 32), (B, 48)], device_slots=65)}.items():
+        assert not O.check_geom(g), f"oracle accepted a geometry with {what}"
+    for what, g in {"four sub-buffers": with_(subs=[(T, 32)] * 4),
+                    "shard alignment 16": with_(layout=O.KV_SPLIT_SHARD, align=16),
+                    "token rows over 65 slots": with_(device_slots=65),
+                    "page blocks over 64 slots": with_(subs=[(T, 32), (B, 48)], device_slots=64)}.items():
+        assert O.check_geom(g), f"oracle refused a valid geometry with {what}"
+    # Five sub-buffers: the struct holds four.  The oracle must refuse on the count alone,
+    # so the memory a fifth entry would occupy is made to look valid: the fifth granularity
+    # overlaps the low word of the first row size (2^32 + 0: token rows), the fifth size
+    # sits right after the struct (16 bytes).
+    four = with_(subs=[(T, (1 << 32)), (T, 32), (T, 32), (T, 32)])
+    assert O.check_geom(four)
+    raw = _raw_geom(four, 5, tail=(16).to_bytes(8, "little") * 4)
+    lib = O.lib()
+    assert lib.orc_check_geom(ctypes.cast(raw, ctypes.POINTER(O._Geom))) != 0, "oracle accepted five sub-buffers"
+    # a refused geometry is refused by the entry points too
+    assert _refused(lambda: O.host_offsets(with_(layout=O.KV_SPLIT_SHARD, align=0), 0, 0, [0]))
+
+
 PINS = [pin_sizes_match_structure, pin_offsets_match_structure, pin_write_back_brute_force,
         pin_write_back_mock_formula, pin_load_back_brute_force, pin_round_trip_restores,
         pin_untouched_and_byte_accounting, pin_round_trip_check_counts, pin_index_preconditions,
         pin_golden_closed_forms, pin_h2h_shard_dump_and_load, pin_burst_algebra,
-        pin_layer_exchange_gather_formula, pin_layer_exchange_restores_owner_rows, pin_layer_exchange_preconditions]
+        pin_layer_exchange_gather_formula, pin_layer_exchange_restores_owner_rows, pin_layer_exchange_preconditions,
+        pin_host_offsets_walk, pin_host_offsets_golden, pin_geometry_refusals]
 
 
 def run_all() -> list:

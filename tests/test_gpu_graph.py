@@ -234,3 +234,60 @@ def test_pool_outlives_its_graphs_and_loaders():
         rig.pool.sync()
     finally:
         rig.close()
+
+
+@pytest.mark.gpu
+def test_caller_capture_rules_on_a_profiling_pool():
+    """A caller's own capture on the pool's stream.  The write-back (its plan is built on the
+    CPU per call), hc_pool_sync and hc_round_trip_check (they wait for the stream) are refused
+    with HC_ERR_UNSUPPORTED and leave the capture usable; per-layer load-backs and a layer pack
+    recorded on a profiling pool are not timed, and every replay (host pool rewritten between
+    replays) matches the oracle."""
+    shape = SHAPES[1]
+    say("[graph] caller capture on a profiling pool")
+    rig = Rig(shape, seed=9, flags=B.HC_FLAG_PROFILE)
+    try:
+        L = shape.layers
+        h, d = lists(shape, 5, 60)
+        h_t, d_t = cuda_i64(h), cuda_i64(d)
+        staging = torch.zeros(rig.pool.layer_pack_bytes(d.size), dtype=torch.uint8, device="cuda")
+        rig.pool.kernel_time(B.KIND_ZC_READ, reset=True)
+        torch.cuda.synchronize()
+        refused = {}
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=rig.stream, capture_error_mode="thread_local"):
+            for what, call in (("write-back", lambda: rig.pool.write_back_all_layers(d_t, h)),
+                               ("sync", rig.pool.sync),
+                               ("round-trip check", lambda: rig.pool.round_trip_check(d_t, d_t))):
+                try:
+                    call()
+                except B.HcError as e:
+                    refused[what] = e.code
+            for l in range(L):
+                rig.pool.load_back_layer(l, h_t, d_t)
+            rig.pool.layer_pack(L - 1, d_t, staging)
+        assert refused == {"write-back": B.HC_ERR_UNSUPPORTED, "sync": B.HC_ERR_UNSUPPORTED,
+                           "round-trip check": B.HC_ERR_UNSUPPORTED}, refused
+        torch.cuda.synchronize()
+        for replay in range(3):
+            randomize_host(rig, 70 + replay)
+            dev0, host0 = rig.dev_np(), rig.host.np.copy()
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            rig.pool.sync()
+            want = [[a.copy() for a in row] for row in dev0]
+            for l in range(L):
+                O.load_back_layer(rig.geom, l, want, host0, h, d)
+            assert_dev_equal(rig.dev_np(), want, f"device pool after replay {replay}")
+            packed = O.layer_pack(rig.geom, L - 1, want, d)
+            assert_bytes_equal(staging.cpu().numpy(), packed, f"pack staging after replay {replay}")
+            assert rig.pool.round_trip_check(d_t, d_t) == 0
+        launches, _ = rig.pool.kernel_time(B.KIND_ZC_READ)
+        assert launches == 0, "a recorded launch was timed"
+        rig.pool.load_back_layer(0, h_t, d_t)  # eager again: timed
+        launches, _ = rig.pool.kernel_time(B.KIND_ZC_READ)
+        assert launches == 1
+        del graph
+    finally:
+        rig.close()

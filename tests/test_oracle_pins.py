@@ -89,6 +89,31 @@ MUTANTS = [
      "if (d[i] < 0 || d[i] >= g->device_slots) { rc = ORC_ERR_INVALID; break; }"),
     ("exchange staging size counts page blocks per token",
      "total += (n / g->page_size) * g->bytes[b];", "total += n * g->bytes[b];"),
+    ("batched host offsets swap page and row",
+     "out[i] = orc_host_offset(g, b, h[i] / g->page_size, layer, (int32_t)(h[i] % g->page_size));",
+     "out[i] = orc_host_offset(g, b, h[i] % g->page_size, layer, (int32_t)(h[i] / g->page_size));"),
+    ("batched host offsets ignore the layer",
+     "out[i] = orc_host_offset(g, b, h[i] / g->page_size, layer, (int32_t)(h[i] % g->page_size));",
+     "out[i] = orc_host_offset(g, b, h[i] / g->page_size, 0, (int32_t)(h[i] % g->page_size));"),
+    ("batched host offsets take the row of the next token",
+     "out[i] = orc_host_offset(g, b, h[i] / g->page_size, layer, (int32_t)(h[i] % g->page_size));",
+     "out[i] = orc_host_offset(g, b, h[i] / g->page_size, layer, (int32_t)((h[i] + 1) % g->page_size));"),
+    ("batched host offsets accept the first token past the pool",
+     "if (h[i] < 0 || h[i] >= g->host_pages * g->page_size) return ORC_ERR_INVALID;",
+     "if (h[i] < 0 || h[i] > g->host_pages * g->page_size) return ORC_ERR_INVALID;"),
+    ("batched host offsets accept a layer past the last",
+     "b < 0 || b >= g->nsub || layer < 0 || layer >= g->layers) return ORC_ERR_INVALID;",
+     "b < 0 || b >= g->nsub || layer < 0 || layer > g->layers) return ORC_ERR_INVALID;"),
+    ("geometry without sub-buffers accepted",
+     "g->nsub <= 0 || g->nsub > ORC_MAX_SUB)", "g->nsub > ORC_MAX_SUB)"),
+    ("geometry with five sub-buffers accepted",
+     "g->nsub <= 0 || g->nsub > ORC_MAX_SUB)", "g->nsub <= 0 || g->nsub > ORC_MAX_SUB + 1)"),
+    ("shard alignment of 0 accepted",
+     "if (g->layout == ORC_KV_SPLIT_SHARD && g->align <= 0) return ORC_ERR_INVALID;", ";"),
+    ("page blocks over a partial device page accepted",
+     "if (has_page_blocks(g) && g->device_slots % g->page_size != 0) return ORC_ERR_INVALID;", ";"),
+    ("unknown granularity accepted",
+     "if (g->gran[b] != ORC_TOKEN_ROWS && g->gran[b] != ORC_PAGE_BLOCKS) return ORC_ERR_INVALID;", ";"),
 ]
 
 
