@@ -100,6 +100,7 @@ _SIGS = {
     "hc_pool_mode": (ctypes.c_int, [_V, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]),
     "hc_pool_sync": (ctypes.c_int, [_V]),
     "hc_write_back_all_layers": (ctypes.c_int, [_V, _V, _V, ctypes.c_int64, _V]),
+    "hc_write_back_all_layers_noalloc": (ctypes.c_int, [_V, _V, _V, ctypes.c_int64, _V]),
     "hc_load_back_layer": (ctypes.c_int, [_V, ctypes.c_int32, _V, _V, ctypes.c_int64, _V]),
     "hc_round_trip_check": (ctypes.c_int, [_V, _V, _V, ctypes.c_int64, _I64P]),
     "hc_layer_pack_bytes": (ctypes.c_int, [_V, ctypes.c_int64, _I64P]),
@@ -416,6 +417,19 @@ class Pool:
             raise ValueError("host_idx and device_idx differ in length")
         check(lib.hc_write_back_all_layers(self.handle, _V(_ptr(device_idx)), _V(_ptr(host_idx)), n,
                                            event.handle if event else None), "hc_write_back_all_layers")
+        _in_use_on(self.stream, device_idx)
+
+    def write_back_all_layers_noalloc(self, device_idx, host_idx: "HostBuffer", n: int,
+                                      event: HipEvent | None = None) -> None:
+        """The write-back that allocates nothing (zero-copy pools): device_idx an int64 CUDA
+        tensor, host_idx a HostBuffer whose first n int64 entries are the host tokens."""
+        if _index_list(device_idx, "device_idx", True) != n:
+            raise ValueError("device_idx must hold n entries")
+        if not isinstance(host_idx, HostBuffer) or host_idx.nbytes < 8 * n:
+            raise TypeError("host_idx must be a HostBuffer of at least n int64 entries")
+        check(lib.hc_write_back_all_layers_noalloc(self.handle, _V(_ptr(device_idx)), _V(_ptr(host_idx)), n,
+                                                   event.handle if event else None),
+              "hc_write_back_all_layers_noalloc")
         _in_use_on(self.stream, device_idx)
 
     def load_back_layer(self, layer: int, host_idx, device_idx, event: HipEvent | None = None) -> None:

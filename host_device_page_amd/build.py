@@ -13,7 +13,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libhc.so")
-SOURCES = ["hc_api.cpp", "hc_layout.cpp", "hc_plan.cpp", "hc_loader.cpp", "hc_h2h.cpp", "hc_kernels.hip", "hc_exchange.hip"]
+SOURCES = ["hc_api.cpp", "hc_layout.cpp", "hc_plan.cpp", "hc_loader.cpp", "hc_h2h.cpp", "hc_kernels.hip", "hc_exchange.hip", "hc_noalloc.hip"]
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 HIPCC = os.environ.get("HIPCC", os.path.join(ROCM, "bin", "hipcc"))
 

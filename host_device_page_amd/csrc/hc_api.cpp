@@ -193,6 +193,19 @@ int check_extent(const void* q, int64_t bytes, bool required, const char* what) 
   return HC_OK;
 }
 
+// A list in pinned host memory, mapped at its host address, holding n int64 entries inside
+// its allocation: the CPU reads it and the copy engines copy it without staging.
+int check_pinned_list(const int64_t* q, int64_t n, const char* what) {
+  hipPointerAttribute_t attr;
+  if (hipPointerGetAttributes(&attr, q) != hipSuccess || attr.type != hipMemoryTypeHost) {
+    (void)hipGetLastError();
+    return set_err(HC_ERR_INVALID, "%s must be pinned host memory (hc_host_alloc or hipHostMalloc)", what);
+  }
+  if (attr.devicePointer != (const void*)q)
+    return set_err(HC_ERR_INVALID, "%s: pinned host memory not mapped at its host address", what);
+  return check_extent(q, n * (int64_t)sizeof(int64_t), true, what);
+}
+
 // The write-back's host list is read by the CPU: device memory would crash it.
 int check_host_list(const int64_t* q, const char* what) {
   hipPointerAttribute_t attr;
@@ -525,6 +538,14 @@ int hc_pool_create(const hc_pool_desc* desc, hc_pool** out) {
   if (hipGetDevice(&p->device) != hipSuccess) return bail(set_err(HC_ERR_HIP, "no HIP device"));
   if (hipDeviceGetAttribute(&p->num_cus, hipDeviceAttributeMultiprocessorCount, p->device) != hipSuccess)
     return bail(set_err(HC_ERR_HIP, "could not query the compute-unit count"));
+  {
+    // Set-up of the no-allocation write-back: the first lookup of its scratch on a device
+    // makes the runtime load the code object that holds the array (device memory, once per
+    // process and device), so that happens here and not inside that call.  A failure is
+    // reported by the no-allocation write-back itself.
+    int64_t* scratch = nullptr;
+    if (hc::noalloc_scratch(p->device, &scratch) != HC_OK) g_err.clear();
+  }
   p->stream = (hipStream_t)desc->copy_stream;
   if (p->stream) {
     hipDevice_t sd = -1;
@@ -773,6 +794,58 @@ int hc_write_back_all_layers(hc_pool* p, const int64_t* device_idx, const int64_
     Timer t(p, 3);
     e = hc::launch_zero_pads(p->host, d_pads, npads, L.stride, L.payload, L.stride - L.payload, t.ev, p->stream);
     t.done(e == hipSuccess);
+    if (e != hipSuccess) return finish(set_err(HC_ERR_HIP, "pad launch failed: %s", hipGetErrorString(e)));
+  }
+  p->stats.write_back_calls++;
+  p->stats.write_back_tokens += n;
+  p->stats.write_back_bytes += layer_bytes(p, n) * L.L;
+  return finish(HC_OK);
+}
+
+int hc_write_back_all_layers_noalloc(hc_pool* p, const int64_t* device_idx, const int64_t* host_idx, int64_t n,
+                                     void* event) {
+  if (!p) return set_err(HC_ERR_INVALID, "pool is null");
+  TraceRange range("hc_write_back_all_layers_noalloc");
+  std::lock_guard<std::recursive_mutex> lock(p->mu);
+  int rc = use_device(p);
+  if (rc != HC_OK) return rc;
+  auto finish = [&](int code) {
+    int r2 = record_event(event, p->stream);
+    return code != HC_OK ? code : r2;
+  };
+  if (p->lay.H == 0) return finish(no_host_pool());
+  if (p->wb_mode != HC_MODE_ZEROCOPY)
+    return finish(set_err(HC_ERR_UNSUPPORTED,
+                          "the write-back without allocation runs on zero-copy pools only (this pool stages its "
+                          "write-back)"));
+  if (stream_capturing(p))
+    return finish(refuse_capture("hc_write_back_all_layers_noalloc",
+                                 "it checks the host list on the CPU for each call"));
+  if (n < 0) return finish(set_err(HC_ERR_INVALID, "n must be >= 0"));
+  if (n == 0) return finish(HC_OK);
+  if (!device_idx || !host_idx) return finish(set_err(HC_ERR_INVALID, "null index list"));
+  if (n > HC_NOALLOC_MAX_TOKENS)
+    return finish(set_err(HC_ERR_INVALID, "n = %lld is above the %d tokens the write-back without allocation holds",
+                          (long long)n, HC_NOALLOC_MAX_TOKENS));
+  rc = check_device_list(p, device_idx, n, "device_idx");
+  if (rc == HC_OK) rc = check_pinned_list(host_idx, n, "host_idx");
+  if (rc != HC_OK) return finish(rc);
+  {
+    char msg[256];
+    rc = p->planner.validate(host_idx, n, msg, sizeof(msg));
+    if (rc != HC_OK) return finish(set_err(rc, "%s", msg));
+  }
+  int64_t* scratch = nullptr;
+  rc = hc::noalloc_scratch(p->device, &scratch);
+  if (rc != HC_OK) return finish(rc);
+  const Layout& L = p->lay;
+  hipError_t e = hipMemcpyAsync(scratch, host_idx, (size_t)n * sizeof(int64_t), hipMemcpyHostToDevice, p->stream);
+  if (e != hipSuccess) return finish(set_err(HC_ERR_HIP, "host list copy failed: %s", hipGetErrorString(e)));
+  e = hc::launch_zc_write(p->geom, device_idx, scratch, nullptr, n, p->host, p->d_err, p->max_ctas, hc::LaunchTimer{},
+                          p->stream);
+  if (e != hipSuccess) return finish(set_err(HC_ERR_HIP, "zero-copy launch failed: %s", hipGetErrorString(e)));
+  if (L.layout == HC_LAYOUT_KV_SPLIT_SHARD && L.stride > L.payload) {
+    e = hc::launch_zero_pads_runs(p->host, scratch, n, L.P, L.H, L.stride, L.payload, L.stride - L.payload, p->stream);
     if (e != hipSuccess) return finish(set_err(HC_ERR_HIP, "pad launch failed: %s", hipGetErrorString(e)));
   }
   p->stats.write_back_calls++;

@@ -107,6 +107,15 @@ int64_t exchange_plan(const Geom& g, int64_t n, int32_t num_cus, XPlan* x);
 hipError_t launch_layer_exchange(const Geom& g, bool pack, int32_t layer, const int64_t* dev_idx, int64_t n,
                                  uint8_t* staging, int32_t* err, int32_t num_cus, const LaunchTimer& t,
                                  hipStream_t stream);
+// Shard pads of the pages a host token list names, found from the list itself: the
+// position that starts each run of same-page entries zeroes [off, off + bytes) of its
+// page (a page named in two runs is zeroed twice).  Tokens outside [0, host_pages * P)
+// are skipped (the transfer kernel reports them).
+hipError_t launch_zero_pads_runs(uint8_t* base, const int64_t* host_idx, int64_t n, int32_t P, int64_t host_pages,
+                                 int64_t stride, int64_t off, int64_t bytes, hipStream_t stream);
+// Device address of the no-allocation write-back's scratch on `device` (which must be
+// current), HC_NOALLOC_MAX_TOKENS int64 entries; looked up once per device (hc_noalloc.hip).
+int noalloc_scratch(int device, int64_t** out);
 hipError_t launch_compare(const Geom& g, const int64_t* a, const int64_t* c, int64_t n,
                           unsigned long long* counter, int32_t* err, const LaunchTimer& t,
                           hipStream_t stream);

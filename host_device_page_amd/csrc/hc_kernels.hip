@@ -473,6 +473,29 @@ __global__ __launch_bounds__(kThreads) void k_zero_pads(uint8_t* __restrict__ ba
   }
 }
 
+// Shard pads from the token list itself (no page list): position k zeroes vector v of its
+// page's pad when it starts a run of same-page entries.  Used where no plan of distinct
+// pages is uploaded (the write-back that allocates nothing).
+__global__ __launch_bounds__(kThreads) void k_zero_pads_runs(uint8_t* __restrict__ base,
+                                                             const int64_t* __restrict__ host_idx, int64_t n,
+                                                             int32_t P, int64_t host_pages, int64_t stride,
+                                                             int64_t off, uint32_t vecs) {
+  const int64_t total = n * (int64_t)vecs;
+  const v4u z = {0u, 0u, 0u, 0u};
+  for (int64_t u = (int64_t)blockIdx.x * kThreads + threadIdx.x; u < total; u += (int64_t)gridDim.x * kThreads) {
+    const int64_t k = u / vecs;
+    const int64_t v = u - k * vecs;
+    const int64_t h = host_idx[k];
+    if (h < 0 || h / P >= host_pages) continue;
+    const int64_t p = h / P;
+    if (k > 0) {
+      const int64_t hp = host_idx[k - 1];
+      if (hp >= 0 && hp / P == p) continue;  // not the first entry of its run
+    }
+    st16((uint64_t)base + (uint64_t)(p * stride + off + v * 16), z);
+  }
+}
+
 // ---------------------------------------------------------------- round-trip compare
 // grid = (tiles, L, nsub).  Counts rows (or page blocks at a[i] % P == 0) whose bytes
 // at slot a[i] and slot c[i] differ.  One wave compares one row at a time; the row's
@@ -677,6 +700,17 @@ hipError_t launch_zero_pads(uint8_t* base, const int64_t* pages, int64_t npages,
   int64_t grid = ceil_div(total, kThreads);
   if (grid > 4096) grid = 4096;
   return launch(k_zero_pads, dim3((unsigned)grid), t, stream, base, pages, npages, stride, off, vecs);
+}
+
+hipError_t launch_zero_pads_runs(uint8_t* base, const int64_t* host_idx, int64_t n, int32_t P, int64_t host_pages,
+                                 int64_t stride, int64_t off, int64_t bytes, hipStream_t stream) {
+  if (n <= 0 || bytes <= 0) return hipSuccess;
+  const uint32_t vecs = (uint32_t)(bytes / 16);
+  const int64_t total = n * (int64_t)vecs;
+  int64_t grid = ceil_div(total, kThreads);
+  if (grid > 4096) grid = 4096;
+  return launch(k_zero_pads_runs, dim3((unsigned)grid), LaunchTimer{}, stream, base, host_idx, n, P, host_pages,
+                stride, off, vecs);
 }
 
 hipError_t launch_compare(const Geom& g, const int64_t* a, const int64_t* c, int64_t n, unsigned long long* counter,

@@ -250,6 +250,36 @@ int hc_pool_sync(hc_pool* pool);
 int hc_write_back_all_layers(hc_pool* pool, const int64_t* device_idx, const int64_t* host_idx,
                              int64_t n, void* event);
 
+/* Write-back that allocates nothing, for callers that cannot allocate device or
+ * pinned memory in the middle of their work (tight serving loops, harnesses that
+ * forbid hipMalloc): hc_write_back_all_layers grows its plan buffers with
+ * hipHostMalloc / hipMalloc when a burst is larger than any before it (waiting
+ * for the copy stream first); this variant never calls an allocator.  Its plan, a
+ * device copy of host_idx, lives in a fixed array of HC_NOALLOC_MAX_TOKENS int64
+ * entries (2 MiB) that every GPU the library runs on holds from the library's load
+ * until the process ends.  Every call on one GPU shares that GPU's array: calls
+ * that overlap on one GPU (pools on different streams) race on it; calls on one
+ * stream run in order.  The result is exactly hc_write_back_all_layers' on a
+ * zero-copy pool: the same rows move with the same kernel, and shard pads of the
+ * named pages become zero.
+ *   pool:       its write-back mode must resolve to zero-copy (HC_ERR_UNSUPPORTED
+ *               otherwise: the staged write-back plans copy-engine regions and a
+ *               staging layout per burst).
+ *   device_idx: n int64 in device memory (or pinned host memory), read on the GPU.
+ *   host_idx:   n int64 in pinned host memory mapped at its host address
+ *               (hc_host_alloc or hipHostMalloc), else HC_ERR_INVALID.  The CPU
+ *               checks it during the call (range, distinctness, whole pages with
+ *               page blocks) and the copy stream copies it into the array, so it
+ *               must not change until the copy stream has passed this call.
+ *   n:          0..HC_NOALLOC_MAX_TOKENS; larger is HC_ERR_INVALID, enqueueing
+ *               nothing.
+ *   event:      as for hc_write_back_all_layers (recorded on error too).
+ * Refused while the pool's stream is capturing, like hc_write_back_all_layers.
+ * Pools created with HC_FLAG_PROFILE do not time this call's kernels. */
+#define HC_NOALLOC_MAX_TOKENS 262144
+int hc_write_back_all_layers_noalloc(hc_pool* pool, const int64_t* device_idx, const int64_t* host_idx,
+                                     int64_t n, void* event);
+
 /* Load-back of one layer (host -> device):
  *   device[sub b][layer][slot d] <- host[sub b][page h/P][layer][row h%P]
  * for every pair (h = host_idx[i], d = device_idx[i]), i < n, every sub-buffer;

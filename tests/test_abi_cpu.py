@@ -95,6 +95,7 @@ def test_null_arguments_without_gpu():
     assert B.lib.hc_desc_check(None) == B.HC_ERR_INVALID
     assert B.lib.hc_pool_destroy(None) == B.HC_OK
     assert B.lib.hc_write_back_all_layers(None, None, None, 0, None) == B.HC_ERR_INVALID
+    assert B.lib.hc_write_back_all_layers_noalloc(None, None, None, 0, None) == B.HC_ERR_INVALID
     # a null pool with a null event: reported, nothing recorded
     assert B.lib.hc_load_back_layer(None, 0, None, None, 0, None) == B.HC_ERR_INVALID
     assert B.lib.hc_round_trip_check(None, None, None, 0, None) == B.HC_ERR_INVALID
