@@ -21,21 +21,19 @@ SHAPE = W.PoolShape("event_rows", 6, 16, ((T, 1024), (T, 1024)), 16384, 128)
 BLOCKS = W.PoolShape("event_blocks", 3, 16, ((T, 64), (BLK, 256)), 4096, 64)
 
 
-def expected_layer_sums(rig, h, layer):
-    host = rig.host.np
-    sums = []
-    for b, (gran, e) in enumerate(rig.shape.subs):
-        offs = O.host_offsets(rig.geom, b, layer, h)
-        rows = np.stack([host[o:o + e] for o in offs])
-        sums.append(int(rows.view(np.int32).astype(np.int64).sum()))
-    return sums
+def expected_layer_rows(rig, h, layer):
+    """The host rows of `layer` named by h, per sub-buffer (the oracle locates them)."""
+    return [np.stack([rig.host.np[o:o + e] for o in O.host_offsets(rig.geom, b, layer, h)])
+            for b, (gran, e) in enumerate(rig.shape.subs)]
 
 
-def consumer_sums(rig, layer, d_t):
-    out = []
-    for b, (gran, e) in enumerate(rig.shape.subs):
-        out.append(rig.dev[b][layer].view(-1, e)[d_t].view(torch.int32).to(torch.int64).sum())
-    return out
+def consumer_rows(rig, layer, d_t):
+    """The device rows of `layer` at d_t, copied on the current stream (the consumer's)."""
+    return [rig.dev[b][layer].view(-1, e)[d_t].clone() for b, (gran, e) in enumerate(rig.shape.subs)]
+
+
+def same_rows(got, want) -> bool:
+    return all(np.array_equal(g.cpu().numpy(), w) for g, w in zip(got, want))
 
 
 def prepare(rig, seed):
@@ -66,11 +64,11 @@ def test_consumer_waits_on_each_layer_event():
             rig.pool.load_back_layer(l, h_t, d2_t, events[l])
             events[l].wait_on(consumer)
             with torch.cuda.stream(consumer):
-                got.append(consumer_sums(rig, l, d2_t))
+                got.append(consumer_rows(rig, l, d2_t))
         consumer.synchronize()
         rig.pool.sync()
         for l in range(SHAPE.layers):
-            assert [int(x) for x in got[l]] == expected_layer_sums(rig, h, l), f"layer {l}"
+            assert same_rows(got[l], expected_layer_rows(rig, h, l)), f"layer {l}"
     finally:
         rig.close()
 
@@ -88,12 +86,12 @@ def test_negative_control_consumer_without_wait_sees_stale_rows():
             torch.cuda._sleep(50_000_000)  # bounded spin
         rig.pool.load_back_layer(0, h_t, d2_t, None)
         with torch.cuda.stream(consumer):
-            early = consumer_sums(rig, 0, d2_t)  # no wait: runs while the copy stream spins
+            early = consumer_rows(rig, 0, d2_t)  # no wait: runs while the copy stream spins
         consumer.synchronize()
         rig.pool.sync()
-        want = expected_layer_sums(rig, h, 0)
-        assert [int(x) for x in early] != want, "a consumer that skips the wait was not caught"
-        assert [int(x) for x in consumer_sums(rig, 0, d2_t)] == want
+        want = expected_layer_rows(rig, h, 0)
+        assert not same_rows(early, want), "a consumer that skips the wait was not caught"
+        assert same_rows(consumer_rows(rig, 0, d2_t), want)
     finally:
         rig.close()
 

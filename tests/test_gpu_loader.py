@@ -1,6 +1,7 @@
 """The asynchronous load-back enqueue with a real pool: a consumer stream waits on
-each layer through the loader's flags and events and checksums the layer; a failed
-burst releases its consumers; the next burst is served."""
+each layer through the loader's flags and events and copies the layer's loaded rows,
+which must equal the host rows element by element; a failed burst releases its
+consumers; the next burst is served."""
 import numpy as np
 import pytest
 import torch
@@ -14,18 +15,19 @@ T = W.TOKEN_ROWS
 SHAPE = W.PoolShape("loader_rows", 8, 16, ((T, 1024), (T, 512)), 16384, 128)
 
 
-def host_sums(rig, h, layer):
-    out = []
-    for b, (_, e) in enumerate(rig.shape.subs):
-        offs = O.host_offsets(rig.geom, b, layer, h)
-        rows = np.stack([rig.host.np[o:o + e] for o in offs])
-        out.append(int(rows.view(np.int32).astype(np.int64).sum()))
-    return out
-
-
-def dev_sums(rig, layer, d_t):
-    return [rig.dev[b][layer].view(-1, e)[d_t].view(torch.int32).to(torch.int64).sum()
+def host_rows(rig, h, layer):
+    """The host rows of `layer` named by h, per sub-buffer (the oracle locates them)."""
+    return [np.stack([rig.host.np[o:o + e] for o in O.host_offsets(rig.geom, b, layer, h)])
             for b, (_, e) in enumerate(rig.shape.subs)]
+
+
+def dev_rows(rig, layer, d_t):
+    """The device rows of `layer` at d_t, copied on the current stream (the consumer's)."""
+    return [rig.dev[b][layer].view(-1, e)[d_t].clone() for b, (_, e) in enumerate(rig.shape.subs)]
+
+
+def same_rows(got, want) -> bool:
+    return all(np.array_equal(g.cpu().numpy(), w) for g, w in zip(got, want))
 
 
 @pytest.mark.gpu
@@ -52,11 +54,11 @@ def test_loader_with_consumer_stream(asynchronous):
         for l in range(SHAPE.layers):
             burst.wait_layer(l, consumer)
             with torch.cuda.stream(consumer):
-                got.append(dev_sums(rig, l, d2_t))
+                got.append(dev_rows(rig, l, d2_t))
         consumer.synchronize()
         burst.wait()
         for l in range(SHAPE.layers):
-            assert [int(x) for x in got[l]] == host_sums(rig, h, l), f"layer {l}"
+            assert same_rows(got[l], host_rows(rig, h, l)), f"layer {l}"
         # a failing burst (null host list) still completes every layer event
         bad_events = [B.HipEvent() for _ in range(SHAPE.layers)]
         bad = loader.submit(None, d2_t, h.size, bad_events)
@@ -70,7 +72,7 @@ def test_loader_with_consumer_stream(asynchronous):
         good.wait()
         rig.pool.sync()
         for l in range(SHAPE.layers):
-            assert [int(x) for x in dev_sums(rig, l, d2_t)] == host_sums(rig, h, l)
+            assert same_rows(dev_rows(rig, l, d2_t), host_rows(rig, h, l))
     finally:
         if loader is not None:
             loader.close()
@@ -152,12 +154,12 @@ def test_loader_replays_a_captured_burst(asynchronous):
             for l in range(SHAPE.layers):
                 burst.wait_layer(l, consumer)
                 with torch.cuda.stream(consumer):
-                    got.append(dev_sums(rig, l, d_buf))
+                    got.append(dev_rows(rig, l, d_buf))
             consumer.synchronize()
             burst.wait()
             burst.release()
             for l in range(SHAPE.layers):
-                assert [int(x) for x in got[l]] == host_sums(rig, h, l), f"replay {r} layer {l}"
+                assert same_rows(got[l], host_rows(rig, h, l)), f"replay {r} layer {l}"
             # an eager burst between replays, on other events
             other = [B.HipEvent() for _ in range(SHAPE.layers)]
             eager = loader.submit(h_t, cuda_i64(d2), h.size, other)
@@ -259,7 +261,7 @@ def test_start_event_orders_the_producers_index_list_before_the_burst():
             burst.wait()
             burst.release()
             torch.cuda.synchronize()
-            at_real = all([int(x) for x in dev_sums(rig, l, real_t)] == host_sums(rig, h, l) for l in range(L))
+            at_real = all(same_rows(dev_rows(rig, l, real_t), host_rows(rig, h, l)) for l in range(L))
             if use_start:
                 assert at_real, "the burst did not wait for the producer's start event"
             else:
