@@ -2,19 +2,24 @@
 
 A step is one write-back burst of every layer (device -> pinned host pool) and
 one per-layer load-back burst of the same host pages into fresh device slots,
-each layer recording its layer-done event.  The workload is the Llama-3-8B MHA
-pool (32 layers, 8 KV heads x 128 dims bf16, 64-token pages, 262144 device
-slots, 8192 host pages) with bursts of 256 pages (16384 tokens) whose device
-slots come from a free list with half the segments contiguous runs of 1-64.
+each layer recording its layer-done event.  The headline workload is the largest
+configuration by bytes moved: the MHA pool in the K page | V page | pad shard
+layout (48 layers, 8 KV heads x 128 dims bf16, 32-token pages, 262144 device
+slots, 4096 host shards), bursts naming 2048 shards (~58k tokens, 11.4 GB each
+way) in requests whose last page is partial, onto scattered device slots.  The
+same line carries a second measured block for the 78-layer MLA + DSA indexer
+pool (two host pools loaded in one burst of 1024 pages, a consumer kernel on a
+second stream waiting on each layer-done event).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 
 Prints one JSON line: whole-step host-link throughput (GB/s, both directions'
 bytes over the step time), per-direction rates, the host-link roofline of the
 dominant kernel (HIP-event timing on the copy stream against the hipMemcpyAsync
-peak measured here), the HBM roofline of the staged relayout kernel and of the
-layer exchange kernels of a rank-sharded tier, and the CPU oracle timed on a
-bounded sample.
+peak measured here), the HBM roofline of the staged relayout kernel (as the path
+runs it, staging chunks resident in the Infinity Cache, and with nothing of the
+launch in that cache) and of the layer exchange kernels of a rank-sharded tier,
+and the CPU oracle timed on a bounded sample.
 """
 from __future__ import annotations
 
@@ -43,7 +48,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", default="llama3_8b_mha_bf16")
+    ap.add_argument("--workload", default="mha_kv_split_shard_bf16")
+    ap.add_argument("--second-workload", default="dsa_mla_indexer_78l",
+                    help="a second workload measured in the same line (write-back + per-layer load-back with a "
+                         "consumer per layer, host-link roofline); empty to skip")
     ap.add_argument("--write-back-mode", choices=["auto", "zerocopy", "staged"], default="zerocopy",
                     help="mode of the timed write-back (zero-copy: the highest burst rate; the staged mode, "
                          "which leaves concurrent compute alone, is measured beside it)")
@@ -72,6 +80,9 @@ def parse():
     ap.add_argument("--gather-patterns", action="store_true",
                     help="instead: the staged gather's rate on the workload's burst with sequential, free-list, "
                          "page-aligned and random device slots")
+    ap.add_argument("--gather-dram", action="store_true",
+                    help="instead: only the staged gather with nothing of its launch in the Infinity Cache "
+                         "(one chunk per call, each after a 1 GiB write on the copy stream)")
     ap.add_argument("--h2h", action="store_true",
                     help="instead: time host-to-host shard dump/load of the shard workload with 1..16 CPU workers")
     ap.add_argument("--max-pinned-gib", type=float, default=64.0,
@@ -83,6 +94,16 @@ def parse():
                          "reference for the FETCH_SIZE / WRITE_SIZE counters)")
     return ap.parse_args()
 
+
+# How each workload draws the device slots of its burst (workloads.burst_for).
+SLOT_DRAWS = {
+    "llama3_8b_mha_bf16": "free list, 50% runs of 1-64",
+    "llama3_8b_mha_bf16_token_major": "free list, 50% runs of 1-64",
+    "dsv3_mla_bf16": "free list, 50% runs of 1-64",
+    "dsa_mla_indexer_78l": "whole page-aligned device pages, random",
+    "mha_kv_split_shard_bf16": "random, no two list neighbours in adjacent slots; requests of 1-8 pages whose "
+                               "last page holds 1..P-1 rows",
+}
 
 # The library caps a staging chunk at this many bytes of page images (MI355X's Infinity Cache).
 STAGING_CHUNK_BYTES = 256 << 20
@@ -163,7 +184,7 @@ def parse_pairs(text: str):
     return tuple(out)
 
 
-def gather_patterns(B, torch, np, W, make_pool, shape, burst, h_np, link_bytes, reps=5, rounds=2):
+def gather_patterns(B, torch, np, W, make_pool, shape, burst, h_np, gather_bytes, reps=5, rounds=2):
     """k_gather_stage rate (read + write bytes over its launch time) on the burst's host tokens
     with four device-slot patterns: one sequential run, the workload's free-list draw, whole
     device pages, and a random permutation.  Rounds interleave the patterns."""
@@ -187,7 +208,7 @@ def gather_patterns(B, torch, np, W, make_pool, shape, burst, h_np, link_bytes, 
                 spool.write_back_all_layers(d_t, h_np)
             spool.sync()
             ng, ms = spool.kernel_time(B.KIND_GATHER)
-            out[name].append(round(2 * link_bytes * reps / (ms * 1e-3) / 1e12, 3))
+            out[name].append(round(2 * gather_bytes * reps / (ms * 1e-3) / 1e12, 3))
             log(f"[bench] gather {name}: {out[name][-1]} TB/s")
     spool.close()
     return {k: {"TBps": v} for k, v in out.items()}
@@ -288,6 +309,15 @@ def duplex_measurement(B, torch, np, hip, make_pool, shape, burst, d_t, h_np, d2
     if duplex["rows"]:
         best = max(duplex["rows"], key=lambda r: r["aggregate_GBps"])
         duplex["best_frac_of_duplex_peak"] = round(best["aggregate_GBps"] / duplex["roofline"]["aggregate_GBps"], 4)
+        preset = [r for r in duplex["rows"]
+                  if r["write_back"] == "staged" and r["load_back_workgroups"] == B.HC_DUPLEX_LOAD_BACK_CTAS]
+        if preset:
+            duplex["preset"] = {"what": "Pool.duplex_partner: a staged write-back pool beside a zero-copy load-back "
+                                        f"pool capped at HC_DUPLEX_LOAD_BACK_CTAS = {B.HC_DUPLEX_LOAD_BACK_CTAS} "
+                                        "workgroups",
+                                "aggregate_GBps": preset[0]["aggregate_GBps"],
+                                "frac_of_duplex_peak": round(preset[0]["aggregate_GBps"]
+                                                             / duplex["roofline"]["aggregate_GBps"], 4)}
     log(f"[bench] duplex copy-engine peak {duplex['roofline']}")
     return duplex
 
@@ -334,6 +364,59 @@ def burst_bytes(shape, burst) -> tuple[int, int]:
     n = burst.n
     whole_pages = int((burst.host_idx % P == 0).sum())
     return L * (n * rows + whole_pages * blocks), 0
+
+
+def staged_bytes(shape, burst) -> int:
+    """Bytes one burst moves through the staged gather: the rows (and page blocks) of every
+    wholly named host page, over all layers.  Rows of pages the burst names in part go
+    through the zero-copy kernel instead (rows it does not name must stay as they are),
+    so they are not the gather's."""
+    import numpy as np
+    P, L = shape.page_size, shape.layers
+    _, counts = np.unique(burst.host_idx // P, return_counts=True)
+    whole = int((counts == P).sum())
+    rows = sum(e for g, e in shape.subs if g == 0)
+    blocks = sum(e for g, e in shape.subs if g == 1)
+    return L * whole * (P * rows + blocks)
+
+
+def gather_dram_bound(B, torch, np, W, make_pool, stream, shape, burst, chunk_pages, reps=5):
+    """k_gather_stage with nothing of its launch in MI355X's 256 MB Infinity Cache.  Each
+    write-back call names exactly one staging chunk of wholly named pages (the burst's
+    first ones), and each follows a 1 GiB write on the copy stream, which leaves the cache
+    full of other dirty lines: the gather reads its rows from DRAM, and its staging writes
+    displace dirty lines that go to DRAM.  The same chunk without the write, back to back,
+    is timed beside it.  Bytes per launch: the chunk's rows read plus the same written."""
+    P = shape.page_size
+    pg = burst.host_idx // P
+    uniq, counts = np.unique(pg, return_counts=True)
+    whole = set(uniq[counts == P].tolist())
+    pick = [int(p) for p in burst.pages if int(p) in whole][:chunk_pages]
+    mask = np.isin(pg, pick)
+    d = np.ascontiguousarray(burst.device_idx[mask])
+    h = np.ascontiguousarray(burst.host_idx[mask])
+    nbytes = staged_bytes(shape, W.Burst(d, h, np.array(pick, dtype=np.int64)))
+    d_t = torch.from_numpy(d).cuda()
+    spool = make_pool(B.HC_MODE_STAGED)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    spool.write_back_all_layers(d_t, h)
+    spool.sync()
+    res = {}
+    for name, flushed in (("dram", True), ("back_to_back", False)):
+        spool.kernel_time(0, reset=True)
+        for k in range(reps):
+            if flushed:
+                with torch.cuda.stream(stream):
+                    flush.fill_(k & 0xFF)
+            spool.write_back_all_layers(d_t, h)
+        spool.sync()
+        n_g, ms_g = spool.kernel_time(B.KIND_GATHER)
+        assert n_g == reps, f"expected one gather launch per call, got {n_g} for {reps}"
+        res[name] = {"avg_launch_ms": round(ms_g / n_g, 4),
+                     "achieved": round(2 * nbytes / (ms_g / n_g * 1e-3) / 1e9, 1)}
+    spool.close()
+    del flush
+    return {"chunk_pages": len(pick), "bytes_per_launch": 2 * nbytes, "flush_bytes": 1 << 30, **res}
 
 
 def _cpu_model() -> str:
@@ -626,6 +709,15 @@ def layer_exchange_timing(B, np, shape, dev, d_t, n, stream, counter_workload=No
             xpool.layer_unpack(l, staging[l], d_t)
     n_p, ms_p = xpool.kernel_time(B.KIND_PACK)
     n_u, ms_u = xpool.kernel_time(B.KIND_UNPACK)
+    # As the path runs it: the owner's pack is read right away (by the broadcast; here by the
+    # unpack), so each layer is packed into one staging buffer and unpacked from it at once.
+    xpool.kernel_time(B.KIND_PACK, reset=True)
+    for _ in range(rounds):
+        for l in range(L):
+            xpool.layer_pack(l, d_t, staging[0])
+            xpool.layer_unpack(l, staging[0], d_t)
+    n_wp, ms_wp = xpool.kernel_time(B.KIND_PACK)
+    n_wu, ms_wu = xpool.kernel_time(B.KIND_UNPACK)
     xpool.sync()
     xpool.close()
     # the same bytes through a plain copy, source and destination as cold as the kernels'
@@ -652,6 +744,16 @@ def layer_exchange_timing(B, np, shape, dev, d_t, n, stream, counter_workload=No
         out[name] = {"bound": "hbm", "kernel": kname, "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "avg_launch_ms": round(avg, 5),
                      "bytes_per_launch": 2 * packed, "traffic": traffic["bytes"] if traffic else None}
+    out["cold"] = "each layer packed into its own staging buffer, then each unpacked (rows and staging cold)"
+    pair_ms = ms_wp / max(1, n_wp) + ms_wu / max(1, n_wu)
+    out["warm_pair"] = {
+        "what": "pack then unpack of each layer on one staging buffer, back to back (the packed layer is read "
+                "right after it is written)",
+        "pack_avg_launch_ms": round(ms_wp / max(1, n_wp), 5), "unpack_avg_launch_ms": round(ms_wu / max(1, n_wu), 5),
+        "pack_GBps": round(2 * packed / (ms_wp / max(1, n_wp) * 1e-3) / 1e9, 1),
+        "unpack_GBps": round(2 * packed / (ms_wu / max(1, n_wu) * 1e-3) / 1e9, 1),
+        "pair_GBps": round(4 * packed / (pair_ms * 1e-3) / 1e9, 1),
+        "pair_frac": round(4 * packed / (pair_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     return out
 
 
@@ -747,30 +849,205 @@ def burst_size_sweep(B, np, pool, shape, stream, burst, d_t, h_np, h_t, d2_t, ar
     return rows
 
 
-def main():
-    args = parse()
-    if args.h2h:
-        return h2h_main(args)
-    if args.gpus != 1:
-        print(json.dumps({"error": "this path runs on one GPU; --gpus above 1 is not supported. The multi-GPU "
-                                   "design (layer-owner sharding with a per-layer broadcast) is described, "
-                                   "not built."}), flush=True)
-        sys.exit(2)
+def staged_probe(B, torch, np, W, make_pool, stream, shape, burst, d_t, h_np, link_bytes, reps, chunk_pages):
+    """The same burst through the staged write-back: the HBM roofline of k_gather_stage as the
+    path runs it (chunks of page images capped to stay in the Infinity Cache until the copy
+    engines read them), the same kernel with nothing of its launch in that cache, and the
+    staged burst's rate."""
+    spool = make_pool(B.HC_MODE_STAGED)
+    for _ in range(2):
+        spool.write_back_all_layers(d_t, h_np)
+    spool.sync()
+    spool.kernel_time(0, reset=True)
+    e0, e1 = B.HipEvent(timing=True), B.HipEvent(timing=True)
+    sms = []
+    for _ in range(reps):
+        e0.record(stream)
+        spool.write_back_all_layers(d_t, h_np)
+        e1.record(stream)
+        e1.synchronize()
+        sms.append(e0.elapsed_ms(e1))
+    n_g, ms_g = spool.kernel_time(B.KIND_GATHER)
+    n_c, ms_c = spool.kernel_time(B.KIND_COPY_ENGINE)
+    spool.sync()
+    spool.close()
+    gbytes = staged_bytes(shape, burst)           # what the gather moves: wholly named pages
+    chunks = n_g // reps
+    g_gbs = 2 * gbytes * reps / (ms_g * 1e-3) / 1e9  # read + write of every gathered byte
+    gtraffic = counter_traffic(shape.name, "k_gather_stage")
+    dram = gather_dram_bound(B, torch, np, W, make_pool, stream, shape, burst, chunk_pages)
+    d_gbs = dram["dram"]["achieved"]
+    roofline_hbm = {"bound": "hbm", "kernel": "k_gather_stage (staged lf->pf relayout, one chunk, all layers)",
+                    "achieved": round(g_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(g_gbs / HBM_PEAK_GBS, 4),
+                    "traffic": gtraffic["bytes"] if gtraffic else None,
+                    "avg_launch_ms": round(ms_g / n_g, 4), "bytes_per_launch": int(2 * gbytes / max(1, chunks)),
+                    "chunk_pages": chunk_pages, "gathered_bytes_per_burst": gbytes,
+                    "staging": "as the path runs: chunks capped at 256 MB so the copy engines read the page images "
+                               "the gather just wrote from the Infinity Cache; part of the write side stays in that "
+                               "cache, so this rate is an upper bound for DRAM alone",
+                    "dram_bound": {"achieved": d_gbs, "frac": round(d_gbs / HBM_PEAK_GBS, 4),
+                                   "avg_launch_ms": dram["dram"]["avg_launch_ms"],
+                                   "bytes_per_launch": dram["bytes_per_launch"], "chunk_pages": dram["chunk_pages"],
+                                   "back_to_back_achieved": dram["back_to_back"]["achieved"],
+                                   "method": "one chunk of wholly named pages per call, each call after a 1 GiB "
+                                             "write on the copy stream (rows read from DRAM, staging writes "
+                                             "displace dirty lines)"},
+                    "meets_70pct_of_peak": {"as_run": g_gbs >= 0.7 * HBM_PEAK_GBS,
+                                            "dram_bound": d_gbs >= 0.7 * HBM_PEAK_GBS}}
+    staged = {"write_back_GBps": round(link_bytes / (float(np.median(sms)) * 1e-3) / 1e9, 3),
+              "copy_engine_ms_per_burst": round(ms_c / reps, 3),
+              "gather_ms_per_burst": round(ms_g / reps, 3)}
+    log(f"[bench] gather {g_gbs:.1f} GB/s as run, {d_gbs} GB/s with nothing in the Infinity Cache")
+    return roofline_hbm, staged
+
+
+def second_block(args, name: str, peaks: dict) -> dict:
+    """A second workload in the same line: K timed steps of write-back (zero-copy) + per-layer
+    load-back, where a consumer stream waits on each layer-done event and runs a small kernel
+    that reads the loaded layer (the dummy attention of the 78-layer two-pool burst); the
+    host-link roofline of its dominant kernel against the peaks measured for the headline; and
+    the staged gather's HBM rates."""
+    import numpy as np
+    import torch
+
+    from host_device_page_amd import binding as B
+    from host_device_page_amd import workloads as W
+    shape = capped_shape(B, W, name, args.max_pinned_gib)
+    L, P = shape.layers, shape.page_size
+    log(f"[bench] second workload {shape.name}: L={L} P={P} subs={shape.subs} S={shape.device_slots} "
+        f"H={shape.host_pages}")
+    t_setup = time.perf_counter()
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(3)
+    dev = []
+    for g, e in shape.subs:
+        units = shape.device_slots // P if g == 1 else shape.device_slots
+        dev.append(torch.empty((L, units * e), dtype=torch.uint8, device="cuda").random_(0, 256, generator=gen))
+    probe, _k = B.make_desc(layers=L, page_size=P, subs=[(g, e, [1] * L) for g, e in shape.subs],
+                            device_slots=shape.device_slots, host_pages=shape.host_pages, layout=shape.layout,
+                            shard_align=shape.align)
+    host = B.HostBuffer(B.host_pool_bytes(probe))
+    img = B.staging_page_bytes(probe)
+    chunk_pages = max(1, STAGING_CHUNK_BYTES // img)
+    staging = torch.empty(chunk_pages * img, dtype=torch.uint8, device="cuda")
+    stream, consumer = torch.cuda.Stream(), torch.cuda.Stream()
+    layers = [[t[l] for l in range(L)] for t in dev]
+
+    def make_pool(mode, max_ctas=None, flags=B.HC_FLAG_PROFILE, stream_=None):
+        return B.Pool(layers=L, page_size=P, subs=list(shape.subs), device_slots=shape.device_slots,
+                      host_pages=shape.host_pages, device_layers=layers, host=host,
+                      stream=stream if stream_ is None else stream_, layout=shape.layout, shard_align=shape.align,
+                      staging=staging, write_back_mode=mode, flags=flags,
+                      max_ctas=args.max_ctas if max_ctas is None else max_ctas)
+
+    pool = make_pool(B.HC_MODE_ZEROCOPY)
+    burst = W.burst_for(shape, seed=1)
+    d2 = W.fresh_slots_like(shape, burst, seed=2)
+    d_t = torch.from_numpy(burst.device_idx).cuda()
+    h_np = np.ascontiguousarray(burst.host_idx)
+    h_t = torch.from_numpy(h_np).cuda()
+    d2_t = torch.from_numpy(d2).cuda()
+    link_bytes, _ = burst_bytes(shape, burst)
+    seen = torch.zeros((L, 16), dtype=torch.uint8, device="cuda")
+    layer_events = [B.HipEvent() for _ in range(L)]
+    ev_wb0, ev_wb1, ev_lb1, ev_c = (B.HipEvent(timing=True) for _ in range(4))
+    torch.cuda.synchronize()
+    log(f"[bench] setup {time.perf_counter() - t_setup:.1f} s; burst {burst.n} tokens, {burst.pages.size} pages")
+
+    def step():
+        ev_wb0.record(stream)
+        pool.write_back_all_layers(d_t, h_np)
+        ev_wb1.record(stream)
+        for l in range(L):
+            pool.load_back_layer(l, h_t, d2_t, layer_events[l])
+            layer_events[l].wait_on(consumer)
+            with torch.cuda.stream(consumer):
+                seen[l].copy_(dev[0][l][:16])  # reads the layer once its event has completed
+        ev_lb1.record(stream)
+        ev_c.record(consumer)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    pool.kernel_time(0, reset=True)
+    wb_ms, lb_ms, c_ms = [], [], []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+        ev_c.synchronize()
+        ev_lb1.synchronize()
+        wb_ms.append(ev_wb0.elapsed_ms(ev_wb1))
+        lb_ms.append(ev_wb1.elapsed_ms(ev_lb1))
+        c_ms.append(ev_wb1.elapsed_ms(ev_c))
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    n_rd, ms_rd = pool.kernel_time(B.KIND_ZC_READ)
+    n_wr, ms_wr = pool.kernel_time(B.KIND_ZC_WRITE)
+    pool.sync()
+    pool.close()
+    wb_gbs = link_bytes / (float(np.median(wb_ms)) * 1e-3) / 1e9
+    lb_gbs = link_bytes / (float(np.median(lb_ms)) * 1e-3) / 1e9
+    per_layer = link_bytes // L
+    if n_wr and ms_wr > ms_rd:
+        kname, avg, nbytes, peak = "k_zc_write", ms_wr / n_wr, link_bytes, peaks["d2h"]
+    else:
+        kname, avg, nbytes, peak = "k_zc_read", ms_rd / max(1, n_rd), per_layer, peaks["h2d"]
+    achieved = nbytes / (avg * 1e-3) / 1e9
+    traffic = counter_traffic(shape.name, kname)
+    roofline = {"bound": "host_link", "kernel": kname, "achieved": round(achieved, 3), "peak": round(peak, 3),
+                "unit": "GB/s", "frac": round(achieved / peak, 4), "traffic": traffic["bytes"] if traffic else None,
+                "avg_launch_ms": round(avg, 4), "bytes_per_launch": nbytes,
+                "launches": n_rd if kname == "k_zc_read" else n_wr,
+                "peak_source": "hipMemcpyAsync pinned<->device 1 GiB best of 5, measured for the headline workload",
+                "frac_of_published": round(achieved / PCIE5_X16_GBS, 4)}
+    roofline_hbm, staged = staged_probe(B, torch, np, W, make_pool, stream, shape, burst, d_t, h_np, link_bytes,
+                                        max(3, args.steps // 2), chunk_pages)
+    host.free()
+    del dev, staging, layers
+    return {"workload": shape.name, "layers": L, "page_size": P, "row_bytes": list(shape.row_bytes),
+            "device_slots": shape.device_slots, "host_pages": shape.host_pages,
+            "burst_pages": int(burst.pages.size), "burst_tokens": burst.n, "burst_bytes_each_way": link_bytes,
+            "steps": args.steps, "warmup": args.warmup,
+            "value": round(2 * link_bytes * args.steps / el / 1e9, 3), "unit": "GB/s",
+            "ms_per_step": round(el * 1e3 / args.steps, 3),
+            "write_back_GBps": round(wb_gbs, 3), "load_back_GBps": round(lb_gbs, 3),
+            "frac_of_link_peak": {"write_back": round(wb_gbs / peaks["d2h"], 4),
+                                  "load_back": round(lb_gbs / peaks["h2d"], 4)},
+            "load_back_with_consumer": {
+                "consumer": "after hipStreamWaitEvent(layer event) on a second stream, a 16-byte copy out of the "
+                            "loaded layer, per layer",
+                "consumer_done_after_load_back_ms": round(float(np.median(c_ms)) - float(np.median(lb_ms)), 4),
+                "GBps_to_last_consumer": round(link_bytes / (float(np.median(c_ms)) * 1e-3) / 1e9, 3)},
+            "pages_per_s": round(2 * burst.pages.size * args.steps / el, 1),
+            "roofline": roofline, "roofline_hbm": roofline_hbm, "staged_write_back": staged}
+
+
+def capped_shape(B, W, name: str, max_pinned_gib: float):
+    """The workload's pool shape with as many host pages as the pinned-memory cap holds."""
+    shape = W.SHAPES[name]
+    L, P = shape.layers, shape.page_size
+    one, _k1 = B.make_desc(layers=L, page_size=P, subs=[(g, e, [1] * L) for g, e in shape.subs],
+                           device_slots=shape.device_slots, host_pages=1, layout=shape.layout, shard_align=shape.align)
+    cap_pages = int(max_pinned_gib * (1 << 30)) // B.host_pool_bytes(one)
+    if cap_pages < shape.host_pages:
+        log(f"[bench] host pool capped at {cap_pages} of {shape.host_pages} pages ({max_pinned_gib} GiB pinned)")
+        shape = W.shape_scaled(shape, shape.name, host_pages=cap_pages)
+    return shape
+
+
+def measure(args):
+    """Every measurement of the headline workload; the result dict, or None for the modes that
+    print their own line."""
     import numpy as np
     import torch
 
     from host_device_page_amd import binding as B
     from host_device_page_amd import workloads as W
 
-    torch.cuda.set_device(0)
     shape = W.SHAPES[args.workload]
     L, P = shape.layers, shape.page_size
-    one, _k1 = B.make_desc(layers=L, page_size=P, subs=[(g, e, [1] * L) for g, e in shape.subs],
-                           device_slots=shape.device_slots, host_pages=1, layout=shape.layout, shard_align=shape.align)
-    cap_pages = int(args.max_pinned_gib * (1 << 30)) // B.host_pool_bytes(one)
-    if cap_pages < shape.host_pages:
-        log(f"[bench] host pool capped at {cap_pages} of {shape.host_pages} pages ({args.max_pinned_gib} GiB pinned)")
-        shape = W.shape_scaled(shape, shape.name, host_pages=cap_pages)
+    shape = capped_shape(B, W, args.workload, args.max_pinned_gib)
     log(f"[bench] workload {shape.name}: L={L} P={P} subs={shape.subs} S={shape.device_slots} H={shape.host_pages}")
     t_setup = time.perf_counter()
     gen = torch.Generator(device="cuda")
@@ -791,7 +1068,7 @@ def main():
         res = layer_exchange_timing(B, np, shape, dev, d2_t, burst.n, stream, counter_workload=shape.name)
         log(f"[bench] layer exchange {res}")
         print(json.dumps({"layer_exchange": res, "workload": shape.name}), flush=True)
-        return
+        return None
     probe, _k = B.make_desc(layers=L, page_size=P, subs=[(g, e, [1] * L) for g, e in shape.subs],
                             device_slots=shape.device_slots, host_pages=shape.host_pages, layout=shape.layout,
                             shard_align=shape.align)
@@ -833,7 +1110,7 @@ def main():
         print(json.dumps({"beside_compute": res, "workload": shape.name,
                           "burst_bytes_each_way": burst_bytes(shape, burst)[0]}), flush=True)
         host.free()
-        return
+        return None
     if args.sweep:
         # no per-launch timing events here: at small bursts their cost (~9 us per launch) would dominate
         pool.close()
@@ -843,16 +1120,23 @@ def main():
                           "max_ctas": args.max_ctas or DEFAULT_MAX_CTAS, "rows": rows}), flush=True)
         pool.close()
         host.free()
-        return
+        return None
 
     link_bytes, _ = burst_bytes(shape, burst)
     if args.gather_patterns:
         pool.close()
-        rows = gather_patterns(B, torch, np, W, make_pool, shape, burst, h_np, link_bytes)
+        rows = gather_patterns(B, torch, np, W, make_pool, shape, burst, h_np, staged_bytes(shape, burst))
         print(json.dumps({"gather_patterns": rows, "workload": shape.name, "chunk_pages": args.staging_pages}),
               flush=True)
         host.free()
-        return
+        return None
+    if args.gather_dram:
+        pool.close()
+        res = gather_dram_bound(B, torch, np, W, make_pool, stream, shape, burst, args.staging_pages)
+        log(f"[bench] gather with nothing in the Infinity Cache: {res}")
+        print(json.dumps({"gather_dram_bound": res, "workload": shape.name}), flush=True)
+        host.free()
+        return None
     if args.duplex_only:
         pool.close()
         hip = hip_setup(B)
@@ -863,7 +1147,7 @@ def main():
         del scratch
         print(json.dumps({"duplex": res, "workload": shape.name, "burst_bytes_each_way": link_bytes}), flush=True)
         host.free()
-        return
+        return None
     ev_wb0, ev_wb1, ev_lb1 = B.HipEvent(timing=True), B.HipEvent(timing=True), B.HipEvent(timing=True)
     layer_events = [B.HipEvent() for _ in range(L)]
     enqueue_s = []
@@ -1001,43 +1285,14 @@ def main():
     roofline_hbm = None
     staged = None
     if not args.no_staged_probe:
-        spool = make_pool(B.HC_MODE_STAGED)
-        for _ in range(2):
-            spool.write_back_all_layers(d_t, h_np)
-        spool.sync()
-        spool.kernel_time(0, reset=True)
-        e0, e1 = B.HipEvent(timing=True), B.HipEvent(timing=True)
-        reps = max(3, args.steps // 2)
-        sms = []
-        for _ in range(reps):
-            e0.record(stream)
-            spool.write_back_all_layers(d_t, h_np)
-            e1.record(stream)
-            e1.synchronize()
-            sms.append(e0.elapsed_ms(e1))
-        n_g, ms_g = spool.kernel_time(B.KIND_GATHER)
-        n_c, ms_c = spool.kernel_time(B.KIND_COPY_ENGINE)
-        spool.sync()
-        chunks = n_g // reps
-        gather_bytes = 2 * link_bytes / max(1, chunks)  # read + write per launch (one chunk)
-        g_gbs = gather_bytes * n_g / (ms_g * 1e-3) / 1e9
-        gtraffic = counter_traffic(shape.name, "k_gather_stage")
-        roofline_hbm = {"bound": "hbm", "kernel": "k_gather_stage (staged lf->pf relayout, one chunk, all layers)",
-                        "achieved": round(g_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                        "frac": round(g_gbs / HBM_PEAK_GBS, 4),
-                        "traffic": gtraffic["bytes"] if gtraffic else None,
-                        "avg_launch_ms": round(ms_g / n_g, 4), "bytes_per_launch": int(gather_bytes),
-                        "chunk_pages": args.staging_pages}
-        staged = {"write_back_GBps": round(link_bytes / (float(np.median(sms)) * 1e-3) / 1e9, 3),
-                  "copy_engine_ms_per_burst": round(ms_c / reps, 3),
-                  "gather_ms_per_burst": round(ms_g / reps, 3)}
-        spool.close()
+        roofline_hbm, staged = staged_probe(B, torch, np, W, make_pool, stream, shape, burst, d_t, h_np, link_bytes,
+                                            max(3, args.steps // 2), args.staging_pages)
         # both write-back modes beside independent compute, on pools without timing events
         ov_pools = {"zerocopy": make_pool(B.HC_MODE_ZEROCOPY, flags=0), "staged": make_pool(B.HC_MODE_STAGED, flags=0)}
         staged["beside_compute"] = write_back_overlap(B, torch, np, ov_pools, d_t, h_np)
         for p in ov_pools.values():
             p.close()
-        log(f"[bench] staged write-back {staged}, gather {g_gbs:.1f} GB/s")
+        log(f"[bench] staged write-back {staged}")
 
     cpu = cpu_mt = None
     if not args.no_cpu_baseline:
@@ -1060,7 +1315,7 @@ def main():
         "config": {"workload": shape.name, "layers": L, "page_size": P, "row_bytes": list(shape.row_bytes),
                    "device_slots": shape.device_slots, "host_pages": shape.host_pages,
                    "burst_pages": int(pages), "burst_tokens": burst.n,
-                   "burst_bytes_each_way": link_bytes, "slots": "free list, 50% runs of 1-64",
+                   "burst_bytes_each_way": link_bytes, "slots": SLOT_DRAWS.get(shape.name, "seeded random"),
                    "write_back_mode": "staged" if wb_mode == B.HC_MODE_STAGED else "zerocopy",
                    "load_back_mode": "zerocopy"},
         "write_back_GBps": round(wb_gbs, 3), "load_back_GBps": round(lb_gbs, 3),
@@ -1082,6 +1337,32 @@ def main():
         "cpu_baseline_threads": cpu_mt,
     }
     host.free()
+    out["_peaks"] = {"h2d": peak_h2d, "d2h": peak_d2h}
+    return out
+
+
+def main():
+    args = parse()
+    if args.h2h:
+        return h2h_main(args)
+    if args.gpus != 1:
+        print(json.dumps({"error": "this path runs on one GPU; --gpus above 1 is not supported. The multi-GPU "
+                                   "design (layer-owner sharding with a per-layer broadcast) is described, "
+                                   "not built."}), flush=True)
+        sys.exit(2)
+    import torch
+
+    torch.cuda.set_device(0)
+    out = measure(args)
+    if out is None:
+        return
+    peaks = out.pop("_peaks")
+    if args.second_workload and args.second_workload != args.workload:
+        import gc
+        gc.collect()
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        out["second_workload"] = second_block(args, args.second_workload, peaks)
     print(json.dumps(out), flush=True)
 
 

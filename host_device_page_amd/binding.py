@@ -43,6 +43,8 @@ HC_MODE_ZEROCOPY = 2
 HC_FLAG_VALIDATE = 1
 HC_FLAG_PROFILE = 2
 HC_MAX_SUBBUFS = 4
+HC_DUPLEX_LOAD_BACK_CTAS = 8
+HC_NOALLOC_MAX_TOKENS = 262144
 
 # hc_pool_kernel_time kinds
 KIND_GATHER, KIND_ZC_WRITE, KIND_ZC_READ, KIND_PADS, KIND_COMPARE, KIND_COPY_ENGINE, KIND_PACK, KIND_UNPACK = range(8)
@@ -404,6 +406,16 @@ class Pool:
         at the default 16 the load-back keeps its full rate and the write-back backs off."""
         return Pool(stream=stream, staging=staging, write_back_mode=write_back_mode, max_ctas=max_ctas,
                     **self._args)
+
+    def duplex_partner(self, stream) -> "Pool":
+        """The load-back pool to run beside this staged write-back pool: a zero-copy sibling
+        on `stream` capped at HC_DUPLEX_LOAD_BACK_CTAS workgroups, the pairing that moves
+        the most bytes in both directions at once (both near 45 GB/s, measured).  Keep the
+        default sibling (16 workgroups) when the load-back must keep its full rate."""
+        if self.mode(0) != HC_MODE_STAGED:
+            raise ValueError("duplex_partner pairs with a staged write-back pool: a zero-copy write-back "
+                             "starves concurrent load-backs")
+        return self.sibling(stream, max_ctas=HC_DUPLEX_LOAD_BACK_CTAS)
 
     def mode(self, which: int) -> int:
         out = ctypes.c_int32()

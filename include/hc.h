@@ -134,6 +134,17 @@ typedef struct hc_subbuf_desc {
                                  read during hc_pool_create only. */
 } hc_subbuf_desc;
 
+/* Both directions at once: two pools over the same device and host buffers, each on
+ * its own copy stream (their rows must not overlap).  Who issues the host accesses
+ * decides how the link is shared (measured on MI355X, PCIe 5.0 x16): a staged
+ * write-back pool (copy engines) beside a zero-copy load-back pool whose max_ctas is
+ * HC_DUPLEX_LOAD_BACK_CTAS moves both directions near 45 GB/s each, ~0.9 of what the
+ * copy engines reach in both directions at once; at the default 16 the load-back keeps
+ * its full rate and the write-back backs off (load-back first, for a forward pass that
+ * waits on it); a zero-copy write-back on 16 workgroups holds the link and starves
+ * concurrent load-backs to ~30 GB/s. */
+#define HC_DUPLEX_LOAD_BACK_CTAS 8
+
 typedef struct hc_pool_desc {
   int32_t num_layers;   /* L, 1..HC_MAX_LAYERS */
   int32_t page_size;    /* P tokens per page, >= 1 */

@@ -158,3 +158,14 @@ def test_layout_arithmetic_matches_oracle(gi):
     out = ctypes.c_int64()
     assert B.lib.hc_host_offset(ctypes.byref(d), 0, g["host_pages"], 0, 0, ctypes.byref(out)) == B.HC_ERR_INVALID
     assert B.lib.hc_host_offset(ctypes.byref(d), 0, 0, g["layers"], 0, ctypes.byref(out)) == B.HC_ERR_INVALID
+
+
+def test_header_constants_match_the_binding():
+    """Every numeric #define of hc.h that the binding also names has the same value there."""
+    text = open(HEADER).read()
+    defs = {m.group(1): int(m.group(2)) for m in re.finditer(r"#define\s+(HC_[A-Z0-9_]+)\s+(\d+)\b", text)}
+    assert {"HC_MAX_SUBBUFS", "HC_DUPLEX_LOAD_BACK_CTAS", "HC_NOALLOC_MAX_TOKENS"} <= set(defs)
+    shared = [k for k in defs if hasattr(B, k)]
+    assert "HC_DUPLEX_LOAD_BACK_CTAS" in shared
+    for k in shared:
+        assert getattr(B, k) == defs[k], k

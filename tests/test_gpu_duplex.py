@@ -62,7 +62,8 @@ def test_write_back_and_load_back_at_once(shape, staged):
         L = shape.layers
         rig.host.np[:] = np.random.default_rng(22).integers(0, 256, rig.host.np.size, dtype=np.uint8)
         load_stream = torch.cuda.Stream()
-        rpool = rig.pool.sibling(load_stream, max_ctas=8)
+        # staged: the library's duplex pairing; zero-copy: the same grid cap by hand
+        rpool = rig.pool.duplex_partner(load_stream) if staged else rig.pool.sibling(load_stream, max_ctas=8)
         for r in range(3):
             (dw, hw), (hl, dl) = bursts(shape, 30 + 10 * r, 9 + 2 * r)
             dw_t, hl_t, dl_t = cuda_i64(dw), cuda_i64(hl), cuda_i64(dl)
@@ -85,6 +86,9 @@ def test_write_back_and_load_back_at_once(shape, staged):
                 O.load_back_layer(rig.geom, l, want_dev, host0, hl, dl)
             assert_bytes_equal(rig.host.np, want_host, f"host pool, round {r}")
             assert_dev_equal(rig.dev_np(), want_dev, f"device pool, round {r}")
+        if not staged:
+            with pytest.raises(ValueError):
+                rig.pool.duplex_partner(load_stream)
     finally:
         if rpool is not None:
             rpool.close()
