@@ -877,6 +877,7 @@ def staged_probe(B, torch, np, W, make_pool, stream, shape, burst, d_t, h_np, li
     gtraffic = counter_traffic(shape.name, "k_gather_stage")
     dram = gather_dram_bound(B, torch, np, W, make_pool, stream, shape, burst, chunk_pages)
     d_gbs = dram["dram"]["achieved"]
+    dtraffic = counter_traffic(shape.name, "k_gather_stage_dram")
     roofline_hbm = {"bound": "hbm", "kernel": "k_gather_stage (staged lf->pf relayout, one chunk, all layers)",
                     "achieved": round(g_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(g_gbs / HBM_PEAK_GBS, 4),
@@ -890,6 +891,7 @@ def staged_probe(B, torch, np, W, make_pool, stream, shape, burst, d_t, h_np, li
                                    "avg_launch_ms": dram["dram"]["avg_launch_ms"],
                                    "bytes_per_launch": dram["bytes_per_launch"], "chunk_pages": dram["chunk_pages"],
                                    "back_to_back_achieved": dram["back_to_back"]["achieved"],
+                                   "traffic": dtraffic["bytes"] if dtraffic else None,
                                    "method": "one chunk of wholly named pages per call, each call after a 1 GiB "
                                              "write on the copy stream (rows read from DRAM, staging writes "
                                              "displace dirty lines)"},
