@@ -36,15 +36,17 @@ constexpr int kXMaxTile = 256;  // positions per unit at most (one per thread at
 #endif
 constexpr int kXUnroll = HC_XCHG_UNROLL;
 // Bytes per unit: the launch's bytes spread over about HC_XCHG_UNITS_PER_CU units per
-// CU, clamped to [kXMinUnitBytes, kXMaxUnitBytes]; a grid of HC_XCHG_BLOCKS_PER_CU
-// workgroups per CU walks them, each loading its next unit's slots one unit ahead
-// (HC_XCHG_PREFETCH).  Measured with cold rows and staging, against a plain copy of the
-// same bytes: 16 units and 8 workgroups per CU with the prefetch reach 80-92 % of that
-// copy's rate on the DeepSeek-V3, MLA + indexer and Llama-3-8B layers, 4 and 4 without
-// it 75-86 %; 2, 8 or 32 units per CU, 2 workgroups per CU, or 4 / 16 loads in flight
-// per lane were no better.
+// CU, clamped to [kXMinUnitBytes, kXMaxUnitBytes], grown until the units fit that many
+// (HC_XCHG_ROUND_FIT); a grid of HC_XCHG_BLOCKS_PER_CU workgroups per CU walks them, each
+// loading its next unit's slots one unit ahead (HC_XCHG_PREFETCH).  Measured with the
+// loads-only hint below, averaged over three interleaved rounds on the 48-layer shard,
+// 78-layer MLA + indexer and Llama-3-8B layers (TB/s, pack then unpack on one staging
+// buffer / each cold): 8 units and 4 workgroups per CU 5.51 / 4.94, 8 and 8 5.48 / 4.86,
+// 16 and 8 5.38 / 4.82 (5.35 / 4.78 without the fit), 4 and 2 ~5.35.  An earlier sweep
+// with both hints found 16 and 8 with the prefetch best (80-92 % of a plain copy of the
+// same bytes), 4 and 4 without it 75-86 %, and 4 or 16 loads in flight per lane no better.
 #ifndef HC_XCHG_UNITS_PER_CU
-#define HC_XCHG_UNITS_PER_CU 16
+#define HC_XCHG_UNITS_PER_CU 8
 #endif
 constexpr int64_t kXMinUnitBytes = 16 << 10;
 constexpr int64_t kXMaxUnitBytes = 256 << 10;
@@ -52,23 +54,30 @@ constexpr int64_t kXMaxUnitBytes = 256 << 10;
 #define HC_XCHG_PREFETCH 1
 #endif
 #ifndef HC_XCHG_BLOCKS_PER_CU
-#define HC_XCHG_BLOCKS_PER_CU 8
+#define HC_XCHG_BLOCKS_PER_CU 4
+#endif
+#ifndef HC_XCHG_ROUND_FIT
+#define HC_XCHG_ROUND_FIT 1
 #endif
 
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(1))) const v4u* gload_t;
 typedef __attribute__((address_space(1))) v4u* gstore_t;
 
-// Both sides of an exchange are streamed once, so loads and stores carry the
-// non-temporal hint (bit 0: loads, bit 1: stores).  Measured with the launch shape above,
-// cold, two rounds: pack / unpack of a DeepSeek-V3 layer 4.39-4.43 / 4.15-4.25 TB/s with
-// both hints against 3.77 / 3.81 without, MLA + indexer 4.91-5.06 / 4.73-4.89 against
-// 4.33-4.60 / 4.45-4.71, Llama-3-8B 4.71-4.94 / 4.65-4.84 against 4.09-4.12 / 4.22-4.26
-// (89-97 % of the same-size copy); stores alone or loads alone gain less.  Eight waves
-// per SIMD (HC_XCHG_MIN_WAVES, which needs 4 loads in flight per lane to fit 64
-// registers) was slower with or without the hints.
+// Loads carry the non-temporal hint (bit 0), stores do not (bit 1 off): on the path the
+// packed layer is read right after it is written (by the broadcast on the owner; by the
+// unpack when a rank packs and unpacks in one place), so the staging bytes should stay in
+// the Infinity Cache.  Measured on one GPU, pack then unpack of each layer on one staging
+// buffer, three interleaved rounds (TB/s of the pair, read + write counted per call):
+// 48-layer shard layer (237 MB) 5.72-5.89 with loads only against 4.92-5.23 with both
+// hints; 78-layer MLA + indexer layer (84 MB) 5.24-5.33 against 5.05; Llama-3-8B layer
+// (64 MiB) 4.93-5.20 against 4.89-4.92.  The unpack then reads staging at ~6 TB/s.  Each
+// layer packed into its own staging buffer and unpacked later (everything cold) runs
+// 3-8 % slower with loads only than with both hints, and 12-18 % slower with neither.
+// Eight waves per SIMD (HC_XCHG_MIN_WAVES, which needs 4 loads in flight per lane to fit
+// 64 registers) was slower with or without the hints.
 #ifndef HC_XCHG_NT
-#define HC_XCHG_NT 3
+#define HC_XCHG_NT 1
 #endif
 #ifndef HC_XCHG_MIN_WAVES
 #define HC_XCHG_MIN_WAVES 1  // launch-bounds floor on waves per SIMD (caps registers)
@@ -194,15 +203,26 @@ int64_t exchange_plan(const Geom& g, int64_t n, int32_t num_cus, XPlan* x) {
     bytes += x->positions[b] * g.sub[b].elem;
   }
   const int64_t cus = num_cus > 0 ? num_cus : 1;
-  int64_t unit_bytes = bytes / (cus * HC_XCHG_UNITS_PER_CU);
+  const int64_t target = cus * HC_XCHG_UNITS_PER_CU;  // a whole number of rounds of the grid
+  int64_t unit_bytes = (bytes + target - 1) / target;
   unit_bytes = unit_bytes < kXMinUnitBytes ? kXMinUnitBytes : (unit_bytes > kXMaxUnitBytes ? kXMaxUnitBytes : unit_bytes);
   int64_t units = 0;
-  for (int b = 0; b < g.nsub; b++) {
-    int64_t t = unit_bytes / g.sub[b].elem;
-    t = t < 1 ? 1 : (t > kXMaxTile ? kXMaxTile : t);
-    x->tile[b] = (int32_t)t;
-    units += (x->positions[b] + t - 1) / t;
-    x->units_end[b] = units;
+  for (;;) {
+    units = 0;
+    bool capped = true;
+    for (int b = 0; b < g.nsub; b++) {
+      int64_t t = unit_bytes / g.sub[b].elem;
+      t = t < 1 ? 1 : (t > kXMaxTile ? kXMaxTile : t);
+      capped = capped && t == kXMaxTile;
+      x->tile[b] = (int32_t)t;
+      units += (x->positions[b] + t - 1) / t;
+      x->units_end[b] = units;
+    }
+    // Whole rows per unit round each sub-buffer's count up, which can leave a few units
+    // past the last full round of the grid, run by a few workgroups alone at the end (the
+    // 48-layer shard layer made 4132 units for 2048 workgroups).  Units grow until they fit.
+    if (!HC_XCHG_ROUND_FIT || units <= target || capped || unit_bytes >= kXMaxUnitBytes) break;
+    unit_bytes += unit_bytes / 64 + 16;
   }
   for (int b = g.nsub; b < HC_MAX_SUBBUFS; b++) {
     x->positions[b] = 0;
