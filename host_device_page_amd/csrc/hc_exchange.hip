@@ -20,6 +20,13 @@
 // vector u % vecs of row u / vecs, in batches of loads issued before their stores.
 // These kernels live apart from the host-link kernels so that each file's measured
 // code stays as it was measured.
+//
+// A flat split was tried and dropped: the layer's vectors cut into one contiguous, equal
+// range per workgroup (2, 4 or 8 per CU), each walked in batches of up to 256 rows with an
+// intake per batch.  It balances the work exactly but starts every workgroup on its intake
+// at once and has no next unit to prefetch: over three interleaved rounds on the shard,
+// 78-layer and Llama-3-8B layers it reached 5.11-5.23 TB/s for pack then unpack (4.53-4.65
+// cold) against 5.47 (4.91) for the units below.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>

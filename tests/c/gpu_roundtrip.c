@@ -1,6 +1,7 @@
-/* A write-back, a per-layer load-back and a captured load-back burst replayed into
- * new slots, through the C ABI from plain C (HIP runtime for memory and streams,
- * no Python), each checked byte for byte against the C oracle.  Built by
+/* A write-back, a per-layer load-back, a captured load-back burst replayed into
+ * new slots and a write-back that allocates nothing, through the C ABI from plain C
+ * (HIP runtime for memory and streams, no Python), each checked byte for byte
+ * against the C oracle.  Built by
  * tests/c/build.py, run by tests/test_c_programs.py on a GPU. */
 #include <stdint.h>
 #include <stdio.h>
@@ -185,8 +186,28 @@ int main(void) {
       free(got);
     }
   HCCK(hc_load_back_graph_destroy(graph));
+
+  /* the write-back that allocates nothing: other host pages, from the slots just loaded;
+   * its host list lives in pinned memory */
+  int64_t* pinned = NULL;
+  HCCK(hc_host_alloc((int64_t)sizeof(hidx), 0, (void**)&pinned));
+  for (int k = 0; k < NPAGES; k++) {
+    int p;
+    do p = (int)(next() % H); while (used_page[p]);
+    used_page[p] = 1;
+    for (int r = 0; r < P; r++) pinned[k * P + r] = (int64_t)p * P + r;
+  }
+  HCCK(hc_write_back_all_layers_noalloc(pool, dd2, pinned, n, NULL));
+  HCCK(hc_pool_sync(pool));
+  if (orc_write_back(&g, hostcopy, want, d3, pinned, n) != ORC_OK) return 11;
+  if (memcmp(want, host, (size_t)host_bytes) != 0) {
+    fprintf(stderr, "write-back without allocation differs from the oracle\n");
+    return 12;
+  }
+  HCCK(hc_host_free(pinned));
   HCCK(hc_pool_destroy(pool));
   HCCK(hc_host_free(host));
-  printf("gpu_roundtrip ok: %lld tokens x %d layers x %d sub-buffers bit-exact, eager and captured\n", (long long)n, L, NSUB);
+  printf("gpu_roundtrip ok: %lld tokens x %d layers x %d sub-buffers bit-exact, eager, captured and without allocation\n",
+         (long long)n, L, NSUB);
   return 0;
 }
