@@ -6,10 +6,11 @@
 // indices CPU-side; the CPU validates it once per burst and uploads a compact
 // plan.  Zero-copy mode then runs one kernel over all tokens, layers and
 // sub-buffers that writes straight into the pinned host pool.  Staged mode
-// gathers chunks of whole host pages into the device staging buffer as exact
-// host page images (one launch per chunk, all layers) and moves each page with
-// the copy engines; tokens of partially named pages go through the zero-copy
-// kernel so rows the list does not name are never overwritten.
+// gathers chunks of wholly named host pages, sorted by host page, into the device
+// staging buffer in their host byte order (one launch per chunk, all layers) and
+// moves each run of adjacent pages with one copy-engine transfer; tokens of
+// partially named pages go through the zero-copy kernel so rows the list does not
+// name are never overwritten.
 //
 // Load-back (loader-thread page, sglang PR 38472, Motivation): one kernel per
 // layer reads device-resident index lists, so the CPU builds no per-layer
@@ -342,7 +343,8 @@ void fill_geom(hc_pool* p) {
     s.host_page_stride = L.host_page_stride[b];
     s.layer_stride = L.layer_stride[b];
     s.row_stride = L.row_stride[b];
-    s.img_off = L.img_off[b];
+    s.img_off = hc::staging_sub_base(L, b, p->chunk_pages);
+    s.stg_slot = hc::staging_slot_stride(L, b);
   }
 }
 
@@ -713,12 +715,13 @@ int hc_write_back_all_layers(hc_pool* p, const int64_t* device_idx, const int64_
   }
   const Layout& L = p->lay;
   const bool staged = p->wb_mode == HC_MODE_STAGED;
-  // plan buffer layout: hidx int64[n] | pads int64[n] | srow int32[n] | ztok int32[n]
+  // plan buffer layout: hidx int64[n] | pads int64[n] | srow int32[n] | ztok int32[n] | perm int32[n]
   const int64_t o_hidx = 0;
   const int64_t o_pads = align16(o_hidx + 8 * n);
   const int64_t o_srow = align16(o_pads + 8 * n);
   const int64_t o_ztok = align16(o_srow + 4 * n);
-  const int64_t bytes = align16(o_ztok + 4 * n);
+  const int64_t o_perm = align16(o_ztok + 4 * n);
+  const int64_t bytes = align16(o_perm + 4 * n);
   rc = plan_reserve(p, bytes);
   if (rc != HC_OK) return finish(rc);
   PlanBuf& pb = p->plan[p->plan_cur];
@@ -726,10 +729,11 @@ int hc_write_back_all_layers(hc_pool* p, const int64_t* device_idx, const int64_
   int64_t* pads = (int64_t*)(pb.h + o_pads);
   int32_t* srow = (int32_t*)(pb.h + o_srow);
   int32_t* ztok = (int32_t*)(pb.h + o_ztok);
+  int32_t* perm = (int32_t*)(pb.h + o_perm);
   memcpy(hidx, host_idx, (size_t)(8 * n));
   int64_t nz = 0, npads = 0;
   if (staged) {
-    p->planner.plan_staged(host_idx, n, p->chunk_pages, p->host, p->staging, srow, ztok, &nz, pads, &npads);
+    p->planner.plan_staged(host_idx, n, p->chunk_pages, p->host, p->staging, perm, srow, ztok, &nz, pads, &npads);
   } else if (L.layout == HC_LAYOUT_KV_SPLIT_SHARD && L.stride > L.payload) {
     npads = p->planner.distinct_pages(host_idx, n, pads);
   }
@@ -740,6 +744,7 @@ int hc_write_back_all_layers(hc_pool* p, const int64_t* device_idx, const int64_
   const int64_t* d_pads = (const int64_t*)(pb.d + o_pads);
   const int32_t* d_srow = (const int32_t*)(pb.d + o_srow);
   const int32_t* d_ztok = (const int32_t*)(pb.d + o_ztok);
+  const int32_t* d_perm = (const int32_t*)(pb.d + o_perm);
   p->plan_cur ^= 1;
   hipError_t e = hipSuccess;
   if (staged) {
@@ -759,8 +764,8 @@ int hc_write_back_all_layers(hc_pool* p, const int64_t* device_idx, const int64_
         // copy engines (measured), which would take away the staged mode's point.
         Timer t(p, 0);
         t.record_start();
-        e = hc::launch_gather_stage(p->geom, device_idx, d_hidx, d_srow, c.t0, c.t1 - c.t0, p->staging, p->d_err,
-                                    p->num_cus, hc::LaunchTimer{}, p->stream);
+        e = hc::launch_gather_stage(p->geom, device_idx, d_hidx, d_perm, d_srow, c.t0, c.t1 - c.t0, p->staging,
+                                    p->d_err, p->num_cus, hc::LaunchTimer{}, p->stream);
         t.record_stop();
         t.done(e == hipSuccess);
       }

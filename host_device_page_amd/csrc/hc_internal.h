@@ -21,7 +21,8 @@ struct SubGeom {
   int64_t host_page_stride;// bytes from page p to page p+1 of this sub-buffer in the host pool
   int64_t layer_stride;    // bytes from layer l to l+1 inside one page
   int64_t row_stride;      // bytes from row r to r+1 inside one page and layer (0 for page blocks)
-  int64_t img_off;         // offset of this sub-buffer inside one staging page image
+  int64_t img_off;         // staging: offset of this sub-buffer's slot-0 page image in a chunk
+  int64_t stg_slot;        // staging: bytes from slot s to slot s+1 of this sub-buffer
 };
 
 struct Geom {
@@ -57,6 +58,18 @@ struct Layout {
 
 // Fills *out from desc; on failure returns a negative hc_status and writes a message.
 int layout_from_desc(const hc_pool_desc* desc, Layout* out, char* msg, size_t msg_len);
+
+// Staging layout of one chunk of C page images.  Shard layout: whole shards back to back,
+// so a shard leaves staging as one region with its zero pad.  Page-first layouts:
+// sub-buffer-major, [sub-buffer][slot][one sub-buffer page], so the pages of one
+// sub-buffer in consecutive slots form one contiguous range, which leaves staging as one
+// region when their host pages are adjacent too.  Either way a chunk takes C * stride bytes.
+inline int64_t staging_sub_base(const Layout& L, int b, int64_t C) {
+  return L.layout == HC_LAYOUT_KV_SPLIT_SHARD ? L.img_off[b] : C * L.img_off[b];
+}
+inline int64_t staging_slot_stride(const Layout& L, int b) {
+  return L.layout == HC_LAYOUT_KV_SPLIT_SHARD ? L.stride : L.subpage[b];
+}
 int64_t layout_host_offset(const Layout& lay, int b, int64_t page, int32_t layer, int32_t row);
 
 // Thread-local error message of the C ABI (hc_last_error); returns `code`.
@@ -81,9 +94,12 @@ struct LaunchTimer {
 };
 
 // Kernel launchers (hc_kernels.hip).  All enqueue on `stream` and return the launch status.
+// Gather of staged tokens [t0, t0 + count) of a write-back plan: perm[k] is the list
+// position of staged token k, srow[k] its row inside the chunk's staging images.
 hipError_t launch_gather_stage(const Geom& g, const int64_t* dev_idx, const int64_t* host_idx,
-                               const int32_t* srow, int64_t t0, int64_t count, uint8_t* staging,
-                               int32_t* err, int32_t num_cus, const LaunchTimer& t, hipStream_t stream);
+                               const int32_t* perm, const int32_t* srow, int64_t t0, int64_t count,
+                               uint8_t* staging, int32_t* err, int32_t num_cus, const LaunchTimer& t,
+                               hipStream_t stream);
 hipError_t launch_zc_write(const Geom& g, const int64_t* dev_idx, const int64_t* host_idx,
                            const int32_t* tok_list, int64_t count, uint8_t* host, int32_t* err,
                            int32_t max_ctas, const LaunchTimer& t, hipStream_t stream);

@@ -280,13 +280,15 @@ __device__ __forceinline__ int unit_sub(const Geom& g, int64_t n, int blk_stride
 }
 
 // ---------------------------------------------------------------- staged write-back: gather
-// Units of (sub-buffer, kGatherTile tokens of [t0, t0+count), layer), walked grid-stride
-// by a grid of a few workgroups per CU: small units keep every CU streaming until the
-// last unit, where one workgroup per (tile, layer, sub) left 2-3 rounds per CU and a
-// thin tail.  srow[i] = slot * P + row inside the chunk's staging images, or -1 for
-// tokens that do not go through staging.
+// Units of (sub-buffer, kGatherTile staged tokens of [t0, t0+count), layer), walked
+// grid-stride by a grid of a few workgroups per CU: small units keep every CU streaming
+// until the last unit, where one workgroup per (tile, layer, sub) left 2-3 rounds per CU
+// and a thin tail.  Staged token k is list position perm[k]; srow[k] = slot * P + row
+// inside the chunk's staging images (the planner lists a chunk's tokens together, so a
+// chunk is a range of k), or -1 for a token that does not go through staging.
 __global__ __launch_bounds__(kThreads) void k_gather_stage(Geom g, const int64_t* __restrict__ dev_idx,
                                                            const int64_t* __restrict__ host_idx,
+                                                           const int32_t* __restrict__ perm,
                                                            const int32_t* __restrict__ srow, int64_t t0,
                                                            int64_t count, uint8_t* __restrict__ staging,
                                                            int32_t* __restrict__ err, int64_t units) {
@@ -302,11 +304,12 @@ __global__ __launch_bounds__(kThreads) void k_gather_stage(Geom g, const int64_t
     const int64_t tile = rem / g.L;
     const int l = (int)(rem - tile * g.L);
     const SubGeom& s = g.sub[b];
-    const int64_t i = t0 + tile * kGatherTile + threadIdx.x;
+    const int64_t k = t0 + tile * kGatherTile + threadIdx.x;
     bool keep = false;
     uint64_t src = 0, dst = 0;
-    if (threadIdx.x < kGatherTile && i < t0 + count) {
-      const int32_t sr = srow[i];
+    if (threadIdx.x < kGatherTile && k < t0 + count) {
+      const int64_t i = perm[k];
+      const int32_t sr = srow[k];
       if (sr >= 0) {
         const int32_t slot = sr / g.P;
         const int32_t r = sr - slot * g.P;
@@ -315,7 +318,7 @@ __global__ __launch_bounds__(kThreads) void k_gather_stage(Geom g, const int64_t
           const int64_t d = dev_idx[i];
           if (d >= 0 && d < g.S) {
             src = layer_base(s, l) + (uint64_t)dev_off(s, d, g.P);
-            dst = (uint64_t)staging + (uint64_t)((int64_t)slot * g.img_bytes + s.img_off +
+            dst = (uint64_t)staging + (uint64_t)((int64_t)slot * s.stg_slot + s.img_off +
                                                  (int64_t)l * s.layer_stride + (int64_t)r * s.row_stride);
             keep = true;
           } else {
@@ -562,15 +565,15 @@ hipError_t launch(void (*kernel)(KArgs...), dim3 grid, const LaunchTimer& t, hip
 
 }  // namespace
 
-hipError_t launch_gather_stage(const Geom& g, const int64_t* dev_idx, const int64_t* host_idx, const int32_t* srow,
-                               int64_t t0, int64_t count, uint8_t* staging, int32_t* err, int32_t num_cus,
-                               const LaunchTimer& t, hipStream_t stream) {
+hipError_t launch_gather_stage(const Geom& g, const int64_t* dev_idx, const int64_t* host_idx, const int32_t* perm,
+                               const int32_t* srow, int64_t t0, int64_t count, uint8_t* staging, int32_t* err,
+                               int32_t num_cus, const LaunchTimer& t, hipStream_t stream) {
   if (count <= 0) return hipSuccess;
   const int64_t units = ceil_div(count, kGatherTile) * g.L * g.nsub;
   const int64_t cap = (int64_t)(num_cus > 0 ? num_cus : 256) * HC_GATHER_BLOCKS_PER_CU;
   const int64_t grid = units < cap ? units : cap;
-  return launch(k_gather_stage, dim3((unsigned)grid), t, stream, g, dev_idx, host_idx, srow, t0, count, staging, err,
-                units);
+  return launch(k_gather_stage, dim3((unsigned)grid), t, stream, g, dev_idx, host_idx, perm, srow, t0, count, staging,
+                err, units);
 }
 
 // Units of a zero-copy launch over list positions [0, count): summed over sub-buffers.

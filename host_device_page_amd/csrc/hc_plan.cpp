@@ -3,6 +3,8 @@
 
 #include <stdio.h>
 
+#include <algorithm>
+
 namespace hc {
 namespace {
 
@@ -91,62 +93,77 @@ void Planner::emit_region(uint8_t* dst, const uint8_t* src, int64_t len) {
 }
 
 void Planner::plan_staged(const int64_t* h, int64_t n, int64_t chunk_pages, uint8_t* host, const uint8_t* staging,
-                          int32_t* srow, int32_t* ztok, int64_t* nz, int64_t* pads, int64_t* npads) {
+                          int32_t* perm, int32_t* srow, int32_t* ztok, int64_t* nz, int64_t* pads, int64_t* npads) {
   const Layout& L = lay_;
   const int64_t C = chunk_pages;
   regions.clear();
   chunks.clear();
-  slot_page_.assign((size_t)C, -1);
-  slot_rows_.assign((size_t)C, 0);
-  int64_t nslots = 0, t0 = 0;
+  whole_.clear();
   *nz = 0;
   *npads = 0;
   max_slots_ = 0;
-  auto close_chunk = [&](int64_t t1) {
-    if (nslots > max_slots_) max_slots_ = nslots;
-    const size_t r0 = regions.size();
-    chunk_first_region_ = r0;
-    for (int64_t s = 0; s < nslots; s++) {
-      const int64_t page = slot_page_[(size_t)s];
-      if (slot_rows_[(size_t)s] == L.P) {
-        const uint8_t* img = staging + s * L.stride;
-        if (L.layout == HC_LAYOUT_KV_SPLIT_SHARD) {
-          emit_region(host + page * L.stride, img, L.stride);
-        } else {
-          for (int b = 0; b < L.nsub; b++)
-            emit_region(host + L.host_region[b] + page * L.subpage[b], img + L.img_off[b], L.subpage[b]);
-        }
-      } else if (L.layout == HC_LAYOUT_KV_SPLIT_SHARD && L.stride > L.payload) {
-        pads[(*npads)++] = page;
-      }
-      page_slot_[(size_t)page] = -1;
-    }
-    for (int64_t i = t0; i < t1; i++) {
-      const int32_t s = srow[i] / L.P;
-      if (slot_rows_[(size_t)s] != L.P) {
-        srow[i] = -1;
-        ztok[(*nz)++] = (int32_t)i;
-      }
-    }
-    chunks.push_back({t0, t1, r0, regions.size()});
-    t0 = t1;
-    nslots = 0;
-  };
+  // rows named per page; the wholly named pages, and the shard pages named in part
+  for (int64_t i = 0; i < n; i++) page_rows_[(size_t)(h[i] / L.P)]++;
+  const bool shard_pad = L.layout == HC_LAYOUT_KV_SPLIT_SHARD && L.stride > L.payload;
   for (int64_t i = 0; i < n; i++) {
     const int64_t page = h[i] / L.P;
-    const int32_t r = (int32_t)(h[i] - page * L.P);
-    int32_t s = page_slot_[(size_t)page];
-    if (s < 0) {
-      if (nslots == C) close_chunk(i);
-      s = (int32_t)nslots++;
-      page_slot_[(size_t)page] = s;
-      slot_page_[(size_t)s] = page;
-      slot_rows_[(size_t)s] = 0;
-    }
-    slot_rows_[(size_t)s]++;
-    srow[i] = s * L.P + r;
+    if (test_and_set(page_seen_, page)) continue;
+    if (page_rows_[(size_t)page] == L.P) whole_.push_back(page);
+    else if (shard_pad) pads[(*npads)++] = page;
   }
-  close_chunk(n);
+  std::sort(whole_.begin(), whole_.end());
+  const int64_t nw = (int64_t)whole_.size();
+  const int64_t nchunks = (nw + C - 1) / C;
+  for (int64_t r = 0; r < nw; r++) page_slot_[(size_t)whole_[(size_t)r]] = (int32_t)r;
+  // staged tokens per chunk, then their positions: chunk by chunk, list order inside
+  chunk_fill_.assign((size_t)nchunks + 1, 0);
+  for (int64_t i = 0; i < n; i++) {
+    const int32_t rank = page_slot_[(size_t)(h[i] / L.P)];
+    if (rank >= 0) chunk_fill_[(size_t)(rank / C) + 1]++;
+  }
+  for (int64_t c = 0; c < nchunks; c++) chunk_fill_[(size_t)c + 1] += chunk_fill_[(size_t)c];
+  for (int64_t c = 0; c < nchunks; c++) chunks.push_back({chunk_fill_[(size_t)c], chunk_fill_[(size_t)c + 1], 0, 0});
+  for (int64_t i = 0; i < n; i++) {
+    const int64_t page = h[i] / L.P;
+    const int32_t rank = page_slot_[(size_t)page];
+    if (rank < 0) {
+      ztok[(*nz)++] = (int32_t)i;
+      continue;
+    }
+    const int64_t k = chunk_fill_[(size_t)(rank / C)]++;
+    perm[k] = (int32_t)i;
+    srow[k] = (int32_t)((rank % C) * L.P + (h[i] - page * L.P));
+  }
+  // the copy-engine regions of each chunk: slot s holds whole_[c * C + s]
+  for (int64_t c = 0; c < nchunks; c++) {
+    Chunk& ch = chunks[(size_t)c];
+    ch.r0 = regions.size();
+    chunk_first_region_ = ch.r0;
+    const int64_t slots = std::min<int64_t>(C, nw - c * C);
+    if (slots > max_slots_) max_slots_ = slots;
+    if (L.layout == HC_LAYOUT_KV_SPLIT_SHARD) {
+      for (int64_t s = 0; s < slots; s++) {
+        const int64_t page = whole_[(size_t)(c * C + s)];
+        emit_region(host + page * L.stride, staging + s * L.stride, L.stride);
+      }
+    } else {
+      // sub-buffer-major staging: slot s of sub-buffer b is one sub-buffer page
+      for (int b = 0; b < L.nsub; b++)
+        for (int64_t s = 0; s < slots; s++) {
+          const int64_t page = whole_[(size_t)(c * C + s)];
+          emit_region(host + L.host_region[b] + page * L.subpage[b],
+                      staging + staging_sub_base(L, b, C) + s * staging_slot_stride(L, b), L.subpage[b]);
+        }
+    }
+    ch.r1 = regions.size();
+  }
+  // the per-page scratch back to its resting state
+  for (int64_t i = 0; i < n; i++) {
+    const int64_t page = h[i] / L.P;
+    page_rows_[(size_t)page] = 0;
+    page_slot_[(size_t)page] = -1;
+    clear_bit(page_seen_, page);
+  }
 }
 
 int64_t Planner::distinct_pages(const int64_t* h, int64_t n, int64_t* pages) {

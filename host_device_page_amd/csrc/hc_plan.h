@@ -20,7 +20,8 @@ struct Region {
   int64_t len;
 };
 
-// One staging chunk: tokens [t0, t1) of the list, its transfers regions[r0, r1).
+// One staging chunk: staged tokens [t0, t1) of the plan's perm / srow arrays, its
+// transfers regions[r0, r1).
 struct Chunk {
   int64_t t0, t1;
   size_t r0, r1;
@@ -36,16 +37,21 @@ class Planner {
   // order.  HC_OK, or HC_ERR_INVALID with a message in msg.
   int validate(const int64_t* host_idx, int64_t n, char* msg, size_t msg_len);
 
-  // Staged plan: the list in order, cut into chunks of at most chunk_pages staging
-  // slots (one slot per distinct host page).  Writes, per token, srow[i] = slot * P +
-  // row inside the chunk's staging images, or -1 for tokens of pages the list names
-  // only in part; those tokens' list positions go to ztok[0, *nz) for the zero-copy
-  // kernel.  Fills regions/chunks: every wholly named page leaves staging as one
-  // region per sub-buffer (page-first layouts) or one region per shard, adjacent
-  // regions merged.  Shard pages named in part go to pads[0, *npads) (their pad is
-  // cleared separately).  host and staging are base addresses for the regions.
+  // Staged plan.  The pages the list names whole (all P rows, anywhere in the list) go
+  // through staging: sorted by host page and cut into chunks of at most chunk_pages
+  // staging slots, so that pages adjacent in the host pool sit in adjacent slots of one
+  // chunk and leave staging as one copy-engine region.  Their tokens are listed chunk by
+  // chunk, in list order inside a chunk: perm[k] is the list position of staged token k
+  // and srow[k] = slot * P + row its row inside the chunk's staging images; chunk c
+  // covers k in [chunks[c].t0, chunks[c].t1).  Tokens of pages the list names only in
+  // part go, in list order, to ztok[0, *nz) for the zero-copy kernel (rows the list does
+  // not name must keep their bytes), and in the shard layout those pages go to
+  // pads[0, *npads) (their pad is cleared separately).  Fills regions/chunks: every
+  // staged page leaves staging as one region per sub-buffer (page-first layouts) or one
+  // region per shard, adjacent regions of a chunk merged.  host and staging are base
+  // addresses for the regions.  perm, srow and ztok hold n entries, pads n.
   void plan_staged(const int64_t* host_idx, int64_t n, int64_t chunk_pages, uint8_t* host, const uint8_t* staging,
-                   int32_t* srow, int32_t* ztok, int64_t* nz, int64_t* pads, int64_t* npads);
+                   int32_t* perm, int32_t* srow, int32_t* ztok, int64_t* nz, int64_t* pads, int64_t* npads);
 
   // Distinct pages named by the list, in order of first use; returns the count.
   int64_t distinct_pages(const int64_t* host_idx, int64_t n, int64_t* pages);
@@ -61,12 +67,12 @@ class Planner {
   Layout lay_;
   size_t chunk_first_region_ = 0;    // regions before this index belong to closed chunks
   int64_t max_slots_ = 0;
-  std::vector<int32_t> page_slot_;   // [H] staging slot of a page in the open chunk, -1 otherwise
+  std::vector<int32_t> page_slot_;   // [H] rank of a staged page among the burst's staged pages, -1 otherwise
   std::vector<uint64_t> seen_;       // bitmap over host tokens (distinctness)
   std::vector<uint64_t> page_seen_;  // bitmap over host pages
-  std::vector<int32_t> page_rows_;   // [H] rows named per page (page-block check)
-  std::vector<int64_t> slot_page_;
-  std::vector<int32_t> slot_rows_;
+  std::vector<int32_t> page_rows_;   // [H] rows named per page
+  std::vector<int64_t> whole_;       // the burst's wholly named pages, sorted
+  std::vector<int64_t> chunk_fill_;  // per chunk: next staged-token position
 };
 
 }  // namespace hc

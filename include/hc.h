@@ -193,8 +193,11 @@ int hc_desc_check(const hc_pool_desc* desc);
  * page-first, H * shard stride for the shard layout. */
 int hc_host_pool_bytes(const hc_pool_desc* desc, int64_t* out_bytes);
 
-/* Bytes of one page image in the device staging buffer (the shard stride for the
- * shard layout, the summed sub-buffer pages for page-first). */
+/* Staging bytes per page of a chunk: the shard stride for the shard layout (each page
+ * is staged as its whole shard image, pad included), the summed sub-buffer pages for the
+ * page-first layouts (a chunk holds each sub-buffer's pages together, so that pages
+ * adjacent in the host pool leave staging as one copy).  A chunk of C pages takes C times
+ * this. */
 int hc_staging_page_bytes(const hc_pool_desc* desc, int64_t* out_bytes);
 
 /* Byte offset of (sub-buffer, page, layer, row) in the host pool.  For a page-block

@@ -4,9 +4,11 @@
 // chunk's staging images, the region list is copied, split-page tokens are written
 // row by row, listed shard pads are zeroed -- and the resulting host pool must hold
 // exactly the named rows (and the named pages' blocks and pads) and nothing else.
-// The structural rules are checked too: chunks partition the list in order, a chunk
-// holds at most chunk_pages pages, a token goes through staging only when its chunk
-// names its whole page, and the split-page token list is exactly the other tokens.
+// The structural rules are checked too: staged and split-page tokens cover the list
+// once; a token goes through staging exactly when the list names its whole page;
+// chunks partition the staged tokens, list order inside a chunk, at most chunk_pages
+// pages each, pages ascending across slots and chunks; host pages adjacent in
+// consecutive slots leave staging as one region.
 #include <stdio.h>
 #include <stdlib.h>
 #include <string.h>
@@ -78,40 +80,68 @@ static void run_case(const Shape& sh, const std::vector<int64_t>& h, int64_t chu
   char msg[256];
   CHECK(pl.validate(h.data(), (int64_t)h.size(), msg, sizeof(msg)) == HC_OK);
   const int64_t n = (int64_t)h.size();
-  std::vector<uint8_t> host((size_t)L.host_bytes, 0xAB), staging((size_t)(chunk_pages * L.stride), 0);
-  std::vector<int32_t> srow((size_t)std::max<int64_t>(n, 1)), ztok((size_t)std::max<int64_t>(n, 1));
+  const int64_t C = chunk_pages;
+  std::vector<uint8_t> host((size_t)L.host_bytes, 0xAB), staging((size_t)(C * L.stride), 0);
+  std::vector<int32_t> perm((size_t)std::max<int64_t>(n, 1)), srow((size_t)std::max<int64_t>(n, 1)),
+      ztok((size_t)std::max<int64_t>(n, 1));
   std::vector<int64_t> pads((size_t)std::max<int64_t>(n, 1));
   int64_t nz = -1, npads = -1;
-  pl.plan_staged(h.data(), n, chunk_pages, host.data(), staging.data(), srow.data(), ztok.data(), &nz, pads.data(),
-                 &npads);
-  // chunks partition [0, n) in order
-  CHECK(!pl.chunks.empty());
-  CHECK(pl.chunks.front().t0 == 0 && pl.chunks.back().t1 == n);
-  for (size_t c = 1; c < pl.chunks.size(); c++) CHECK(pl.chunks[c].t0 == pl.chunks[c - 1].t1);
-  CHECK(pl.chunks.back().r1 == pl.regions.size());
+  pl.plan_staged(h.data(), n, C, host.data(), staging.data(), perm.data(), srow.data(), ztok.data(), &nz,
+                 pads.data(), &npads);
+  std::map<int64_t, int> rows;  // page -> rows the whole list names
+  for (int64_t t : h) rows[t / L.P]++;
+  const int64_t ns = n - nz;
+  CHECK(nz >= 0 && ns >= 0);
+  // staged tokens and split-page tokens: every list position exactly once
+  std::vector<int> seen((size_t)std::max<int64_t>(n, 1), 0);
+  for (int64_t k = 0; k < ns; k++) {
+    CHECK(perm[(size_t)k] >= 0 && perm[(size_t)k] < n);
+    CHECK(seen[(size_t)perm[(size_t)k]]++ == 0);
+  }
+  for (int64_t k = 0; k < nz; k++) {
+    CHECK(ztok[(size_t)k] >= 0 && ztok[(size_t)k] < n);
+    CHECK(seen[(size_t)ztok[(size_t)k]]++ == 0);
+  }
+  // split-page tokens: exactly those of pages the list names in part, in list order
   std::vector<int32_t> expect_z;
   std::set<int64_t> expect_pads;
+  for (int64_t i = 0; i < n; i++) {
+    const int64_t page = h[(size_t)i] / L.P;
+    if (rows[page] != L.P) {
+      expect_z.push_back((int32_t)i);
+      if (L.layout == HC_LAYOUT_KV_SPLIT_SHARD && L.stride > L.payload) expect_pads.insert(page);
+    }
+  }
+  CHECK(nz == (int64_t)expect_z.size());
+  for (int64_t k = 0; k < nz; k++) CHECK(ztok[(size_t)k] == expect_z[(size_t)k]);
+  // pads: each page named in part once
+  std::set<int64_t> got_pads(pads.begin(), pads.begin() + npads);
+  CHECK((int64_t)got_pads.size() == npads && got_pads == expect_pads);
+  // chunks partition [0, ns) in order; regions likewise
+  if (ns == 0) CHECK(pl.chunks.empty() && pl.regions.empty());
+  if (ns > 0) {
+    CHECK(pl.chunks.front().t0 == 0 && pl.chunks.back().t1 == ns);
+    CHECK(pl.chunks.front().r0 == 0 && pl.chunks.back().r1 == pl.regions.size());
+  }
+  for (size_t c = 1; c < pl.chunks.size(); c++) {
+    CHECK(pl.chunks[c].t0 == pl.chunks[c - 1].t1);
+    CHECK(pl.chunks[c].r0 == pl.chunks[c - 1].r1);
+  }
+  int64_t prev_page = -1;
   for (const hc::Chunk& c : pl.chunks) {
-    CHECK(c.t0 <= c.t1 && c.r0 <= c.r1);
-    std::map<int64_t, int> rows;  // page -> rows named inside this chunk
-    for (int64_t i = c.t0; i < c.t1; i++) rows[h[(size_t)i] / L.P]++;
-    CHECK((int64_t)rows.size() <= chunk_pages);
+    CHECK(c.t0 < c.t1 && c.r0 < c.r1);
     // model of the gather: each staged token's rows into its slot's page image
     std::map<int32_t, int64_t> slot_page;
     std::fill(staging.begin(), staging.end(), 0);
-    for (int64_t i = c.t0; i < c.t1; i++) {
+    for (int64_t k = c.t0; k < c.t1; k++) {
+      if (k > c.t0) CHECK(perm[(size_t)k] > perm[(size_t)k - 1]);  // list order inside a chunk
+      const int64_t i = perm[(size_t)k];
       const int64_t page = h[(size_t)i] / L.P;
       const int row = (int)(h[(size_t)i] % L.P);
-      const bool whole = rows[page] == L.P;
-      if (!whole) {
-        CHECK(srow[(size_t)i] == -1);
-        expect_z.push_back((int32_t)i);
-        if (L.layout == HC_LAYOUT_KV_SPLIT_SHARD && L.stride > L.payload) expect_pads.insert(page);
-        continue;
-      }
-      CHECK(srow[(size_t)i] >= 0 && srow[(size_t)i] % L.P == row);
-      const int32_t slot = srow[(size_t)i] / L.P;
-      CHECK(slot < chunk_pages);
+      CHECK(rows[page] == L.P);
+      CHECK(srow[(size_t)k] >= 0 && srow[(size_t)k] % L.P == row);
+      const int32_t slot = srow[(size_t)k] / L.P;
+      CHECK(slot < C);
       auto it = slot_page.find(slot);
       if (it == slot_page.end()) slot_page[slot] = page;
       else CHECK(it->second == page);
@@ -120,15 +150,32 @@ static void run_case(const Shape& sh, const std::vector<int64_t>& h, int64_t chu
         const int r = L.gran[b] == HC_PAGE_BLOCKS ? 0 : row;
         for (int l = 0; l < L.L; l++) {
           const int64_t src = hc::layout_host_offset(L, b, page, l, r);
-          const int64_t img = (int64_t)slot * L.stride + L.img_off[b] + (int64_t)l * L.layer_stride[b] +
-                              (int64_t)r * L.row_stride[b];
-          for (int64_t k = 0; k < L.elem[b]; k++) staging[(size_t)(img + k)] = truth(src + k);
+          const int64_t img = hc::staging_sub_base(L, b, C) + (int64_t)slot * hc::staging_slot_stride(L, b) +
+                              (int64_t)l * L.layer_stride[b] + (int64_t)r * L.row_stride[b];
+          for (int64_t k2 = 0; k2 < L.elem[b]; k2++) staging[(size_t)(img + k2)] = truth(src + k2);
         }
       }
     }
-    // every staged page has a distinct slot
-    std::set<int64_t> pages_seen;
-    for (auto& kv : slot_page) CHECK(pages_seen.insert(kv.second).second);
+    // slots 0..m-1, pages ascending with the slot, and above every earlier chunk's pages
+    CHECK((int64_t)slot_page.size() <= C);
+    int32_t expect_slot = 0;
+    int64_t runs = 0;
+    for (auto& kv : slot_page) {
+      CHECK(kv.first == expect_slot++);
+      CHECK(kv.second > prev_page);
+      if (kv.second != prev_page + 1 || kv.first == 0) runs++;
+      prev_page = kv.second;
+    }
+    // adjacent host pages in consecutive slots leave staging as one region: at most one
+    // region per run of adjacent pages and sub-buffer, and no two consecutive regions that
+    // could have been one copy
+    const int64_t per_run = L.layout == HC_LAYOUT_KV_SPLIT_SHARD ? 1 : L.nsub;
+    CHECK((int64_t)(c.r1 - c.r0) <= runs * per_run && (int64_t)(c.r1 - c.r0) >= runs);
+    for (size_t r = c.r0 + 1; r < c.r1; r++) {
+      const hc::Region& a = pl.regions[r - 1];
+      const hc::Region& z = pl.regions[r];
+      CHECK(!(a.dst + a.len == z.dst && a.src + a.len == z.src));
+    }
     // the region list of this chunk, executed
     for (size_t r = c.r0; r < c.r1; r++) {
       const hc::Region& g = pl.regions[r];
@@ -138,16 +185,11 @@ static void run_case(const Shape& sh, const std::vector<int64_t>& h, int64_t chu
       memcpy(g.dst, g.src, (size_t)g.len);
     }
   }
-  // split-page tokens: exactly the unstaged ones, in list order
-  CHECK(nz == (int64_t)expect_z.size());
-  for (int64_t k = 0; k < nz; k++) CHECK(ztok[(size_t)k] == expect_z[(size_t)k]);
+  CHECK(pl.max_chunk_slots() <= C);
   for (int64_t k = 0; k < nz; k++) {
     const int64_t t = h[(size_t)ztok[(size_t)k]];
     write_row(L, host.data(), t / L.P, (int)(t % L.P));
   }
-  // pads of partly named shards: exactly those pages, each once per chunk it appears in
-  std::set<int64_t> got_pads(pads.begin(), pads.begin() + npads);
-  CHECK(got_pads == expect_pads);
   for (int64_t k = 0; k < npads; k++)
     memset(host.data() + pads[(size_t)k] * L.stride + L.payload, 0, (size_t)(L.stride - L.payload));
   // the host pool now holds the named rows, pads of named shards, and nothing else
@@ -172,9 +214,9 @@ static void run_case(const Shape& sh, const std::vector<int64_t>& h, int64_t chu
   std::vector<int64_t> dp((size_t)std::max<int64_t>(n, 1));
   const int64_t k = pl.distinct_pages(h.data(), n, dp.data());
   std::vector<int64_t> order;
-  std::set<int64_t> seen;
+  std::set<int64_t> seen_pages;
   for (int64_t t : h)
-    if (seen.insert(t / L.P).second) order.push_back(t / L.P);
+    if (seen_pages.insert(t / L.P).second) order.push_back(t / L.P);
   CHECK(k == (int64_t)order.size());
   for (int64_t i = 0; i < k; i++) CHECK(dp[(size_t)i] == order[(size_t)i]);
 }

@@ -176,3 +176,51 @@ def test_no_alloc_write_back_refusals():
         if staged is not None:
             staged.close()
         pair.close()
+
+
+@pytest.mark.gpu
+def test_no_alloc_write_back_reports_bad_device_rows():
+    """The kernels range-check every device slot: an out-of-range slot is skipped and reported
+    (HC_ERR_DEVICE with its list position) at the next sync, and every other row lands; with
+    HC_FLAG_VALIDATE a page-block list whose rows do not form one whole device page is reported
+    the same way."""
+    shape = SHAPES[0]
+    say("[noalloc] device-side reports")
+    pair = Pair(shape, seed=14)
+    try:
+        rig = pair.rig
+        h, d = burst(shape, 6, 500)
+        bad_at = 7
+        d_bad = d.copy()
+        d_bad[bad_at] = shape.device_slots + 5  # out of range
+        pair.lists.np.view(np.int64)[:h.size] = h
+        dev0 = rig.dev_np()
+        torch.cuda.synchronize()
+        pair.pool_b.write_back_all_layers_noalloc(cuda_i64(d_bad), pair.lists, h.size)
+        with pytest.raises(B.HcError) as e:
+            pair.pool_b.sync()
+        assert e.value.code == B.HC_ERR_DEVICE and f"position {bad_at}" in str(e.value)
+        keep = np.arange(h.size) != bad_at
+        want = np.full(pair.host_b.np.size, FILL, dtype=np.uint8)
+        O.write_back(rig.geom, dev0, want, d[keep], h[keep])
+        assert_bytes_equal(pair.host_b.np, want, "rows other than the bad one")
+        pair.pool_b.sync()  # the report was cleared
+    finally:
+        pair.close()
+    blk = SHAPES[2]
+    rig = Rig(blk, seed=15, flags=B.HC_FLAG_VALIDATE)
+    lists = B.HostBuffer(8 * MAX)
+    try:
+        h, d = burst(blk, 3, 600)
+        P = blk.page_size
+        d_mis = d.copy()
+        d_mis[P:2 * P] = d[P:2 * P] + 1 if d[2 * P - 1] + 1 < blk.device_slots else d[P:2 * P] - 1  # page 2 shifted
+        lists.np.view(np.int64)[:h.size] = h
+        torch.cuda.synchronize()
+        rig.pool.write_back_all_layers_noalloc(cuda_i64(d_mis), lists, h.size)
+        with pytest.raises(B.HcError) as e:
+            rig.pool.sync()
+        assert e.value.code == B.HC_ERR_DEVICE and "whole device page" in str(e.value)
+    finally:
+        lists.free()
+        rig.close()
