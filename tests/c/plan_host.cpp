@@ -266,7 +266,9 @@ static void validate_rejects() {
   CHECK(pl.validate(neg.data(), 1, msg, sizeof(msg)) == HC_ERR_INVALID);
 }
 
-int main() {
+int main(int argc, char** argv) {
+  // optional: random cases per (shape, chunk size); 40 by default
+  const int trials = argc > 1 ? atoi(argv[1]) : 40;
   validate_rejects();
   const std::vector<Shape> shapes = {
       {3, 4, 24, HC_LAYOUT_PAGE_FIRST, {{HC_TOKEN_ROWS, 32}, {HC_TOKEN_ROWS, 16}}, 4096},
@@ -281,7 +283,7 @@ int main() {
   for (size_t s = 0; s < shapes.size(); s++) {
     const bool blocks = shapes[s].subs.back().first == HC_PAGE_BLOCKS;
     for (int64_t chunk : {1, 2, 3, 5, 64}) {
-      for (int trial = 0; trial < 40; trial++) {
+      for (int trial = 0; trial < trials; trial++) {
         g_case = (int)(s * 1000 + chunk * 100 + trial);
         const bool interleave = !blocks && trial % 3 == 2;
         run_case(shapes[s], random_list(rng, shapes[s], blocks || trial % 4 == 0, interleave), chunk);
