@@ -402,6 +402,22 @@ def gather_dram_bound(B, torch, np, W, make_pool, stream, shape, burst, chunk_pa
     spool.write_back_all_layers(d_t, h)
     spool.sync()
     res = {}
+    # the runtime's plain device-to-device copy of the same bytes under the same condition
+    # (after the same 1 GiB write), for reference
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    e0, e1 = B.HipEvent(timing=True), B.HipEvent(timing=True)
+    cms = []
+    for k in range(reps):
+        with torch.cuda.stream(stream):
+            flush.fill_(k & 0xFF)
+            e0.record(stream)
+            dst.copy_(src)
+            e1.record(stream)
+        e1.synchronize()
+        cms.append(e0.elapsed_ms(e1))
+    res["plain_copy_same_condition_GBps"] = round(2 * nbytes / (float(np.median(cms)) * 1e-3) / 1e9, 1)
+    del src, dst
     for name, flushed in (("dram", True), ("back_to_back", False)):
         spool.kernel_time(0, reset=True)
         for k in range(reps):
@@ -417,6 +433,26 @@ def gather_dram_bound(B, torch, np, W, make_pool, stream, shape, burst, chunk_pa
     spool.close()
     del flush
     return {"chunk_pages": len(pick), "bytes_per_launch": 2 * nbytes, "flush_bytes": 1 << 30, **res}
+
+
+def plain_copy_dram(B, torch, np, stream, nbytes: int = 2 << 30, reps: int = 5) -> float:
+    """The runtime's plain device-to-device copy (torch copy_) of 2 GiB, 8 times the Infinity
+    Cache, so both sides stream from and to DRAM: a reference for what this memory system
+    copies (read + write bytes over the copy's time, best of `reps`)."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    e0, e1 = B.HipEvent(timing=True), B.HipEvent(timing=True)
+    best = None
+    for _ in range(reps):
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            dst.copy_(src)
+            e1.record(stream)
+        e1.synchronize()
+        ms = e0.elapsed_ms(e1)
+        best = ms if best is None else min(best, ms)
+    del src, dst
+    return round(2 * nbytes / (best * 1e-3) / 1e9, 1)
 
 
 def _cpu_model() -> str:
@@ -876,6 +912,7 @@ def staged_probe(B, torch, np, W, make_pool, stream, shape, burst, d_t, h_np, li
     g_gbs = 2 * gbytes * reps / (ms_g * 1e-3) / 1e9  # read + write of every gathered byte
     gtraffic = counter_traffic(shape.name, "k_gather_stage")
     dram = gather_dram_bound(B, torch, np, W, make_pool, stream, shape, burst, chunk_pages)
+    copy_ref = plain_copy_dram(B, torch, np, stream)
     d_gbs = dram["dram"]["achieved"]
     dtraffic = counter_traffic(shape.name, "k_gather_stage_dram")
     roofline_hbm = {"bound": "hbm", "kernel": "k_gather_stage (staged lf->pf relayout, one chunk, all layers)",
@@ -891,10 +928,12 @@ def staged_probe(B, torch, np, W, make_pool, stream, shape, burst, d_t, h_np, li
                                    "avg_launch_ms": dram["dram"]["avg_launch_ms"],
                                    "bytes_per_launch": dram["bytes_per_launch"], "chunk_pages": dram["chunk_pages"],
                                    "back_to_back_achieved": dram["back_to_back"]["achieved"],
+                                   "plain_copy_same_condition_GBps": dram["plain_copy_same_condition_GBps"],
                                    "traffic": dtraffic["bytes"] if dtraffic else None,
                                    "method": "one chunk of wholly named pages per call, each call after a 1 GiB "
                                              "write on the copy stream (rows read from DRAM, staging writes "
                                              "displace dirty lines)"},
+                    "plain_copy_dram_GBps": copy_ref,
                     "meets_70pct_of_peak": {"as_run": g_gbs >= 0.7 * HBM_PEAK_GBS,
                                             "dram_bound": d_gbs >= 0.7 * HBM_PEAK_GBS}}
     staged = {"write_back_GBps": round(link_bytes / (float(np.median(sms)) * 1e-3) / 1e9, 3),
