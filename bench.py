@@ -85,6 +85,8 @@ def parse():
                          "(one chunk per call, each after a 1 GiB write on the copy stream)")
     ap.add_argument("--h2h", action="store_true",
                     help="instead: time host-to-host shard dump/load of the shard workload with 1..16 CPU workers")
+    ap.add_argument("--compute-streams", type=int, default=5,
+                    help="with --beside-compute: compute streams to try beside each write-back mode")
     ap.add_argument("--max-pinned-gib", type=float, default=64.0,
                     help="cap on the pinned host pool; a larger pool keeps the burst and shrinks the page count")
     ap.add_argument("--exchange-only", action="store_true",
@@ -618,12 +620,14 @@ def layer_pipeline(B, torch, pool, shape, h_t, d2_t, n, stream, layer_events, ma
     return res
 
 
-def write_back_overlap(B, torch, np, pools, d_t, h_np):
-    """A whole write-back burst next to independent compute (bf16 4096^3 matmuls on a
-    second stream, about as long as the burst), per write-back mode.  overlap =
-    (write-back + compute - both) / min(write-back, compute); compute_slowdown = how
-    much longer the matmuls take beside the burst than alone."""
-    consumer = torch.cuda.Stream()
+def write_back_overlap(B, torch, np, pools, d_t, h_np, consumers: int = 3):
+    """A whole write-back burst next to independent compute (bf16 4096^3 matmuls on another
+    stream, about as long as the burst), per write-back mode, once for each of `consumers`
+    compute streams: HIP maps a process's streams onto GPU_MAX_HW_QUEUES hardware queues, so
+    whether a compute stream shares a queue with a stream of the write-back (and then waits
+    behind it) depends on the stream.  overlap = (write-back + compute - both) /
+    min(write-back, compute) per compute stream; `overlap` is their median."""
+    streams = [torch.cuda.Stream() for _ in range(consumers)]
     a = torch.randn(4096, 4096, device="cuda", dtype=torch.bfloat16)
     w = torch.randn(4096, 4096, device="cuda", dtype=torch.bfloat16)
     out = torch.empty(4096, 4096, device="cuda", dtype=torch.bfloat16)
@@ -635,27 +639,34 @@ def write_back_overlap(B, torch, np, pools, d_t, h_np):
         torch.cuda.synchronize()
         return time.perf_counter() - t0
 
-    def matmuls(k):
-        with torch.cuda.stream(consumer):
+    def matmuls(cs, k):
+        with torch.cuda.stream(cs):
             for _ in range(k):
                 torch.matmul(a, w, out=out)
     for _ in range(3):
-        timed(lambda: matmuls(1))
-    per_mm = float(np.median([timed(lambda: matmuls(1)) for _ in range(5)]))
-    res = {"compute": "bf16 matmul 4096^3 repeated on a second stream, no dependency on the burst"}
+        timed(lambda: matmuls(streams[0], 1))
+    per_mm = float(np.median([timed(lambda: matmuls(streams[0], 1)) for _ in range(5)]))
+    res = {"compute": "bf16 matmul 4096^3 repeated on another stream, no dependency on the burst",
+           "compute_streams": consumers,
+           "hw_queues": os.environ.get("GPU_MAX_HW_QUEUES", "4 (HIP default)")}
     for mode, p in pools.items():
         p.write_back_all_layers(d_t, h_np)
         t_wb = float(np.median([timed(lambda: p.write_back_all_layers(d_t, h_np)) for _ in range(3)]))
         k = max(1, int(round(t_wb / max(per_mm, 1e-6))))
-        t_c = float(np.median([timed(lambda: matmuls(k)) for _ in range(3)]))
+        rows = []
+        for cs in streams:
+            t_c = float(np.median([timed(lambda: matmuls(cs, k)) for _ in range(3)]))
 
-        def both():
-            p.write_back_all_layers(d_t, h_np)
-            matmuls(k)
-        t_both = float(np.median([timed(both) for _ in range(3)]))
-        res[mode] = {"write_back_ms": round(1e3 * t_wb, 3), "compute_ms": round(1e3 * t_c, 3),
-                     "both_ms": round(1e3 * t_both, 3), "matmuls": k,
-                     "overlap": round((t_wb + t_c - t_both) / min(t_wb, t_c), 4)}
+            def both():
+                p.write_back_all_layers(d_t, h_np)
+                matmuls(cs, k)
+            t_both = float(np.median([timed(both) for _ in range(3)]))
+            rows.append({"compute_ms": round(1e3 * t_c, 3), "both_ms": round(1e3 * t_both, 3),
+                         "overlap": round((t_wb + t_c - t_both) / min(t_wb, t_c), 4)})
+        ovs = [r["overlap"] for r in rows]
+        res[mode] = {"write_back_ms": round(1e3 * t_wb, 3), "matmuls": k, "overlap": float(np.median(ovs)),
+                     "overlap_by_compute_stream": ovs, "compute_ms": rows[0]["compute_ms"],
+                     "both_ms": [r["both_ms"] for r in rows]}
         log(f"[bench] write-back beside compute, {mode}: {res[mode]}")
     return res
 
@@ -1145,7 +1156,7 @@ def measure(args):
     if args.beside_compute:
         pool.close()
         pools = {"zerocopy": make_pool(B.HC_MODE_ZEROCOPY, flags=0), "staged": make_pool(B.HC_MODE_STAGED, flags=0)}
-        res = write_back_overlap(B, torch, np, pools, d_t, h_np)
+        res = write_back_overlap(B, torch, np, pools, d_t, h_np, consumers=args.compute_streams)
         for p in pools.values():
             p.close()
         print(json.dumps({"beside_compute": res, "workload": shape.name,

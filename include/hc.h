@@ -119,7 +119,11 @@ enum { HC_LAYOUT_PAGE_FIRST = 0, HC_LAYOUT_KV_SPLIT_SHARD = 1, HC_LAYOUT_PAGE_FI
  * while its kernel saturates the link, compute kernels on other streams slow down
  * until they barely overlap it; staged write-back runs ~12 % slower alone and leaves
  * concurrent compute almost untouched, because the copy engines carry its host
- * writes.  Zero-copy load-back overlaps compute well on its default grid. */
+ * writes.  Zero-copy load-back overlaps compute well on its default grid.  Either way
+ * the overlap needs the compute on a stream that does not share a hardware queue with
+ * the copy stream: HIP maps a process's streams onto GPU_MAX_HW_QUEUES queues (4 by
+ * default), and work on a shared queue runs in that queue's order (measured: with 4
+ * queues one compute stream in five waited behind the whole burst; with 16, none). */
 enum { HC_MODE_AUTO = 0, HC_MODE_STAGED = 1, HC_MODE_ZEROCOPY = 2 };
 /* Pool flags. */
 enum { HC_FLAG_VALIDATE = 1, HC_FLAG_PROFILE = 2 };

@@ -165,7 +165,12 @@ def test_header_constants_match_the_binding():
     text = open(HEADER).read()
     defs = {m.group(1): int(m.group(2)) for m in re.finditer(r"#define\s+(HC_[A-Z0-9_]+)\s+(\d+)\b", text)}
     assert {"HC_MAX_SUBBUFS", "HC_DUPLEX_LOAD_BACK_CTAS", "HC_NOALLOC_MAX_TOKENS"} <= set(defs)
+    # enumerators too (modes, layouts, flags, status codes)
+    body = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    for m in re.finditer(r"\b(HC_[A-Z0-9_]+)\s*=\s*(-?\d+)", body):
+        defs[m.group(1)] = int(m.group(2))
+    assert {"HC_FLAG_PROFILE", "HC_MODE_STAGED", "HC_ERR_DEVICE"} <= set(defs)
     shared = [k for k in defs if hasattr(B, k)]
-    assert "HC_DUPLEX_LOAD_BACK_CTAS" in shared
+    assert {"HC_DUPLEX_LOAD_BACK_CTAS", "HC_FLAG_PROFILE", "HC_LAYOUT_KV_SPLIT_SHARD", "HC_ERR_DEVICE"} <= set(shared)
     for k in shared:
         assert getattr(B, k) == defs[k], k

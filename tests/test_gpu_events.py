@@ -258,6 +258,41 @@ def test_validate_flag_reports_misaligned_page_blocks_on_write_back(mode):
 
 
 @pytest.mark.gpu
+@pytest.mark.parametrize("mode", [B.HC_MODE_ZEROCOPY, B.HC_MODE_STAGED], ids=["zerocopy", "staged"])
+def test_done_event_covers_back_to_back_write_backs(mode):
+    """Three write-back bursts enqueued back to back, no synchronization between them, over
+    host pages that overlap from one burst to the next, each with a page named in part.
+    Waiting on the last burst's done event alone (no stream or pool sync) must leave the
+    whole host pool equal to the oracle's after all three in order: the event covers every
+    copy and kernel of its burst, and a burst's host writes land after those of the burst
+    before it (staged: the next burst's gathers into the shared staging chunk come after
+    the copies that read it)."""
+    say(f"[events] back-to-back write-backs, mode {mode}")
+    shape = W.PoolShape("event_chain", 3, 16, ((T, 1024), (T, 512)), 16384, 96)
+    rig = Rig(shape, seed=33, write_back_mode=mode, staging_pages=6 if mode == B.HC_MODE_STAGED else 0)
+    try:
+        dev0 = rig.dev_np()
+        want = rig.host.np.copy()
+        keep, events = [], []
+        for k in range(3):
+            pages = W.host_pages(40 + k, shape.host_pages, 40)
+            h = W.whole_page_tokens(pages, shape.page_size)
+            h = h[: h.size - 5]  # the last page named in part: zero-copy rows after the copies
+            d = W.permutation_slots(50 + k, shape.device_slots, h.size)
+            d_t = cuda_i64(d)
+            ev = B.HipEvent()
+            rig.pool.write_back_all_layers(d_t, h, ev)
+            keep.append(d_t)
+            events.append(ev)
+            O.write_back(rig.geom, dev0, want, d, h)
+        events[-1].synchronize()
+        assert np.array_equal(rig.host.np, want), "host pool after the last burst's event differs from the oracle's"
+        rig.pool.sync()
+    finally:
+        rig.close()
+
+
+@pytest.mark.gpu
 def test_block_pool_write_back_rejects_out_of_order_pages():
     """Whole pages whose rows are interleaved or out of order are refused on the CPU,
     before anything is enqueued: the kernels find a page's block at its row-0 position."""
