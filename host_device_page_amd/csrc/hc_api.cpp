@@ -121,6 +121,7 @@ struct hc_pool {
   int64_t kind_launches[kKinds] = {};
   double kind_ms[kKinds] = {};
   hc_pool_stats stats{};
+  std::vector<int64_t> wg_load;       // [max_ctas] host scratch of the zero-copy launchers' tile sizing
   int64_t row_bytes_per_layer = 0;    // sum of token-row sub-buffers' elem_bytes
   int64_t block_bytes_per_layer = 0;  // sum of page-block sub-buffers' elem_bytes
 };
@@ -561,6 +562,11 @@ int hc_pool_create(const hc_pool_desc* desc, hc_pool** out) {
   }
   p->flags = desc->flags;
   p->max_ctas = desc->max_ctas > 0 ? desc->max_ctas : kDefaultMaxCtas;
+  try {
+    p->wg_load.assign((size_t)p->max_ctas, 0);
+  } catch (...) {
+    return bail(set_err(HC_ERR_NOMEM, "host scratch allocation failed"));
+  }
   // memory kinds
   if (L.H > 0) {
     void* dptr = nullptr;
@@ -784,14 +790,15 @@ int hc_write_back_all_layers(hc_pool* p, const int64_t* device_idx, const int64_
     }
     if (nz > 0) {
       Timer t(p, 1);
-      e = hc::launch_zc_write(p->geom, device_idx, d_hidx, d_ztok, nz, p->host, p->d_err, p->max_ctas, t.ev,
-                              p->stream);
+      e = hc::launch_zc_write(p->geom, device_idx, d_hidx, d_ztok, nz, p->host, p->d_err, p->max_ctas,
+                              p->wg_load.data(), t.ev, p->stream);
       t.done(e == hipSuccess);
       if (e != hipSuccess) return finish(set_err(HC_ERR_HIP, "zero-copy launch failed: %s", hipGetErrorString(e)));
     }
   } else {
     Timer t(p, 1);
-    e = hc::launch_zc_write(p->geom, device_idx, d_hidx, nullptr, n, p->host, p->d_err, p->max_ctas, t.ev, p->stream);
+    e = hc::launch_zc_write(p->geom, device_idx, d_hidx, nullptr, n, p->host, p->d_err, p->max_ctas,
+                            p->wg_load.data(), t.ev, p->stream);
     t.done(e == hipSuccess);
     if (e != hipSuccess) return finish(set_err(HC_ERR_HIP, "zero-copy launch failed: %s", hipGetErrorString(e)));
   }
@@ -846,8 +853,8 @@ int hc_write_back_all_layers_noalloc(hc_pool* p, const int64_t* device_idx, cons
   const Layout& L = p->lay;
   hipError_t e = hipMemcpyAsync(scratch, host_idx, (size_t)n * sizeof(int64_t), hipMemcpyHostToDevice, p->stream);
   if (e != hipSuccess) return finish(set_err(HC_ERR_HIP, "host list copy failed: %s", hipGetErrorString(e)));
-  e = hc::launch_zc_write(p->geom, device_idx, scratch, nullptr, n, p->host, p->d_err, p->max_ctas, hc::LaunchTimer{},
-                          p->stream);
+  e = hc::launch_zc_write(p->geom, device_idx, scratch, nullptr, n, p->host, p->d_err, p->max_ctas,
+                          p->wg_load.data(), hc::LaunchTimer{}, p->stream);
   if (e != hipSuccess) return finish(set_err(HC_ERR_HIP, "zero-copy launch failed: %s", hipGetErrorString(e)));
   if (L.layout == HC_LAYOUT_KV_SPLIT_SHARD && L.stride > L.payload) {
     e = hc::launch_zero_pads_runs(p->host, scratch, n, L.P, L.H, L.stride, L.payload, L.stride - L.payload, p->stream);
@@ -890,7 +897,8 @@ int hc_load_back_layer(hc_pool* p, int32_t layer, const int64_t* host_idx, const
   hipError_t e;
   {
     Timer t(p, 2, !stream_capturing(p));
-    e = hc::launch_zc_read(p->geom, layer, host_idx, device_idx, n, p->host, p->d_err, p->max_ctas, t.ev, p->stream);
+    e = hc::launch_zc_read(p->geom, layer, host_idx, device_idx, n, p->host, p->d_err, p->max_ctas,
+                           p->wg_load.data(), t.ev, p->stream);
     t.done(e == hipSuccess);
   }
   if (e != hipSuccess) return finish(set_err(HC_ERR_HIP, "load-back launch failed: %s", hipGetErrorString(e)));

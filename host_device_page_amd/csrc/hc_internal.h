@@ -100,11 +100,13 @@ hipError_t launch_gather_stage(const Geom& g, const int64_t* dev_idx, const int6
                                const int32_t* perm, const int32_t* srow, int64_t t0, int64_t count,
                                uint8_t* staging, int32_t* err, int32_t num_cus, const LaunchTimer& t,
                                hipStream_t stream);
+// The zero-copy launchers size their tiles on the host; wg_load is host scratch of at
+// least max_ctas entries for that (the caller's, so a launch allocates nothing).
 hipError_t launch_zc_write(const Geom& g, const int64_t* dev_idx, const int64_t* host_idx,
                            const int32_t* tok_list, int64_t count, uint8_t* host, int32_t* err,
-                           int32_t max_ctas, const LaunchTimer& t, hipStream_t stream);
+                           int32_t max_ctas, int64_t* wg_load, const LaunchTimer& t, hipStream_t stream);
 hipError_t launch_zc_read(const Geom& g, int32_t layer, const int64_t* host_idx, const int64_t* dev_idx,
-                          int64_t n, const uint8_t* host, int32_t* err, int32_t max_ctas,
+                          int64_t n, const uint8_t* host, int32_t* err, int32_t max_ctas, int64_t* wg_load,
                           const LaunchTimer& t, hipStream_t stream);
 hipError_t launch_zero_pads(uint8_t* base, const int64_t* pages, int64_t npages, int64_t stride,
                             int64_t off, int64_t bytes, const LaunchTimer& t, hipStream_t stream);

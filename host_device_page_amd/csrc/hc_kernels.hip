@@ -29,8 +29,6 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include <vector>
-
 #include "hc_internal.h"
 
 namespace hc {
@@ -610,8 +608,8 @@ constexpr int kMaxTileShift = 6;
 constexpr int64_t kUnitIntakeBytes = 8192;  // the intake's cost, in bytes of copying
 
 static int64_t busiest_workgroup_bytes(const Geom& g, int64_t count, int bs, int tile_n, int bt, int64_t mult,
-                                       int64_t grid) {
-  std::vector<int64_t> load((size_t)grid, 0);
+                                       int64_t grid, int64_t* load) {
+  for (int64_t w = 0; w < grid; w++) load[w] = 0;
   int64_t u = 0;
   for (int pass = 0; pass < 2; pass++) {
     for (int b = 0; b < g.nsub; b++) {
@@ -623,17 +621,17 @@ static int64_t busiest_workgroup_bytes(const Geom& g, int64_t count, int bs, int
         int64_t items = pos - j0 < t ? pos - j0 : t;
         if (s.gran == HC_PAGE_BLOCKS && bs <= 1) items = (items + g.P - 1) / g.P;  // one block per page
         const int64_t bytes = items * s.elem + kUnitIntakeBytes;
-        for (int64_t l = 0; l < mult; l++) load[(size_t)(u++ % grid)] += bytes;
+        for (int64_t l = 0; l < mult; l++) load[u++ % grid] += bytes;
       }
     }
   }
   int64_t most = 0;
-  for (int64_t x : load) most = x > most ? x : most;
+  for (int64_t w = 0; w < grid; w++) most = load[w] > most ? load[w] : most;
   return most;
 }
 
 static int tile_shift_for(const Geom& g, int64_t count, int blk_stride, int blk_tile, int64_t mult,
-                          int32_t max_ctas) {
+                          int32_t max_ctas, int64_t* wg_load) {
   // under the block stride, page blocks have their own units (block_tile_for spreads them)
   auto row_units = [&](int tile_n) {
     int64_t n = 0;
@@ -650,7 +648,7 @@ static int tile_shift_for(const Geom& g, int64_t count, int blk_stride, int blk_
     if (shift > 0 && row_units(kTile >> (shift - 1)) >= 4 * ctas) break;  // finer tiles only add intakes
     const int64_t units = zc_units(g, count, blk_stride, kTile >> shift, blk_tile, mult);
     const int64_t grid = units < ctas ? units : ctas;
-    const int64_t most = busiest_workgroup_bytes(g, count, blk_stride, kTile >> shift, blk_tile, mult, grid);
+    const int64_t most = busiest_workgroup_bytes(g, count, blk_stride, kTile >> shift, blk_tile, mult, grid, wg_load);
     if (best_bytes < 0 || most < best_bytes) {
       best = shift;
       best_bytes = most;
@@ -670,12 +668,12 @@ static int block_stride(const Geom& g, bool full_list) {
 }
 
 hipError_t launch_zc_write(const Geom& g, const int64_t* dev_idx, const int64_t* host_idx, const int32_t* tok_list,
-                           int64_t count, uint8_t* host, int32_t* err, int32_t max_ctas, const LaunchTimer& t,
-                           hipStream_t stream) {
+                           int64_t count, uint8_t* host, int32_t* err, int32_t max_ctas, int64_t* wg_load,
+                           const LaunchTimer& t, hipStream_t stream) {
   if (count <= 0) return hipSuccess;
   const int bs = block_stride(g, tok_list == nullptr);
   const int bt = block_tile_for(count, bs, g.L, max_ctas);
-  const int shift = tile_shift_for(g, count, bs, bt, g.L, max_ctas);
+  const int shift = tile_shift_for(g, count, bs, bt, g.L, max_ctas, wg_load);
   const int64_t units = zc_units(g, count, bs, kTile >> shift, bt, g.L);
   const int64_t grid = units < max_ctas ? units : max_ctas;
   return launch(k_zc_write, dim3((unsigned)grid), t, stream, g, dev_idx, host_idx, tok_list, count, host, err, units,
@@ -683,12 +681,12 @@ hipError_t launch_zc_write(const Geom& g, const int64_t* dev_idx, const int64_t*
 }
 
 hipError_t launch_zc_read(const Geom& g, int32_t layer, const int64_t* host_idx, const int64_t* dev_idx, int64_t n,
-                          const uint8_t* host, int32_t* err, int32_t max_ctas, const LaunchTimer& t,
+                          const uint8_t* host, int32_t* err, int32_t max_ctas, int64_t* wg_load, const LaunchTimer& t,
                           hipStream_t stream) {
   if (n <= 0) return hipSuccess;
   const int bs = block_stride(g, true);
   const int bt = block_tile_for(n, bs, 1, max_ctas);
-  const int shift = tile_shift_for(g, n, bs, bt, 1, max_ctas);
+  const int shift = tile_shift_for(g, n, bs, bt, 1, max_ctas, wg_load);
   const int64_t units = zc_units(g, n, bs, kTile >> shift, bt, 1);
   const int64_t grid = units < max_ctas ? units : max_ctas;
   return launch(k_zc_read, dim3((unsigned)grid), t, stream, g, layer, host_idx, dev_idx, n, host, err, units, shift,

@@ -272,7 +272,8 @@ int hc_write_back_all_layers(hc_pool* pool, const int64_t* device_idx, const int
  * pinned memory in the middle of their work (tight serving loops, harnesses that
  * forbid hipMalloc): hc_write_back_all_layers grows its plan buffers with
  * hipHostMalloc / hipMalloc when a burst is larger than any before it (waiting
- * for the copy stream first); this variant never calls an allocator.  Its plan, a
+ * for the copy stream first); this variant never calls an allocator (device,
+ * pinned or host heap: its host-side scratch is the pool's, sized at creation).  Its plan, a
  * device copy of host_idx, lives in a fixed array of HC_NOALLOC_MAX_TOKENS int64
  * entries (2 MiB) that every GPU the library runs on holds from the library's load
  * until the process ends.  Every call on one GPU shares that GPU's array: calls
