@@ -529,6 +529,15 @@ int hc_pool_create(const hc_pool_desc* desc, hc_pool** out) {
   *out = nullptr;
   int rc = hc_desc_check(desc);
   if (rc != HC_OK) return rc;
+  {
+    // set-up copies the layer tables on the copy stream and waits for it: not inside a capture
+    hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing((hipStream_t)desc->copy_stream, &st) != hipSuccess) {
+      (void)hipGetLastError();  // an invalid stream is reported below
+    } else if (st != hipStreamCaptureStatusNone) {
+      return refuse_capture("hc_pool_create", "its set-up copies to the device and waits for the copy stream");
+    }
+  }
   hc_pool* p = new (std::nothrow) hc_pool();
   if (!p) return set_err(HC_ERR_NOMEM, "pool allocation failed");
   char msg[256];
@@ -638,6 +647,8 @@ int hc_pool_destroy(hc_pool* p) {
   if (p->users.load() > 0)
     return set_err(HC_ERR_INVALID, "%lld loader(s) or captured graph(s) still use the pool; destroy them first",
                    (long long)p->users.load());
+  if (p->d_tables && stream_capturing(p))
+    return refuse_capture("hc_pool_destroy", "it waits for the copy stream before freeing (nothing was freed)");
   int rc = HC_OK;
   if (p->stream || p->d_tables) {
     if (hipStreamSynchronize(p->stream) != hipSuccess) rc = set_err(HC_ERR_HIP, "stream sync failed in destroy");

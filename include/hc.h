@@ -82,7 +82,9 @@
  *     stream is capturing, hc_write_back_all_layers (its plan is built on the CPU
  *     for each call, so a replay would reuse a stale plan), hc_pool_sync and
  *     hc_round_trip_check (both wait for the stream) return HC_ERR_UNSUPPORTED
- *     and enqueue nothing.
+ *     and enqueue nothing; so do hc_pool_create on a copy stream that is
+ *     capturing (its set-up copies and waits) and hc_pool_destroy (it waits for
+ *     the stream; nothing is freed, destroy the pool after the capture ends).
  */
 #ifndef HC_H
 #define HC_H

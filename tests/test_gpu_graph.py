@@ -239,8 +239,10 @@ def test_pool_outlives_its_graphs_and_loaders():
 @pytest.mark.gpu
 def test_caller_capture_rules_on_a_profiling_pool():
     """A caller's own capture on the pool's stream.  The write-back (its plan is built on the
-    CPU per call), hc_pool_sync and hc_round_trip_check (they wait for the stream) are refused
-    with HC_ERR_UNSUPPORTED and leave the capture usable; per-layer load-backs and a layer pack
+    CPU per call), hc_pool_sync and hc_round_trip_check (they wait for the stream), creating a
+    pool on the capturing stream (its set-up copies and waits) and destroying one (it waits
+    before freeing) are refused with HC_ERR_UNSUPPORTED and leave the capture usable (the
+    refused pool is destroyed after the capture); per-layer load-backs and a layer pack
     recorded on a profiling pool are not timed, and every replay (host pool rewritten between
     replays) matches the oracle."""
     shape = SHAPES[1]
@@ -252,13 +254,16 @@ def test_caller_capture_rules_on_a_profiling_pool():
         h_t, d_t = cuda_i64(h), cuda_i64(d)
         staging = torch.zeros(rig.pool.layer_pack_bytes(d.size), dtype=torch.uint8, device="cuda")
         rig.pool.kernel_time(B.KIND_ZC_READ, reset=True)
+        other = rig.pool.sibling(rig.stream)
         torch.cuda.synchronize()
         refused = {}
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph, stream=rig.stream, capture_error_mode="thread_local"):
             for what, call in (("write-back", lambda: rig.pool.write_back_all_layers(d_t, h)),
                                ("sync", rig.pool.sync),
-                               ("round-trip check", lambda: rig.pool.round_trip_check(d_t, d_t))):
+                               ("round-trip check", lambda: rig.pool.round_trip_check(d_t, d_t)),
+                               ("pool create", lambda: rig.pool.sibling(rig.stream)),
+                               ("pool destroy", other.close)):
                 try:
                     call()
                 except B.HcError as e:
@@ -267,7 +272,10 @@ def test_caller_capture_rules_on_a_profiling_pool():
                 rig.pool.load_back_layer(l, h_t, d_t)
             rig.pool.layer_pack(L - 1, d_t, staging)
         assert refused == {"write-back": B.HC_ERR_UNSUPPORTED, "sync": B.HC_ERR_UNSUPPORTED,
-                           "round-trip check": B.HC_ERR_UNSUPPORTED}, refused
+                           "round-trip check": B.HC_ERR_UNSUPPORTED, "pool create": B.HC_ERR_UNSUPPORTED,
+                           "pool destroy": B.HC_ERR_UNSUPPORTED}, refused
+        assert other.handle.value, "the refused destroy freed the pool"
+        other.close()
         torch.cuda.synchronize()
         for replay in range(3):
             randomize_host(rig, 70 + replay)
