@@ -72,6 +72,15 @@ constexpr int32_t kDefaultMaxCtas = 16;
 // fits stays cache-resident between the two (measured: 32 x 8 MiB page images
 // gather at 5.9 TB/s, 64 at 5.4 TB/s, 128 at 5.1 TB/s).
 constexpr int64_t kStagingChunkTarget = (int64_t)256 << 20;
+// Which engine runs a hipMemcpyAsync is the runtime's choice, and its device-to-host
+// copies follow the stream's recent copies: rocprofv3 kernel + memory-copy traces on MI355X
+// showed them as copy kernels on the CUs on a stream whose last host-to-device copy was 16
+// KiB or smaller (or absent), and on the copy engines right after one of 64 KiB or more, a
+// kernel in between or not.  A staged burst's plan upload is that copy, so it is padded to
+// at least this size: the region copies that follow go to the copy engines for small
+// bursts too (unpadded, a 512-token burst's 14 KB upload left every region copy of the
+// bursts after the first on the CUs).
+constexpr int64_t kCopyEngineUploadBytes = (int64_t)256 << 10;
 
 struct PlanBuf {
   uint8_t* h = nullptr;   // pinned
@@ -739,7 +748,7 @@ int hc_write_back_all_layers(hc_pool* p, const int64_t* device_idx, const int64_
   const int64_t o_ztok = align16(o_srow + 4 * n);
   const int64_t o_perm = align16(o_ztok + 4 * n);
   const int64_t bytes = align16(o_perm + 4 * n);
-  rc = plan_reserve(p, bytes);
+  rc = plan_reserve(p, staged ? std::max(bytes, kCopyEngineUploadBytes) : bytes);
   if (rc != HC_OK) return finish(rc);
   PlanBuf& pb = p->plan[p->plan_cur];
   int64_t* hidx = (int64_t*)(pb.h + o_hidx);
@@ -754,7 +763,8 @@ int hc_write_back_all_layers(hc_pool* p, const int64_t* device_idx, const int64_
   } else if (L.layout == HC_LAYOUT_KV_SPLIT_SHARD && L.stride > L.payload) {
     npads = p->planner.distinct_pages(host_idx, n, pads);
   }
-  const int64_t upload = staged ? bytes : align16(o_pads + 8 * npads);
+  // staged: padded so the region copies below go to the copy engines (the padding is not read)
+  const int64_t upload = staged ? std::max(bytes, kCopyEngineUploadBytes) : align16(o_pads + 8 * npads);
   rc = plan_upload(p, upload);
   if (rc != HC_OK) return finish(rc);
   const int64_t* d_hidx = (const int64_t*)(pb.d + o_hidx);
