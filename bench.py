@@ -139,7 +139,7 @@ def memcpy_peak(hip, host_ptr: int, dev_ptr: int, nbytes: int, stream_ptr: int, 
 def memcpy_duplex_peak(hip, host_ptr: int, dev_ptr: int, nbytes: int, streams, reps: int = 5) -> dict:
     """hipMemcpyAsync D2H and H2D of nbytes each at the same time on two streams (host
     regions [0, nbytes) and [nbytes, 2 nbytes) of host_ptr, device likewise); best span of
-    `reps`.  The copy engines move both directions at once."""
+    `reps`: the runtime's own rate in both directions at once."""
     V = ctypes.c_void_p
     sw, sr = streams
     ev = [V() for _ in range(3)]

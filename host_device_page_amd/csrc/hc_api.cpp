@@ -72,14 +72,14 @@ constexpr int32_t kDefaultMaxCtas = 16;
 // fits stays cache-resident between the two (measured: 32 x 8 MiB page images
 // gather at 5.9 TB/s, 64 at 5.4 TB/s, 128 at 5.1 TB/s).
 constexpr int64_t kStagingChunkTarget = (int64_t)256 << 20;
-// Which engine runs a hipMemcpyAsync is the runtime's choice, and its device-to-host
-// copies follow the stream's recent copies: rocprofv3 kernel + memory-copy traces on MI355X
-// showed them as copy kernels on the CUs on a stream whose last host-to-device copy was 16
-// KiB or smaller (or absent), and on the copy engines right after one of 64 KiB or more, a
-// kernel in between or not.  A staged burst's plan upload is that copy, so it is padded to
-// at least this size: the region copies that follow go to the copy engines for small
-// bursts too (unpadded, a 512-token burst's 14 KB upload left every region copy of the
-// bursts after the first on the CUs).
+// Which engine runs a hipMemcpyAsync is the runtime's choice.  In rocprofv3 kernel +
+// memory-copy traces on MI355X its device-to-host copies ran as copy kernels on the CUs on a
+// stream whose last host-to-device copy was 16 KiB or smaller (or absent), and on the copy
+// engines right after one of 64 KiB or more, a kernel in between or not; that is not the
+// whole rule (a few small bursts still got copy kernels after a large upload).  A staged
+// burst's plan upload is that copy, so it is padded to at least this size: unpadded, every
+// region copy of a 512-token burst (a 14 KB plan) ran on the CUs; padded, most went to the
+// copy engines, and every one of the 78-layer bursts (a ~2 MB plan) did either way.
 constexpr int64_t kCopyEngineUploadBytes = (int64_t)256 << 10;
 
 struct PlanBuf {

@@ -121,7 +121,9 @@ enum { HC_LAYOUT_PAGE_FIRST = 0, HC_LAYOUT_KV_SPLIT_SHARD = 1, HC_LAYOUT_PAGE_FI
  * while its kernel saturates the link, compute kernels on other streams slow down
  * until they barely overlap it; staged write-back runs ~12 % slower alone and leaves
  * concurrent compute almost untouched, because the copy engines carry its host
- * writes.  Zero-copy load-back overlaps compute well on its default grid.  Either way
+ * writes (which engine runs a copy is the runtime's choice: the library pads each
+ * burst's plan upload to 256 KiB, after which the runtime sent the region copies to
+ * the copy engines in every traced burst of 2 MB plans and in most small ones).  Zero-copy load-back overlaps compute well on its default grid.  Either way
  * the overlap needs the compute on a stream that does not share a hardware queue with
  * the copy stream: HIP maps a process's streams onto GPU_MAX_HW_QUEUES queues (4 by
  * default), and work on a shared queue runs in that queue's order (measured: with 4
@@ -144,8 +146,8 @@ typedef struct hc_subbuf_desc {
  * its own copy stream (their rows must not overlap).  Who issues the host accesses
  * decides how the link is shared (measured on MI355X, PCIe 5.0 x16): a staged
  * write-back pool (copy engines) beside a zero-copy load-back pool whose max_ctas is
- * HC_DUPLEX_LOAD_BACK_CTAS moves both directions near 45 GB/s each, ~0.9 of what the
- * copy engines reach in both directions at once; at the default 16 the load-back keeps
+ * HC_DUPLEX_LOAD_BACK_CTAS moves both directions near 45 GB/s each, ~0.9 of what
+ * hipMemcpyAsync reaches in both directions at once; at the default 16 the load-back keeps
  * its full rate and the write-back backs off (load-back first, for a forward pass that
  * waits on it); a zero-copy write-back on 16 workgroups holds the link and starves
  * concurrent load-backs to ~30 GB/s. */
