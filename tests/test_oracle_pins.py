@@ -114,6 +114,22 @@ MUTANTS = [
      "if (has_page_blocks(g) && g->device_slots % g->page_size != 0) return ORC_ERR_INVALID;", ";"),
     ("unknown granularity accepted",
      "if (g->gran[b] != ORC_TOKEN_ROWS && g->gran[b] != ORC_PAGE_BLOCKS) return ORC_ERR_INVALID;", ";"),
+    ("load-back writes one slot past the listed one",
+     "uint8_t* dst = dev[b * L + layer] + orc_device_offset(g, b, d[i]);",
+     "uint8_t* dst = dev[b * L + layer] + orc_device_offset(g, b, (d[i] + 1) % g->device_slots);"),
+    ("store dump copies only the first sub-buffer",
+     "    for (int b = 0; b < pf->nsub; b++) {\n      int32_t rows = pf->gran[b] == ORC_PAGE_BLOCKS ? 1 : pf->page_size;\n"
+     "      for (int32_t l = 0; l < pf->layers; l++)\n        for (int32_t r = 0; r < rows; r++)\n"
+     "          memcpy(store + orc_host_offset(sh, b, dst_shards[i], l, r)",
+     "    for (int b = 0; b < 1; b++) {\n      int32_t rows = pf->gran[b] == ORC_PAGE_BLOCKS ? 1 : pf->page_size;\n"
+     "      for (int32_t l = 0; l < pf->layers; l++)\n        for (int32_t r = 0; r < rows; r++)\n"
+     "          memcpy(store + orc_host_offset(sh, b, dst_shards[i], l, r)"),
+    ("round-trip check skips page-block sub-buffers",
+     "if (g->gran[b] == ORC_PAGE_BLOCKS && a[i] % P != 0) continue;",
+     "if (g->gran[b] == ORC_PAGE_BLOCKS) continue;"),
+    ("write-back writes into the next host page",
+     "uint8_t* dst = host + orc_host_offset(g, b, page, l, row);",
+     "uint8_t* dst = host + orc_host_offset(g, b, (page + 1) % g->host_pages, l, row);"),
 ]
 
 
