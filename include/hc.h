@@ -234,12 +234,15 @@ int hc_host_free(void* ptr);
  * buffers, the staging buffer and copy_stream must be that device's
  * (HC_ERR_INVALID otherwise), and every later call makes it current.  Each device
  * layer, the used part of the staging buffer and (when HIP can look it up) the host
- * pool must fit inside their allocations, else HC_ERR_INVALID. */
+ * pool must fit inside their allocations, else HC_ERR_INVALID.  Refused
+ * (HC_ERR_UNSUPPORTED) while copy_stream is capturing a graph: set-up copies the
+ * layer tables on it and waits. */
 int hc_pool_create(const hc_pool_desc* desc, hc_pool** out);
 
 /* Waits for the pool's copy stream, then frees the handle and its scratch.  NULL is a no-op.
  * Refused (HC_ERR_INVALID, nothing freed) while a loader or a captured load-back graph
- * created on the pool still exists: destroy those first. */
+ * created on the pool still exists: destroy those first; and (HC_ERR_UNSUPPORTED,
+ * nothing freed) while the copy stream is capturing a graph. */
 int hc_pool_destroy(hc_pool* pool);
 
 /* The mode write-back (which = 0) or load-back (which = 1) resolves to
