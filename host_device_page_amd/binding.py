@@ -427,9 +427,10 @@ class Pool:
         n = _index_list(device_idx, "device_idx", True)
         if _index_list(host_idx, "host_idx", False) != n:
             raise ValueError("host_idx and device_idx differ in length")
-        check(lib.hc_write_back_all_layers(self.handle, _V(_ptr(device_idx)), _V(_ptr(host_idx)), n,
-                                           event.handle if event else None), "hc_write_back_all_layers")
-        _in_use_on(self.stream, device_idx)
+        rc = lib.hc_write_back_all_layers(self.handle, _V(_ptr(device_idx)), _V(_ptr(host_idx)), n,
+                                          event.handle if event else None)
+        _in_use_on(self.stream, device_idx)  # also after a failure that enqueued part of the burst
+        check(rc, "hc_write_back_all_layers")
 
     def write_back_all_layers_noalloc(self, device_idx, host_idx: "HostBuffer", n: int,
                                       event: HipEvent | None = None) -> None:
@@ -439,19 +440,20 @@ class Pool:
             raise ValueError("device_idx must hold n entries")
         if not isinstance(host_idx, HostBuffer) or host_idx.nbytes < 8 * n:
             raise TypeError("host_idx must be a HostBuffer of at least n int64 entries")
-        check(lib.hc_write_back_all_layers_noalloc(self.handle, _V(_ptr(device_idx)), _V(_ptr(host_idx)), n,
-                                                   event.handle if event else None),
-              "hc_write_back_all_layers_noalloc")
+        rc = lib.hc_write_back_all_layers_noalloc(self.handle, _V(_ptr(device_idx)), _V(_ptr(host_idx)), n,
+                                                  event.handle if event else None)
         _in_use_on(self.stream, device_idx)
+        check(rc, "hc_write_back_all_layers_noalloc")
 
     def load_back_layer(self, layer: int, host_idx, device_idx, event: HipEvent | None = None) -> None:
         """host_idx, device_idx: int64 CUDA tensors."""
         n = _index_list(device_idx, "device_idx", True)
         if _index_list(host_idx, "host_idx", True) != n:
             raise ValueError("host_idx and device_idx differ in length")
-        check(lib.hc_load_back_layer(self.handle, layer, _V(_ptr(host_idx)), _V(_ptr(device_idx)), n,
-                                     event.handle if event else None), "hc_load_back_layer")
+        rc = lib.hc_load_back_layer(self.handle, layer, _V(_ptr(host_idx)), _V(_ptr(device_idx)), n,
+                                    event.handle if event else None)
         _in_use_on(self.stream, host_idx, device_idx)
+        check(rc, "hc_load_back_layer")
 
     # The host-pool method names the pages use (hybrid-pool write-back page, host-pool
     # excerpt; loader-thread page, Motivation), in their argument order, host indices
@@ -487,16 +489,18 @@ class Pool:
     def layer_pack(self, layer: int, device_idx, dst, event: HipEvent | None = None) -> None:
         """dst <- rows of `layer` at device_idx, sub-buffer after sub-buffer (dst: CUDA tensor)."""
         n = _index_list(device_idx, "device_idx", True)
-        check(lib.hc_layer_pack(self.handle, layer, _V(_ptr(device_idx)), n, _V(_ptr(dst)), _staging_bytes(dst, "dst"),
-                                event.handle if event else None), "hc_layer_pack")
+        rc = lib.hc_layer_pack(self.handle, layer, _V(_ptr(device_idx)), n, _V(_ptr(dst)), _staging_bytes(dst, "dst"),
+                               event.handle if event else None)
         _in_use_on(self.stream, device_idx, dst)
+        check(rc, "hc_layer_pack")
 
     def layer_unpack(self, layer: int, src, device_idx, event: HipEvent | None = None) -> None:
         """Rows of `layer` at device_idx <- src, in the order layer_pack writes."""
         n = _index_list(device_idx, "device_idx", True)
-        check(lib.hc_layer_unpack(self.handle, layer, _V(_ptr(src)), _staging_bytes(src, "src"), _V(_ptr(device_idx)), n,
-                                  event.handle if event else None), "hc_layer_unpack")
+        rc = lib.hc_layer_unpack(self.handle, layer, _V(_ptr(src)), _staging_bytes(src, "src"), _V(_ptr(device_idx)), n,
+                                 event.handle if event else None)
         _in_use_on(self.stream, device_idx, src)
+        check(rc, "hc_layer_unpack")
 
     def sync(self) -> None:
         check(lib.hc_pool_sync(self.handle), "hc_pool_sync")
